@@ -1,0 +1,222 @@
+/*
+ * replayssm.h -- C ABI of the ReplaySSM decode-step library for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Method: "NVIDIA ReplaySSM: hybrid model SSM decoding with a state buffer"
+ * (devotd.net news article; section numbers below refer to its English
+ * edition).  The SSM state of a sequence is kept as a checkpoint taken at the
+ * start of an interval plus a buffer of the inputs of the tokens since then
+ * (section 1).  Every token reads the checkpoint and replays the buffer to
+ * form its output; the checkpoint is rewritten once per interval, when the
+ * buffer is full.  Speculative verification produces outputs only and
+ * rollback moves a buffer position (section 3).  An optional precision split
+ * keeps a stochastically rounded update checkpoint and a separate 4-bit
+ * output copy (section 4).
+ *
+ * The recurrence being replayed (per head h, group g = h / (H/G)):
+ *     a_t = exp(dt_t * A_h)
+ *     S_t = a_t * S_{t-1} + dt_t * x_t (outer) B_t       S: P x N
+ *     y_t = S_t . C_t + D_h * x_t
+ * and its replayed form after k buffered tokens j = 1..k since checkpoint S0:
+ *     y_k = Lambda_k (S0 . C_k) + sum_j w_kj (B_j . C_k) x_j + D_h x_k
+ *     S_k = Lambda_k S0 + sum_j w_kj x_j (outer) B_j
+ * with l_i = A_h dt_i, Lambda_k = exp(sum_{i<=k} l_i) and
+ * w_kj = dt_j exp(sum_{j<i<=k} l_i).
+ *
+ * Conventions for every call
+ *  - Pointers named in rssm_state and the data arguments are DEVICE pointers
+ *    unless stated otherwise; the rssm_desc / rssm_state structs themselves
+ *    are host memory read during the call only.
+ *  - All tensors are dense, row-major (last dimension innermost),
+ *    little-endian.  The caller owns and allocates all memory; the library
+ *    never allocates, frees or synchronises (except
+ *    replayssm_check_device_errors) and never throws.
+ *  - Every call is asynchronous on `stream`.  Calls that touch the same
+ *    rssm_state must be issued on one stream (or otherwise ordered); calls on
+ *    different states may run concurrently.
+ *  - Return value: RSSM_OK, or a negative rssm_status.  Argument errors are
+ *    detected on the host before anything is launched.  A failed launch
+ *    returns RSSM_E_HIP.  The message of the last error of the calling thread
+ *    is available from replayssm_last_error().
+ *  - Device-side range errors (a position count out of range, n_keep > T)
+ *    are clamped and recorded in a sticky flag read by
+ *    replayssm_check_device_errors().
+ *
+ * Shapes (B = batch, H = n_heads, P = head_dim, N = d_state, G = n_groups,
+ * L = interval, Tmax = max_draft, Lcap = L + Tmax - 1):
+ *   x    [B, H, P]          B, C  [B, G, N]         dt [B, H]     (in_dtype)
+ *   speculative calls add a token axis after B: x [B, T, H, P] etc.
+ *   y    [B, H, P] or [B, T, H, P]   fp32
+ *   A, D [H] fp32
+ *   ckpt [B, H, P, N] (ckpt_dtype)
+ *   xbuf [B, Lcap, H, P]   bbuf [B, Lcap, G, N]   dtbuf [B, Lcap, H]   (in_dtype)
+ *   pos, intv [B] int32;  work [B + 1] int32 (all zero before first use)
+ *   out_q [B, H, P, N/2] uint8 (two FP4 codes per byte, even element in the
+ *   low nibble);  out_scale [B, H, P, N/32] uint8 (E4M3 scale per 32 elements)
+ *
+ * Supported: P = 64, N = 128; in_dtype F32 or BF16; H % G == 0;
+ * 1 <= L, 1 <= Tmax <= 8, Lcap <= 32.
+ */
+#ifndef REPLAYSSM_H_
+#define REPLAYSSM_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rssm_status {
+    RSSM_OK = 0,
+    RSSM_E_ARG = -1,          /* null pointer, bad size, inconsistent descriptor */
+    RSSM_E_UNSUPPORTED = -2,  /* shape / dtype combination not built */
+    RSSM_E_CAPACITY = -3,     /* T > max_draft or Lcap too large */
+    RSSM_E_HIP = -4,          /* a HIP runtime call failed */
+    RSSM_E_DEVICE = -5        /* device-side range error recorded (sticky) */
+} rssm_status;
+
+typedef enum rssm_dtype {
+    RSSM_F32 = 0,
+    RSSM_BF16 = 1,
+    RSSM_FP8_E4M3 = 2,        /* OCP FP8 E4M3 ("FN": no inf, max 448) */
+    RSSM_FP4_E2M1 = 3,        /* OCP MX FP4 E2M1 with an E4M3 scale per 32 */
+    RSSM_NONE = 4
+} rssm_dtype;
+
+/* Layer descriptor (host struct). */
+typedef struct rssm_desc {
+    int32_t batch;        /* B: sequence slots */
+    int32_t n_heads;      /* H */
+    int32_t head_dim;     /* P */
+    int32_t d_state;      /* N */
+    int32_t n_groups;     /* G: B/C groups; heads h use group h / (H/G) */
+    int32_t interval;     /* L: tokens per checkpoint interval (article: 16) */
+    int32_t max_draft;    /* Tmax: largest T of a speculative round (1 if unused) */
+    int32_t in_dtype;     /* rssm_dtype of x, B, C, dt and the buffers: F32 | BF16 */
+    int32_t ckpt_dtype;   /* checkpoint: F32, or BF16 / FP8_E4M3 (update checkpoint of the split) */
+    int32_t out_dtype;    /* NONE: outputs read ckpt; FP4_E2M1: separate output copy */
+    int32_t shared_lowp;  /* 1: the FP4 output copy is the only state (ablation) */
+    int32_t layer_id;     /* stochastic-rounding stream: layer index */
+    uint64_t seed;        /* stochastic-rounding stream: key */
+} rssm_desc;
+
+/* Device buffers of one layer (host struct of device pointers). */
+typedef struct rssm_state {
+    void *ckpt;           /* [B,H,P,N] ckpt_dtype; NULL when shared_lowp */
+    void *out_q;          /* [B,H,P,N/2] u8 when out_dtype == FP4_E2M1, else NULL */
+    void *out_scale;      /* [B,H,P,N/32] u8 (E4M3) when out_dtype == FP4_E2M1 */
+    void *xbuf;           /* [B,Lcap,H,P] in_dtype */
+    void *bbuf;           /* [B,Lcap,G,N] in_dtype */
+    void *dtbuf;          /* [B,Lcap,H]   in_dtype */
+    int32_t *pos;         /* [B] valid buffer entries since the checkpoint, 0..L-1 at rest */
+    int32_t *intv;        /* [B] checkpoints written so far (the rounding stream's interval index) */
+    int32_t *work;        /* [B+1] library scratch: per-slot arrival counters + sticky error word; zero-initialise once */
+    const float *A;       /* [H] decay rate, A < 0 */
+    const float *D;       /* [H] skip weight */
+    float *debug_prequant;/* optional [B,H,P,N] fp32: commit values before rounding (split path tests); NULL */
+} rssm_state;
+
+/*
+ * Standard decode step (article sections 1-2): one token per slot.
+ * For each slot with k = pos[b] buffered tokens: y = replayed output of the
+ * (k+1)-th token of the interval.  If k + 1 < L the token's x, B, dt are
+ * appended at buffer entry k and pos becomes k + 1.  If k + 1 == L the
+ * checkpoint is rewritten in the same pass that reads it (S_L from the
+ * replayed form above), pos becomes 0 and intv is incremented.
+ * x [B,H,P], B, C [B,G,N], dt [B,H] (in_dtype); y [B,H,P] fp32.
+ */
+int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x,
+                   const void *B, const void *C, const void *dt, float *y,
+                   hipStream_t stream);
+
+/*
+ * Speculative verification (article section 3): T draft positions per slot
+ * are appended at buffer entries pos .. pos+T-1 and the outputs of all T
+ * positions are produced from the checkpoint and the buffer; no state is
+ * written and pos is unchanged.  Requires 1 <= T <= max_draft.
+ * x [B,T,H,P], B, C [B,T,G,N], dt [B,T,H] (in_dtype); y [B,T,H,P] fp32.
+ */
+int replayssm_verify(const rssm_desc *desc, const rssm_state *st, int32_t T,
+                     const void *x, const void *B, const void *C, const void *dt,
+                     float *y, hipStream_t stream);
+
+/*
+ * Accept / rollback (article section 3): pos[b] += n_keep[b], so only the
+ * first n_keep[b] verified positions stay valid; rejected entries are
+ * simply overwritten later.  Slots whose count reaches L are committed (all
+ * their buffered tokens folded into the checkpoint, pos = 0, intv + 1).
+ * n_keep [B] int32 device, 0 <= n_keep <= T (larger values are clamped and
+ * flagged).
+ */
+int replayssm_accept(const rssm_desc *desc, const rssm_state *st,
+                     const int32_t *n_keep, int32_t T, hipStream_t stream);
+
+/*
+ * Flush: commit every slot with pos > 0 (checkpoint <- state after its
+ * buffered tokens, pos = 0, intv + 1).  Slots with pos == 0 are untouched.
+ */
+int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t stream);
+
+/*
+ * Load a checkpoint from an fp32 state src [B,H,P,N] (device): writes ckpt
+ * (and the output copy when configured), rounding with stream index intv[b]
+ * for the split formats, and sets pos = 0.  For F32 checkpoints it is a copy.
+ */
+int replayssm_load_checkpoint(const rssm_desc *desc, const rssm_state *st,
+                              const float *src, hipStream_t stream);
+
+/*
+ * Conventional decode step, the in-run baseline (article section 1: every
+ * token reads and writes the whole state): state [B,H,P,N] fp32 is updated
+ * in place, y [B,H,P] fp32.
+ */
+int replayssm_recurrent_step(const rssm_desc *desc, float *state, const void *x,
+                             const void *B, const void *C, const void *dt,
+                             const float *A, const float *D, float *y,
+                             hipStream_t stream);
+
+/*
+ * Conventional speculative verification, the in-run baseline (article
+ * section 3: a state copy is kept for every draft token).  pool
+ * [B, Tmax+1, H, P, N] fp32 holds each slot's states; sel [B] int32 names the
+ * current one.  The T per-token states are written to pool slots
+ * (sel + 1 + t) mod (Tmax + 1), t = 0..T-1; y [B,T,H,P] fp32.
+ */
+int replayssm_recurrent_verify(const rssm_desc *desc, float *pool, const int32_t *sel,
+                               int32_t T, const void *x, const void *B, const void *C,
+                               const void *dt, const float *A, const float *D,
+                               float *y, hipStream_t stream);
+
+/* Baseline accept: sel[b] <- (sel[b] + n_keep[b]) mod (Tmax + 1) when
+ * n_keep[b] > 0 (the kept state is the n_keep-th copy; 0 keeps the old one). */
+int replayssm_recurrent_accept(const rssm_desc *desc, int32_t *sel,
+                               const int32_t *n_keep, int32_t T, hipStream_t stream);
+
+/* Buffer capacity Lcap = L + Tmax - 1 in entries (0 for an invalid desc). */
+size_t replayssm_buffer_capacity(const rssm_desc *desc);
+
+/* Validate a descriptor without launching anything: RSSM_OK or an error. */
+int replayssm_check_desc(const rssm_desc *desc);
+
+/* Static text for a status code. */
+const char *replayssm_status_string(int status);
+
+/* Message of the calling thread's last error ("" if none). */
+const char *replayssm_last_error(void);
+
+/* Synchronise `stream`, read and clear the sticky device error word of st:
+ * RSSM_OK, RSSM_E_DEVICE (with the recorded condition in last_error) or
+ * RSSM_E_HIP. */
+int replayssm_check_device_errors(const rssm_state *st, int32_t batch, hipStream_t stream);
+
+/* Library version string. */
+const char *replayssm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REPLAYSSM_H_ */

@@ -1,0 +1,295 @@
+// api.cpp -- extern "C" entry points of libreplayssm: argument validation on
+// the host, then asynchronous kernel launches.  See include/replayssm.h for
+// the contract of every call.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "replayssm.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return status;
+}
+
+int hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return RSSM_OK;
+    return fail(RSSM_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int kMaxLcap = 32;
+constexpr int kMaxDraft = 8;
+
+int lcap_of(const rssm_desc *d) { return d->interval + d->max_draft - 1; }
+
+int heads_per_wg(const rssm_desc *d) {
+    const int hpg = d->n_heads / d->n_groups;
+    return hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
+}
+
+int check_desc(const rssm_desc *d) {
+    if (!d) return fail(RSSM_E_ARG, "desc is NULL");
+    if (d->batch < 0) return fail(RSSM_E_ARG, "batch %d < 0", d->batch);
+    if (d->n_heads <= 0 || d->n_groups <= 0)
+        return fail(RSSM_E_ARG, "n_heads %d / n_groups %d must be positive", d->n_heads, d->n_groups);
+    if (d->n_heads % d->n_groups != 0)
+        return fail(RSSM_E_ARG, "n_heads %d not a multiple of n_groups %d", d->n_heads, d->n_groups);
+    if (d->head_dim != 64 || d->d_state != 128)
+        return fail(RSSM_E_UNSUPPORTED, "head_dim %d x d_state %d: only 64 x 128 is built",
+                    d->head_dim, d->d_state);
+    if (d->interval < 1) return fail(RSSM_E_ARG, "interval %d < 1", d->interval);
+    if (d->max_draft < 1 || d->max_draft > kMaxDraft)
+        return fail(RSSM_E_CAPACITY, "max_draft %d outside 1..%d", d->max_draft, kMaxDraft);
+    if (lcap_of(d) > kMaxLcap)
+        return fail(RSSM_E_CAPACITY, "interval + max_draft - 1 = %d exceeds %d", lcap_of(d), kMaxLcap);
+    if (d->in_dtype != RSSM_F32 && d->in_dtype != RSSM_BF16)
+        return fail(RSSM_E_UNSUPPORTED, "in_dtype %d: only F32 and BF16 inputs", d->in_dtype);
+    if (d->ckpt_dtype != RSSM_F32 && d->ckpt_dtype != RSSM_BF16 && d->ckpt_dtype != RSSM_FP8_E4M3)
+        return fail(RSSM_E_UNSUPPORTED, "ckpt_dtype %d", d->ckpt_dtype);
+    if (d->out_dtype != RSSM_NONE && d->out_dtype != RSSM_FP4_E2M1)
+        return fail(RSSM_E_UNSUPPORTED, "out_dtype %d", d->out_dtype);
+    if (d->shared_lowp != 0 && d->shared_lowp != 1)
+        return fail(RSSM_E_ARG, "shared_lowp must be 0 or 1");
+    if (d->shared_lowp && d->out_dtype != RSSM_FP4_E2M1)
+        return fail(RSSM_E_ARG, "shared_lowp requires out_dtype FP4_E2M1");
+    if (d->ckpt_dtype == RSSM_F32 && d->out_dtype != RSSM_NONE)
+        return fail(RSSM_E_UNSUPPORTED, "an FP4 output copy needs a BF16/FP8 update checkpoint (or shared_lowp)");
+    if (d->ckpt_dtype != RSSM_F32 || d->out_dtype != RSSM_NONE)
+        return fail(RSSM_E_UNSUPPORTED, "the precision-split formats are not built in this library yet");
+    if ((int64_t)d->batch * d->n_heads > (int64_t)1 << 24)
+        return fail(RSSM_E_ARG, "batch * n_heads too large");
+    return RSSM_OK;
+}
+
+int check_state(const rssm_desc *d, const rssm_state *s) {
+    if (!s) return fail(RSSM_E_ARG, "state is NULL");
+    if (d->batch == 0) return RSSM_OK;
+    if (!s->ckpt) return fail(RSSM_E_ARG, "state->ckpt is NULL");
+    if (!s->xbuf || !s->bbuf || !s->dtbuf) return fail(RSSM_E_ARG, "state buffers are NULL");
+    if (!s->pos || !s->intv || !s->work) return fail(RSSM_E_ARG, "state pos/intv/work is NULL");
+    if (!s->A || !s->D) return fail(RSSM_E_ARG, "state A/D is NULL");
+    return RSSM_OK;
+}
+
+rssm::ReplayParams replay_params(const rssm_desc *d, const rssm_state *s) {
+    rssm::ReplayParams p{};
+    p.ckpt = static_cast<float *>(s->ckpt);
+    p.xbuf = s->xbuf;
+    p.bbuf = s->bbuf;
+    p.dtbuf = s->dtbuf;
+    p.pos = s->pos;
+    p.intv = s->intv;
+    p.work = s->work;
+    p.A = s->A;
+    p.D = s->D;
+    p.batch = d->batch;
+    p.H = d->n_heads;
+    p.G = d->n_groups;
+    p.L = d->interval;
+    p.Lcap = lcap_of(d);
+    p.T = 1;
+    p.hpw = heads_per_wg(d);
+    p.wg_per_slot = d->n_heads / p.hpw;
+    return p;
+}
+
+#define RSSM_TRY(expr)              \
+    do {                            \
+        int rc_ = (expr);           \
+        if (rc_ != RSSM_OK) return rc_; \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int replayssm_check_desc(const rssm_desc *desc) {
+    g_last_error[0] = 0;
+    return check_desc(desc);
+}
+
+size_t replayssm_buffer_capacity(const rssm_desc *desc) {
+    if (check_desc(desc) != RSSM_OK) return 0;
+    return (size_t)lcap_of(desc);
+}
+
+int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x, const void *B,
+                   const void *C, const void *dt, float *y, hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    RSSM_TRY(check_state(desc, st));
+    if (desc->batch == 0) return RSSM_OK;
+    if (!x || !B || !C || !dt || !y) return fail(RSSM_E_ARG, "step: an input/output pointer is NULL");
+    rssm::ReplayParams p = replay_params(desc, st);
+    p.x = x;
+    p.Bm = B;
+    p.Cm = C;
+    p.dt = dt;
+    p.y = y;
+    return hip_status(rssm::launch_replay_step(p, desc->in_dtype == RSSM_BF16, stream), "replay step launch");
+}
+
+int replayssm_verify(const rssm_desc *desc, const rssm_state *st, int32_t T, const void *x,
+                     const void *B, const void *C, const void *dt, float *y, hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    RSSM_TRY(check_state(desc, st));
+    if (T < 1 || T > desc->max_draft)
+        return fail(RSSM_E_CAPACITY, "verify: T = %d outside 1..max_draft (%d)", T, desc->max_draft);
+    if (desc->batch == 0) return RSSM_OK;
+    if (!x || !B || !C || !dt || !y) return fail(RSSM_E_ARG, "verify: an input/output pointer is NULL");
+    rssm::ReplayParams p = replay_params(desc, st);
+    p.x = x;
+    p.Bm = B;
+    p.Cm = C;
+    p.dt = dt;
+    p.y = y;
+    p.T = T;
+    return hip_status(rssm::launch_replay_verify(p, desc->in_dtype == RSSM_BF16, stream),
+                      "replay verify launch");
+}
+
+int replayssm_accept(const rssm_desc *desc, const rssm_state *st, const int32_t *n_keep, int32_t T,
+                     hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    RSSM_TRY(check_state(desc, st));
+    if (T < 1 || T > desc->max_draft)
+        return fail(RSSM_E_CAPACITY, "accept: T = %d outside 1..max_draft (%d)", T, desc->max_draft);
+    if (desc->batch == 0) return RSSM_OK;
+    if (!n_keep) return fail(RSSM_E_ARG, "accept: n_keep is NULL");
+    rssm::ReplayParams p = replay_params(desc, st);
+    p.n_keep = n_keep;
+    p.T = T;
+    return hip_status(rssm::launch_replay_commit(p, desc->in_dtype == RSSM_BF16, true, stream),
+                      "accept launch");
+}
+
+int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    RSSM_TRY(check_state(desc, st));
+    if (desc->batch == 0) return RSSM_OK;
+    rssm::ReplayParams p = replay_params(desc, st);
+    return hip_status(rssm::launch_replay_commit(p, desc->in_dtype == RSSM_BF16, false, stream),
+                      "commit launch");
+}
+
+int replayssm_load_checkpoint(const rssm_desc *desc, const rssm_state *st, const float *src,
+                              hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    RSSM_TRY(check_state(desc, st));
+    if (desc->batch == 0) return RSSM_OK;
+    if (!src) return fail(RSSM_E_ARG, "load_checkpoint: src is NULL");
+    const size_t bytes = (size_t)desc->batch * desc->n_heads * desc->head_dim * desc->d_state * sizeof(float);
+    RSSM_TRY(hip_status(hipMemcpyAsync(st->ckpt, src, bytes, hipMemcpyDeviceToDevice, stream),
+                        "load_checkpoint copy"));
+    return hip_status(rssm::launch_zero_pos(st->pos, desc->batch, stream), "load_checkpoint pos reset");
+}
+
+int replayssm_recurrent_step(const rssm_desc *desc, float *state, const void *x, const void *B,
+                             const void *C, const void *dt, const float *A, const float *D, float *y,
+                             hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    if (desc->batch == 0) return RSSM_OK;
+    if (!state || !x || !B || !C || !dt || !A || !D || !y)
+        return fail(RSSM_E_ARG, "recurrent_step: a pointer is NULL");
+    rssm::RecurrentParams p{};
+    p.state = state;
+    p.x = x;
+    p.Bm = B;
+    p.Cm = C;
+    p.dt = dt;
+    p.A = A;
+    p.D = D;
+    p.y = y;
+    p.batch = desc->batch;
+    p.H = desc->n_heads;
+    p.G = desc->n_groups;
+    p.T = 1;
+    p.Tmax = desc->max_draft;
+    p.hpw = heads_per_wg(desc);
+    p.wg_per_slot = desc->n_heads / p.hpw;
+    return hip_status(rssm::launch_recurrent(p, desc->in_dtype == RSSM_BF16, false, stream),
+                      "recurrent step launch");
+}
+
+int replayssm_recurrent_verify(const rssm_desc *desc, float *pool, const int32_t *sel, int32_t T,
+                               const void *x, const void *B, const void *C, const void *dt,
+                               const float *A, const float *D, float *y, hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    if (T < 1 || T > desc->max_draft)
+        return fail(RSSM_E_CAPACITY, "recurrent_verify: T = %d outside 1..max_draft (%d)", T, desc->max_draft);
+    if (desc->batch == 0) return RSSM_OK;
+    if (!pool || !sel || !x || !B || !C || !dt || !A || !D || !y)
+        return fail(RSSM_E_ARG, "recurrent_verify: a pointer is NULL");
+    rssm::RecurrentParams p{};
+    p.state = pool;
+    p.sel = sel;
+    p.x = x;
+    p.Bm = B;
+    p.Cm = C;
+    p.dt = dt;
+    p.A = A;
+    p.D = D;
+    p.y = y;
+    p.batch = desc->batch;
+    p.H = desc->n_heads;
+    p.G = desc->n_groups;
+    p.T = T;
+    p.Tmax = desc->max_draft;
+    p.hpw = heads_per_wg(desc);
+    p.wg_per_slot = desc->n_heads / p.hpw;
+    return hip_status(rssm::launch_recurrent(p, desc->in_dtype == RSSM_BF16, true, stream),
+                      "recurrent verify launch");
+}
+
+int replayssm_recurrent_accept(const rssm_desc *desc, int32_t *sel, const int32_t *n_keep, int32_t T,
+                               hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    if (T < 1 || T > desc->max_draft)
+        return fail(RSSM_E_CAPACITY, "recurrent_accept: T = %d outside 1..max_draft (%d)", T, desc->max_draft);
+    if (desc->batch == 0) return RSSM_OK;
+    if (!sel || !n_keep) return fail(RSSM_E_ARG, "recurrent_accept: a pointer is NULL");
+    return hip_status(rssm::launch_recurrent_accept(sel, n_keep, desc->batch, T, desc->max_draft, stream),
+                      "recurrent accept launch");
+}
+
+const char *replayssm_status_string(int status) {
+    switch (status) {
+        case RSSM_OK: return "ok";
+        case RSSM_E_ARG: return "invalid argument";
+        case RSSM_E_UNSUPPORTED: return "unsupported configuration";
+        case RSSM_E_CAPACITY: return "capacity exceeded";
+        case RSSM_E_HIP: return "HIP runtime error";
+        case RSSM_E_DEVICE: return "device-side range error";
+        default: return "unknown status";
+    }
+}
+
+const char *replayssm_last_error(void) { return g_last_error; }
+
+int replayssm_check_device_errors(const rssm_state *st, int32_t batch, hipStream_t stream) {
+    if (!st || !st->work) return fail(RSSM_E_ARG, "check_device_errors: state/work is NULL");
+    if (batch < 0) return fail(RSSM_E_ARG, "check_device_errors: batch < 0");
+    RSSM_TRY(hip_status(hipStreamSynchronize(stream), "check_device_errors sync"));
+    int32_t word = 0;
+    RSSM_TRY(hip_status(hipMemcpy(&word, st->work + batch, sizeof(word), hipMemcpyDeviceToHost),
+                        "check_device_errors read"));
+    if (word == 0) return RSSM_OK;
+    const int32_t zero = 0;
+    RSSM_TRY(hip_status(hipMemcpy(st->work + batch, &zero, sizeof(zero), hipMemcpyHostToDevice),
+                        "check_device_errors clear"));
+    return fail(RSSM_E_DEVICE, "device range error flags 0x%x (1: position out of range, 2: n_keep out of range)",
+                word);
+}
+
+const char *replayssm_version(void) { return "replayssm-gfx950 0.1"; }
+
+}  // extern "C"

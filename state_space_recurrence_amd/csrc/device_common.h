@@ -1,0 +1,127 @@
+// device_common.h -- gfx950 device helpers shared by the ReplaySSM kernels.
+//
+// Lane layout used by every state-streaming kernel (P = 64 rows, N = 128
+// columns of fp32 per head):
+//   one wave64 owns one head; lane l = 32*hf + c reads, with one 16-byte
+//   load, columns 4c..4c+3 of row 2i+hf for i = 0..31 (a whole 512-byte row
+//   per 32-lane half, two rows per wave-wide load instruction: fully
+//   coalesced).  A per-row partial dot product over the lane's 4 columns is
+//   then reduced across the 32 lanes of the half by a reduce-scatter
+//   butterfly after which lane c of half hf holds the total of row 2c+hf.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm {
+
+constexpr int kP = 64;
+constexpr int kN = 128;
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- inputs --
+// Input element types: fp32, or bf16 carried as its 16 raw bits.
+template <typename T> struct io;
+
+template <> struct io<float> {
+    using raw4 = float4;   // four elements as stored
+    static __device__ __forceinline__ raw4 load_raw4(const float *p) {
+        return *reinterpret_cast<const float4 *>(p);
+    }
+    static __device__ __forceinline__ float4 widen(raw4 r) { return r; }
+    static __device__ __forceinline__ float load1(const float *p) { return *p; }
+    static __device__ __forceinline__ float4 load4(const float *p) {
+        return *reinterpret_cast<const float4 *>(p);
+    }
+    static __device__ __forceinline__ void copy1(float *dst, const float *src) { *dst = *src; }
+};
+
+template <> struct io<uint16_t> {
+    using raw4 = uint2;    // four bf16 as stored
+    static __device__ __forceinline__ raw4 load_raw4(const uint16_t *p) {
+        return *reinterpret_cast<const uint2 *>(p);
+    }
+    static __device__ __forceinline__ float4 widen(raw4 u) {
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    }
+    static __device__ __forceinline__ float load1(const uint16_t *p) {
+        return __uint_as_float(uint32_t(*p) << 16);
+    }
+    static __device__ __forceinline__ float4 load4(const uint16_t *p) {
+        uint2 u = *reinterpret_cast<const uint2 *>(p);
+        return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
+                           __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
+    }
+    static __device__ __forceinline__ void copy1(uint16_t *dst, const uint16_t *src) { *dst = *src; }
+};
+
+__device__ __forceinline__ float dot4(float4 a, float4 b) {
+    return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
+}
+
+// ------------------------------------------------------------- cross-lane --
+// DPP controls (GCN/CDNA encoding).
+constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within a 16-lane row
+constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within 8 lanes
+constexpr int kDppQuadRev = 0x1B;         // quad_perm [3,2,1,0]
+constexpr int kDppQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// One butterfly stage on pairs (v[i], v[i+H]): the partner lane holds the
+// complementary half; the lane keeps index i if `up` is false, i+H if true.
+template <int CTRL, int H, int NV>
+__device__ __forceinline__ void rs_stage(float (&v)[NV], bool up) {
+#pragma unroll
+    for (int i = 0; i < H; ++i) {
+        float lo = v[i] + dpp<CTRL>(v[i]);
+        float hi = v[i + H] + dpp<CTRL>(v[i + H]);
+        v[i] = up ? hi : lo;
+    }
+}
+
+// Reduce-scatter of 32 per-lane values over the 32 lanes of each half-wave.
+// On entry v[i] is lane c's partial of item i; on exit v[0] is the total of
+// item c over the 32 lanes of the half.
+__device__ __forceinline__ void reduce_scatter32(float (&v)[32], int lane) {
+    // lane bit 4: rows (16-lane groups) 0<->1 and 2<->3 exchange through
+    // v_permlane16_swap: odd rows of the first operand trade places with even
+    // rows of the second, so both sides of each pair see own + partner.
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 16]),
+                                                  false, false);
+        v[i] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    rs_stage<kDppRowMirror, 8>(v, (lane & 8) != 0);
+    rs_stage<kDppRowHalfMirror, 4>(v, (lane & 4) != 0);
+    rs_stage<kDppQuadRev, 2>(v, (lane & 2) != 0);
+    rs_stage<kDppQuadSwap1, 1>(v, (lane & 1) != 0);
+}
+
+// Sum over the 16 lanes of a DPP row, result in every lane of the row.
+__device__ __forceinline__ float row16_sum(float v) {
+    v += dpp<kDppRowMirror>(v);
+    v += dpp<kDppRowHalfMirror>(v);
+    v += dpp<kDppQuadRev>(v);
+    v += dpp<kDppQuadSwap1>(v);
+    return v;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs of the chip; remap
+// so that each XCD (and its L2) works on a contiguous range of logical
+// workgroups (adjacent heads of the same slot share B/C and buffer reads).
+__device__ __forceinline__ int xcd_remap(int bid, int nwg) {
+    if (nwg % 8 != 0) return bid;
+    return (bid % 8) * (nwg / 8) + bid / 8;
+}
+
+// Sticky device error bits (stored in work[batch]).
+constexpr int kErrPos = 1;    // position count out of range on entry
+constexpr int kErrKeep = 2;   // n_keep outside 0..T
+
+}  // namespace rssm

@@ -1,0 +1,51 @@
+// kernels.h -- host-side launch interface of the ReplaySSM HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm {
+
+// Arguments shared by the replay kernels (fp32 checkpoint path).
+struct ReplayParams {
+    float *ckpt;            // [B,H,P,N] fp32 checkpoint
+    const void *x;          // [B,T,H,P] in dtype
+    const void *Bm;         // [B,T,G,N]
+    const void *Cm;         // [B,T,G,N]
+    const void *dt;         // [B,T,H]
+    float *y;               // [B,T,H,P] fp32
+    void *xbuf;             // [B,Lcap,H,P]
+    void *bbuf;             // [B,Lcap,G,N]
+    void *dtbuf;            // [B,Lcap,H]
+    int32_t *pos;           // [B]
+    int32_t *intv;          // [B]
+    int32_t *work;          // [B+1]
+    const float *A;         // [H]
+    const float *D;         // [H]
+    const int32_t *n_keep;  // [B] (accept)
+    int batch, H, G, L, Lcap, T;
+    int hpw;                // heads (waves) per workgroup
+    int wg_per_slot;        // H / hpw
+};
+
+// Arguments of the conventional (recurrent) baseline kernels.
+struct RecurrentParams {
+    float *state;           // [B,H,P,N] (in place) or pool [B,Tmax+1,H,P,N]
+    const int32_t *sel;     // [B] current pool slot (pool mode)
+    const void *x, *Bm, *Cm, *dt;
+    const float *A, *D;
+    float *y;
+    int batch, H, G, T, Tmax;
+    int hpw, wg_per_slot;
+};
+
+// Launchers; in_bf16 selects bf16 inputs (else fp32).  Return hipError_t.
+hipError_t launch_replay_step(const ReplayParams &p, bool in_bf16, hipStream_t s);
+hipError_t launch_replay_verify(const ReplayParams &p, bool in_bf16, hipStream_t s);
+hipError_t launch_replay_commit(const ReplayParams &p, bool in_bf16, bool accept, hipStream_t s);
+hipError_t launch_zero_pos(int32_t *pos, int batch, hipStream_t s);
+hipError_t launch_recurrent(const RecurrentParams &p, bool in_bf16, bool pool, hipStream_t s);
+hipError_t launch_recurrent_accept(int32_t *sel, const int32_t *n_keep, int batch, int T,
+                                   int Tmax, hipStream_t s);
+
+}  // namespace rssm
