@@ -1,0 +1,400 @@
+#!/usr/bin/env python3
+"""Benchmark of the ReplaySSM decode step on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu-baseline]
+
+Workload (one "step" = one decode token for every slot through every stacked
+SSM layer, i.e. one pass of the hot path): 4B-class hybrid-model SSM layers,
+batch 256, 4 stacked layers, 96 heads, head dim 64, state dim 128, 8 B/C
+groups, fp32 checkpoint, bf16 x/B/C/dt inputs, 16-token interval; inputs for
+every timed step are resident in HBM before timing starts; every 16th step
+rewrites the checkpoints (fused commit), and those steps are inside the timed
+region.
+
+Prints ONE JSON line.  `value` = decode tokens/s (batch * steps / wall time of
+the stacked-layer loop, HIP events on the launch stream).  `roofline` rates
+the replay step kernel: algorithmic bytes per launch (byte model below) over
+its average launch duration, measured with per-launch HIP events in a second
+pass.  Extras: the conventional recurrent baseline on the same inputs, a
+batch sweep (1, 512), the 120B-class shape, and speculative verify + accept
+vs. the per-draft-copy baseline.  `cpu_baseline` times the fp64 oracle on a
+bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+# ----------------------------------------------------------------------------
+# Algorithmic byte model (per slot per layer per token), see the kernel docs.
+# ----------------------------------------------------------------------------
+def replay_bytes_per_token(H, G, P=64, N=128, L=16, in_bytes=2, state_bytes=4):
+    """Unique HBM bytes one decode token moves through one layer for one slot
+    on the replay path, averaged over an interval of L steps:
+      checkpoint read every step, rewritten once per interval (1/L);
+      current x, B, C, dt read; x, B, dt appended (not on the commit step);
+      buffer read: k entries at position k, k = 0..L-1 -> (L-1)/2 on average;
+      y written (fp32)."""
+    state = H * P * N * state_bytes
+    entry = (H * P + G * N + H) * in_bytes          # one buffered token
+    cur = (H * P + 2 * G * N + H) * in_bytes
+    y = H * P * 4
+    return state + state / L + cur + entry * (L - 1) / L + entry * (L - 1) / 2 + y
+
+
+def recurrent_bytes_per_token(H, G, P=64, N=128, in_bytes=2, state_bytes=4):
+    """Conventional step: state read + written every token, inputs read, y written."""
+    return 2 * H * P * N * state_bytes + (H * P + 2 * G * N + H) * in_bytes + H * P * 4
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-steps", type=int, default=16)
+    ap.add_argument("--probe", action="store_true",
+                    help="short fixed run for profiler counters: 16 warm-up + 16 replay steps, "
+                         "16 recurrent steps, then 3 plain 1 GiB device copies (calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the ReplaySSM decode step "
+              "has no cross-GPU exchange; every GPU would run its own slots (or head groups) "
+              "independently. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    import state_space_recurrence_amd as rs
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    L = rs.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    sh = ctypes.c_void_p(stream.cuda_stream)
+    log = lambda *a: print(*a, file=sys.stderr, flush=True)
+
+    w = synth.WORKLOADS["4b"]
+
+    # ------------------------------------------------------------------ setup
+    def make_layers(w, batch, nsteps, max_draft=1, tokens=None):
+        layers = []
+        for l in range(w.layers):
+            A, D = synth.layer_params(w, l, device=dev)
+            S0 = synth.init_state(w, l, device=dev, batch=batch)
+            ins = synth.token_inputs(w, l, nsteps, device=dev, batch=batch, tokens=tokens)
+            ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=w.interval,
+                               max_draft=max_draft, in_dtype=ins[0].dtype, device=dev, layer_id=l)
+            rs.load_checkpoint(ls, S0)
+            layers.append({"ls": ls, "S0": S0, "A": ls.A, "D": ls.D, "in": ins,
+                           "desc": ls.desc(), "st": ls.cstate()})
+        torch.cuda.synchronize()
+        return layers
+
+    def replay_loop(layers, t0, n, y, events=None):
+        """n decode steps starting at input index t0 (cyclic)."""
+        for i in range(n):
+            for li, lay in enumerate(layers):
+                x, Bm, Cm, dt = lay["in"]
+                t = (t0 + i) % x.shape[0]
+                if events is not None:
+                    events.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                    events[-1][0].record(stream)
+                rc = L.replayssm_step(ctypes.byref(lay["desc"]), ctypes.byref(lay["st"]),
+                                      x[t].data_ptr(), Bm[t].data_ptr(), Cm[t].data_ptr(),
+                                      dt[t].data_ptr(), y[li].data_ptr(), sh)
+                if events is not None:
+                    events[-1][1].record(stream)
+                if rc:
+                    raise RuntimeError(L.replayssm_last_error().decode())
+
+    def recurrent_loop(layers, states, t0, n, y, events=None):
+        for i in range(n):
+            for li, lay in enumerate(layers):
+                x, Bm, Cm, dt = lay["in"]
+                t = (t0 + i) % x.shape[0]
+                if events is not None:
+                    events.append((torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)))
+                    events[-1][0].record(stream)
+                rc = L.replayssm_recurrent_step(ctypes.byref(lay["desc"]), states[li].data_ptr(),
+                                                x[t].data_ptr(), Bm[t].data_ptr(), Cm[t].data_ptr(),
+                                                dt[t].data_ptr(), lay["A"].data_ptr(), lay["D"].data_ptr(),
+                                                y[li].data_ptr(), sh)
+                if events is not None:
+                    events[-1][1].record(stream)
+                if rc:
+                    raise RuntimeError(L.replayssm_last_error().decode())
+
+    def timed(fn, *a):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(*a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3   # seconds
+
+    def per_launch_us(events):
+        torch.cuda.synchronize()
+        d = [a.elapsed_time(b) * 1e3 for a, b in events]
+        return sum(d) / len(d)
+
+    def run_standard(w, batch, steps, warmup, with_recurrent=True, per_launch=True):
+        n_in = min(steps + warmup, 64) if batch <= 32 else steps + warmup
+        layers = make_layers(w, batch, n_in)
+        y = [torch.empty(batch, w.heads, 64, device=dev) for _ in layers]
+        replay_loop(layers, 0, warmup, y)
+        sec = timed(replay_loop, layers, warmup, steps, y)
+        out = {"batch": batch, "layers": w.layers, "heads": w.heads, "groups": w.groups,
+               "steps": steps, "replay_ms_per_step": sec / steps * 1e3,
+               "replay_tokens_per_s": batch * steps / sec}
+        if per_launch:
+            ev = []
+            replay_loop(layers, warmup + steps, 4 * w.interval, y, ev)
+            out["replay_kernel_avg_us"] = per_launch_us(ev)
+        if with_recurrent:
+            states = [lay["S0"].clone() for lay in layers]
+            recurrent_loop(layers, states, 0, warmup, y)
+            rsec = timed(recurrent_loop, layers, states, warmup, steps, y)
+            out["recurrent_ms_per_step"] = rsec / steps * 1e3
+            out["recurrent_tokens_per_s"] = batch * steps / rsec
+            out["replay_speedup_vs_recurrent"] = rsec / sec
+            if per_launch:
+                ev = []
+                recurrent_loop(layers, states, warmup + steps, 4 * w.interval, y, ev)
+                out["recurrent_kernel_avg_us"] = per_launch_us(ev)
+        rb = replay_bytes_per_token(w.heads, w.groups, L=w.interval)
+        cb = recurrent_bytes_per_token(w.heads, w.groups)
+        out["replay_bytes_per_token_layer"] = rb
+        out["recurrent_bytes_per_token_layer"] = cb
+        out["replay_GBps_stack"] = rb * batch * w.layers * steps / sec / 1e9
+        del layers
+        torch.cuda.empty_cache()
+        return out
+
+    if args.probe:
+        layers = make_layers(w, args.batch, 32)
+        y = [torch.empty(args.batch, w.heads, 64, device=dev) for _ in layers]
+        replay_loop(layers, 0, 32, y)
+        states = [lay["S0"].clone() for lay in layers]
+        recurrent_loop(layers, states, 0, 16, y)
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] probe done: 32 replay steps, 16 recurrent steps, 3 x 1 GiB copies")
+        return
+
+    # -------------------------------------------------------------- headline
+    log(f"[bench] {w.describe()} batch={args.batch} steps={args.steps} warmup={args.warmup}")
+    main_res = run_standard(w, args.batch, args.steps, args.warmup)
+    log(f"[bench] replay {main_res['replay_tokens_per_s']:.0f} tok/s, "
+        f"recurrent {main_res.get('recurrent_tokens_per_s', 0):.0f} tok/s")
+
+    rb = main_res["replay_bytes_per_token_layer"]
+    avg_us = main_res["replay_kernel_avg_us"]
+    achieved = rb * args.batch / (avg_us * 1e-6) / 1e9
+    traffic = _load_traffic()
+    roofline = {"bound": "hbm", "kernel": "replay_step_kernel<bf16,16>",
+                "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "bytes_per_launch": rb * args.batch, "avg_launch_us": round(avg_us, 2)}
+
+    extras = {"recurrent_baseline": {k: main_res[k] for k in main_res if k.startswith("recurrent")},
+              "replay_speedup_vs_recurrent": main_res.get("replay_speedup_vs_recurrent")}
+    if not args.no_extras:
+        for b in (1, 512):
+            r = run_standard(w, b, 128 if b == 1 else 256, 16)
+            extras[f"4b_batch{b}"] = r
+            log(f"[bench] batch {b}: replay {r['replay_tokens_per_s']:.0f} tok/s, "
+                f"recurrent {r['recurrent_tokens_per_s']:.0f} tok/s")
+        w2 = synth.WORKLOADS["120b"]
+        r = run_standard(w2, w2.batch, 128, 16)
+        extras["120b_batch256"] = r
+        log(f"[bench] 120b: replay {r['replay_tokens_per_s']:.0f} tok/s, "
+            f"recurrent {r['recurrent_tokens_per_s']:.0f} tok/s")
+        extras["spec_batch512"] = run_spec(rs, L, torch, synth, dev, stream, sh, log)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_steps, log)
+
+    res = {
+        "metric": "SSM-layer decode tokens/s @B=256,L=16 + achieved HBM GB/s (% of peak)",
+        "value": round(main_res["replay_tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(main_res["replay_ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded; bf16 x/B/C/dt ~ the stated distributions, fp32 checkpoint)",
+        "config": {"workload": "4B-class hybrid SSM layers: batch 256, 4 stacked layers, 96 heads, "
+                               "P=64, N=128, 8 groups, L=16, fp32 checkpoint, bf16 inputs",
+                   "batch": args.batch, "layers": w.layers, "heads": w.heads, "groups": w.groups,
+                   "interval": w.interval, "parallelism": "single GPU"},
+        "hbm_GBps_stack": round(main_res["replay_GBps_stack"], 1),
+        "hbm_frac_stack": round(main_res["replay_GBps_stack"] / HBM_PEAK_GBS, 4),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def run_spec(rs, L, torch, synth, dev, stream, sh, log, rounds=64, warm=8):
+    """Speculative verify + accept (replay) vs. per-draft-copy recurrent
+    verify + accept, 120B-class shape, batch 512, 4 drafts, 4 layers; the
+    same seeded accepted lengths drive both paths."""
+    w = synth.WORKLOADS["spec"]
+    T = w.drafts + 1
+    nin = 16
+    nk = synth.n_keep(w, nin, device=dev)
+    layers = []
+    for l in range(w.layers):
+        A, D = synth.layer_params(w, l, device=dev)
+        S0 = synth.init_state(w, l, device=dev)
+        x, Bm, Cm, dt = synth.token_inputs(w, l, nin, device=dev, tokens=T)
+        bt = lambda t: t.transpose(1, 2).contiguous()   # [R,T,B,..] -> [R,B,T,..]
+        ls = rs.LayerState(w.batch, w.heads, w.groups, A, D, interval=w.interval, max_draft=T,
+                           in_dtype=x.dtype, device=dev, layer_id=l)
+        rs.load_checkpoint(ls, S0)
+        layers.append({"ls": ls, "desc": ls.desc(), "st": ls.cstate(), "S0": S0,
+                       "in": (bt(x), bt(Bm), bt(Cm), bt(dt)), "A": ls.A, "D": ls.D})
+    y = torch.empty(w.batch, T, w.heads, 64, device=dev)
+
+    def replay_rounds(r0, n):
+        for i in range(n):
+            r = (r0 + i) % nin
+            for lay in layers:
+                x, Bm, Cm, dt = lay["in"]
+                rc = L.replayssm_verify(ctypes.byref(lay["desc"]), ctypes.byref(lay["st"]), T,
+                                        x[r].data_ptr(), Bm[r].data_ptr(), Cm[r].data_ptr(),
+                                        dt[r].data_ptr(), y.data_ptr(), sh)
+                rc |= L.replayssm_accept(ctypes.byref(lay["desc"]), ctypes.byref(lay["st"]),
+                                         nk[r].data_ptr(), T, sh)
+                if rc:
+                    raise RuntimeError(L.replayssm_last_error().decode())
+
+    def t(fn, *a):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn(*a)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    replay_rounds(0, warm)
+    sec = t(replay_rounds, warm, rounds)
+    kept = float(nk.double().mean()) * w.batch * rounds
+    out = {"batch": w.batch, "layers": w.layers, "heads": w.heads, "drafts": w.drafts,
+           "rounds": rounds, "replay_ms_per_round": sec / rounds * 1e3,
+           "replay_kept_tokens_per_s": kept / sec}
+    # conventional: a pool of T+1 states per slot, one copy written per draft
+    pools, sels = [], []
+    for lay in layers:
+        lay["ls"].ckpt = None
+        p = torch.empty(w.batch, T + 1, w.heads, 64, 128, device=dev)
+        p[:, 0] = lay["S0"]
+        pools.append(p)
+        sels.append(torch.zeros(w.batch, dtype=torch.int32, device=dev))
+    torch.cuda.empty_cache()
+
+    def rec_rounds(r0, n):
+        for i in range(n):
+            r = (r0 + i) % nin
+            for li, lay in enumerate(layers):
+                x, Bm, Cm, dt = lay["in"]
+                d = lay["desc"]
+                dd = rs.RssmDesc(d.batch, d.n_heads, 64, 128, d.n_groups, 1, T, d.in_dtype, 0, 4, 0, 0, 0)
+                rc = L.replayssm_recurrent_verify(ctypes.byref(dd), pools[li].data_ptr(), sels[li].data_ptr(),
+                                                  T, x[r].data_ptr(), Bm[r].data_ptr(), Cm[r].data_ptr(),
+                                                  dt[r].data_ptr(), lay["A"].data_ptr(), lay["D"].data_ptr(),
+                                                  y.data_ptr(), sh)
+                rc |= L.replayssm_recurrent_accept(ctypes.byref(dd), sels[li].data_ptr(), nk[r].data_ptr(), T, sh)
+                if rc:
+                    raise RuntimeError(L.replayssm_last_error().decode())
+
+    rec_rounds(0, warm)
+    rsec = t(rec_rounds, warm, rounds)
+    out["recurrent_ms_per_round"] = rsec / rounds * 1e3
+    out["recurrent_kept_tokens_per_s"] = kept / rsec
+    out["replay_speedup_vs_recurrent"] = rsec / sec
+    log(f"[bench] spec: replay {out['replay_kept_tokens_per_s']:.0f} kept tok/s, "
+        f"recurrent {out['recurrent_kept_tokens_per_s']:.0f} ({out['replay_speedup_vs_recurrent']:.2f}x)")
+    del pools, layers
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(w, steps, log, slots=None):
+    """fp64 oracle (the plain per-token recurrence) on the host cores: the
+    full batch of the workload for `steps` decode steps through all layers."""
+    import numpy as np
+    import oracle
+    import synth
+    b = slots or w.batch
+    total = 0.0
+    # warm the library and its thread pool on a tiny call
+    S, x, Bm, Cm, dt = (oracle._f64(t) for t in (synth.init_state(w, 0, batch=1),
+                                                 *synth.token_inputs(w, 0, 1, batch=1)))
+    A, D = (oracle._f64(t) for t in synth.layer_params(w, 0))
+    oracle.recurrent(S, x, Bm, Cm, dt, A, D, w.groups)
+    for l in range(w.layers):
+        A, D = (oracle._f64(t) for t in synth.layer_params(w, l))
+        S = oracle._f64(synth.init_state(w, l, batch=b))
+        ins = [oracle._f64(t) for t in synth.token_inputs(w, l, steps, batch=b)]
+        t0 = time.perf_counter()
+        oracle.recurrent(S, *ins, A, D, w.groups)
+        total += time.perf_counter() - t0
+        del S, ins
+    tok = b * steps / total
+    log(f"[bench] cpu oracle: {tok:.1f} tok/s on {oracle.num_threads()} threads ({total:.1f}s)")
+    return {"value": round(tok, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"full workload batch {b} x {w.layers} layers x {steps} decode steps "
+                      f"(fp64 per-token recurrence, OpenMP over slot x head)",
+            "seconds": round(total, 2)}
+
+
+def _load_traffic():
+    """HBM traffic of the replay step kernel from the committed rocprofv3
+    counter summary, if one matching the current kernel source exists."""
+    path = os.path.join(ROOT, "profiles", "replay_step_4b_b256_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        d = json.load(open(path))
+        import hashlib
+        src = os.path.join(ROOT, "state_space_recurrence_amd", "csrc", "replay_kernels.hip")
+        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        if d.get("kernel_source_sha256_16") != h:
+            return None
+        return d.get("traffic_bytes_per_launch")
+    except Exception:
+        return None
+
+
+if __name__ == "__main__":
+    main()
