@@ -29,6 +29,12 @@ template <> struct io<float> {
         return *reinterpret_cast<const float4 *>(p);
     }
     static __device__ __forceinline__ float4 widen(raw4 r) { return r; }
+    // widen() behind an optimisation fence: the result is recomputed at each
+    // use instead of being kept live (trades 2 VALU ops for 4 VGPRs).
+    static __device__ __forceinline__ float4 widen_here(raw4 r) {
+        asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w));
+        return r;
+    }
     static __device__ __forceinline__ float load1(const float *p) { return *p; }
     static __device__ __forceinline__ float4 load4(const float *p) {
         return *reinterpret_cast<const float4 *>(p);
@@ -45,6 +51,10 @@ template <> struct io<uint16_t> {
         return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xFFFF0000u),
                            __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xFFFF0000u));
     }
+    static __device__ __forceinline__ float4 widen_here(raw4 u) {
+        asm volatile("" : "+v"(u.x), "+v"(u.y));
+        return widen(u);
+    }
     static __device__ __forceinline__ float load1(const uint16_t *p) {
         return __uint_as_float(uint32_t(*p) << 16);
     }
@@ -55,6 +65,23 @@ template <> struct io<uint16_t> {
     }
     static __device__ __forceinline__ void copy1(uint16_t *dst, const uint16_t *src) { *dst = *src; }
 };
+
+// ------------------------------------------------------------ state stream --
+// The checkpoint is streamed once per step and is far larger than the caches
+// at serving batch sizes, so its loads (and the commit's stores) carry the
+// non-temporal hint: they do not displace the reused small tensors (inputs,
+// buffer entries) from L2 / MALL.
+typedef float f4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 stream_load4(const float *p) {
+    const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void stream_store4(float *p, float4 v) {
+    f4v u = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(u, reinterpret_cast<f4v *>(p));
+}
 
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
@@ -101,6 +128,39 @@ __device__ __forceinline__ void reduce_scatter32(float (&v)[32], int lane) {
     rs_stage<kDppRowHalfMirror, 4>(v, (lane & 4) != 0);
     rs_stage<kDppQuadRev, 2>(v, (lane & 2) != 0);
     rs_stage<kDppQuadSwap1, 1>(v, (lane & 1) != 0);
+}
+
+// ---------------------------------------------------------- chunked stream --
+// The 32 rows a lane touches (rows 2i+hf, i = 0..31) are streamed in 4 chunks
+// of 8: chunk c holds i = c + 4m, m = 0..7.  With that order the first three
+// butterfly stages (lane bits 4, 3, 2 <-> index bits 4, 3, 2 = m bits 2, 1, 0)
+// close inside a chunk, leaving one value per chunk; the last two stages
+// (lane bits 1, 0 <-> c bits 1, 0) combine the 4 chunk values.  The lane that
+// ends with a total is the same as for reduce_scatter32: lane c of half hf
+// holds row 2c + hf.
+constexpr int kChunks = 4;
+constexpr int kPerChunk = 8;
+
+__device__ __forceinline__ int chunk_index(int c, int m) { return c + 4 * m; }
+
+// Stages for lane bits 4, 3, 2 on the 8 partials of a chunk.
+__device__ __forceinline__ float chunk_reduce8(float (&v)[8], int lane) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+        auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[m]), __float_as_uint(v[m + 4]),
+                                                  false, false);
+        v[m] = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+    rs_stage<kDppRowMirror, 2>(v, (lane & 8) != 0);
+    rs_stage<kDppRowHalfMirror, 1>(v, (lane & 4) != 0);
+    return v[0];
+}
+
+// Stages for lane bits 1, 0 on the 4 chunk values.
+__device__ __forceinline__ float chunk_combine4(float (&r)[4], int lane) {
+    rs_stage<kDppQuadRev, 2>(r, (lane & 2) != 0);
+    rs_stage<kDppQuadSwap1, 1>(r, (lane & 1) != 0);
+    return r[0];
 }
 
 // Sum over the 16 lanes of a DPP row, result in every lane of the row.

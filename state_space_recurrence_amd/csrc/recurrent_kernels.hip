@@ -17,11 +17,13 @@ namespace {
 
 constexpr int kMaxHpw = 4;
 
+constexpr int kNB = 2;   // state chunks in flight per wave
+
 template <typename TIn, int T, bool POOL>
 __global__ void __launch_bounds__(256) recurrent_kernel(RecurrentParams a) {
-    // x of each token, split by row parity so a half-wave reads its 32 rows
-    // contiguously: s_x[w][t][hf][i] = x_t[2i + hf]
-    __shared__ float s_x[kMaxHpw][T][2][32];
+    // x of each token in the order a lane consumes rows: s_x[w][t][hf][c][m]
+    // = x_t[2(c + 4m) + hf] (chunk c of the state stream, see device_common.h)
+    __shared__ float s_x[kMaxHpw][T][2][kChunks][kPerChunk];
 
     const int wg = xcd_remap(blockIdx.x, gridDim.x);
     const int b = wg / a.wg_per_slot, tile = wg - b * a.wg_per_slot;
@@ -41,11 +43,14 @@ __global__ void __launch_bounds__(256) recurrent_kernel(RecurrentParams a) {
         src = a.state + ((size_t)b * a.H + h) * PN;
     }
     const size_t lane_off = (size_t)hf * kN + 4 * c;
+    src += lane_off;
 
-    float4 st[32];
+    float4 buf[kNB][kPerChunk];
 #pragma unroll
-    for (int i = 0; i < 32; ++i)
-        st[i] = *reinterpret_cast<const float4 *>(src + lane_off + (size_t)i * 2 * kN);
+    for (int q = 0; q < kNB; ++q)
+#pragma unroll
+        for (int m = 0; m < kPerChunk; ++m)
+            buf[q][m] = stream_load4(src + (size_t)chunk_index(q, m) * 2 * kN);
 
     const TIn *xin = reinterpret_cast<const TIn *>(a.x) + (size_t)b * T * HP + (size_t)h * kP;
     const TIn *Bin = reinterpret_cast<const TIn *>(a.Bm) + (size_t)b * T * GN + (size_t)g * kN;
@@ -53,54 +58,67 @@ __global__ void __launch_bounds__(256) recurrent_kernel(RecurrentParams a) {
     const TIn *dtin = reinterpret_cast<const TIn *>(a.dt) + (size_t)b * T * a.H + h;
     const float Ah = a.A[h], Dh = a.D[h];
 
-    float4 B4[T], C4[T];
-    float dtv[T], xcur[T];
+    typename io<TIn>::raw4 Braw[T], Craw[T];   // widened at each use
+    float dtv[T], at[T], xcur[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const float xl = io<TIn>::load1(xin + (size_t)t * HP + lane);
-        s_x[wave][t][lane & 1][lane >> 1] = xl;
+        s_x[wave][t][lane & 1][(lane >> 1) & 3][lane >> 3] = xl;
         xcur[t] = io<TIn>::load1(xin + (size_t)t * HP + prow);
-        B4[t] = io<TIn>::load4(Bin + (size_t)t * GN + 4 * c);
-        C4[t] = io<TIn>::load4(Cin + (size_t)t * GN + 4 * c);
+        Braw[t] = io<TIn>::load_raw4(Bin + (size_t)t * GN + 4 * c);
+        Craw[t] = io<TIn>::load_raw4(Cin + (size_t)t * GN + 4 * c);
         dtv[t] = io<TIn>::load1(dtin + (size_t)t * a.H);
+        at[t] = expf(dtv[t] * Ah);
     }
     __syncthreads();
 
+    float r[T][kChunks];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const float d = dtv[t];
-        const float at = expf(d * Ah);
-        const float *xs = s_x[wave][t][hf];
-        float v[32];
+    for (int q = 0; q < kChunks; ++q) {
+        float4 (&st)[kPerChunk] = buf[q % kNB];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const float4 xr = *reinterpret_cast<const float4 *>(xs + 4 * q);
-            const float xq[4] = {xr.x, xr.y, xr.z, xr.w};
+        for (int t = 0; t < T; ++t) {
+            const float *xs = s_x[wave][t][hf][q];
+            const float4 x0 = *reinterpret_cast<const float4 *>(xs);
+            const float4 x1 = *reinterpret_cast<const float4 *>(xs + 4);
+            const float xr[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const float4 Bt = io<TIn>::widen_here(Braw[t]), Ct = io<TIn>::widen_here(Craw[t]);
+            float v[kPerChunk];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int i = 4 * q + u;
-                const float cx = d * xq[u];
-                st[i].x = at * st[i].x + cx * B4[t].x;
-                st[i].y = at * st[i].y + cx * B4[t].y;
-                st[i].z = at * st[i].z + cx * B4[t].z;
-                st[i].w = at * st[i].w + cx * B4[t].w;
-                v[i] = dot4(st[i], C4[t]);
+            for (int m = 0; m < kPerChunk; ++m) {
+                const float cx = dtv[t] * xr[m];
+                st[m].x = at[t] * st[m].x + cx * Bt.x;
+                st[m].y = at[t] * st[m].y + cx * Bt.y;
+                st[m].z = at[t] * st[m].z + cx * Bt.z;
+                st[m].w = at[t] * st[m].w + cx * Bt.w;
+                v[m] = dot4(st[m], Ct);
             }
-        }
-        reduce_scatter32(v, lane);
-        a.y[((size_t)b * T + t) * HP + (size_t)h * kP + prow] = v[0] + Dh * xcur[t];
-        if (POOL) {
-            const int slot = (cur + 1 + t) % (a.Tmax + 1);
-            float *dst = a.state + (((size_t)b * (a.Tmax + 1) + slot) * a.H + h) * PN + lane_off;
+            r[t][q] = chunk_reduce8(v, lane);
+            if (POOL) {
+                const int slot = (cur + 1 + t) % (a.Tmax + 1);
+                float *dst = a.state + (((size_t)b * (a.Tmax + 1) + slot) * a.H + h) * PN + lane_off;
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-                *reinterpret_cast<float4 *>(dst + (size_t)i * 2 * kN) = st[i];
+                for (int m = 0; m < kPerChunk; ++m)
+                    stream_store4(dst + (size_t)chunk_index(q, m) * 2 * kN, st[m]);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one token's work at a time
+        }
+        if (!POOL) {
+            float *dst = a.state + ((size_t)b * a.H + h) * PN + lane_off;
+#pragma unroll
+            for (int m = 0; m < kPerChunk; ++m)
+                stream_store4(dst + (size_t)chunk_index(q, m) * 2 * kN, st[m]);
+        }
+        if (q + kNB < kChunks) {
+#pragma unroll
+            for (int m = 0; m < kPerChunk; ++m)
+                st[m] = stream_load4(src + (size_t)chunk_index(q + kNB, m) * 2 * kN);
         }
     }
-    if (!POOL) {
-        float *dst = a.state + ((size_t)b * a.H + h) * PN + lane_off;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) *reinterpret_cast<float4 *>(dst + (size_t)i * 2 * kN) = st[i];
+    for (int t = 0; t < T; ++t) {
+        const float y0 = chunk_combine4(r[t], lane);
+        a.y[((size_t)b * T + t) * HP + (size_t)h * kP + prow] = y0 + Dh * xcur[t];
     }
 }
 

@@ -10,9 +10,13 @@
 //
 // Work split: one workgroup = `hpw` (<= 4) heads of one slot that share a
 // B/C group; one wave64 per head.  Each wave streams its head's 32 KB of
-// checkpoint once (lane layout in device_common.h), computes S0 . C with a
-// reduce-scatter, and adds the replay terms.  The per-slot scalars
-// (decays, weights, Gram row B_j . C) are computed once per workgroup in LDS.
+// checkpoint exactly once, in 4 chunks of 8 x 16-byte loads per lane (see
+// device_common.h), with up to kNB chunks in flight; everything that does
+// not depend on the checkpoint (decays, weights, the Gram row B_j . C, the
+// buffer part of the output and the commit coefficients) is computed while
+// the first chunks are in flight.  When the interval closes, each chunk's
+// rows are rewritten in place right after they are consumed, so a commit
+// step reads the checkpoint once and writes it once.
 //
 // Decays are formed as exp of segment sums of A dt (never as ratios of
 // prefix products, which underflow to 0/0 over an interval).
@@ -24,6 +28,7 @@ namespace rssm {
 namespace {
 
 constexpr int kMaxHpw = 4;
+constexpr int kNB = 2;   // checkpoint chunks in flight per wave
 
 struct Slot {
     int b, tile, wave, lane, h, g, c, hf, prow, hpg;
@@ -45,14 +50,16 @@ __device__ __forceinline__ Slot slot_of(const ReplayParams &a) {
     return s;
 }
 
-// Pointer to row (2i + hf), columns 4c.. of head (b,h) of an fp32 state.
+// Lane base pointer into head (b,h) of an fp32 state: row hf, columns 4c..;
+// value index i adds i * 2 rows.
 __device__ __forceinline__ float *state_ptr(float *base, const Slot &s, int H) {
     return base + ((size_t)(s.b * H + s.h) * kP + s.hf) * kN + 4 * s.c;
 }
 
-__device__ __forceinline__ void load_state(float4 (&st)[32], const float *p) {
+__device__ __forceinline__ void load_chunk(float4 (&buf)[kPerChunk], const float *p, int c) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) st[i] = *reinterpret_cast<const float4 *>(p + (size_t)i * 2 * kN);
+    for (int m = 0; m < kPerChunk; ++m)
+        buf[m] = stream_load4(p + (size_t)chunk_index(c, m) * 2 * kN);
 }
 
 // Last-arriving workgroup of slot b publishes the slot's new position (and
@@ -70,31 +77,45 @@ __device__ __forceinline__ void publish_position(const ReplayParams &a, int b, i
     }
 }
 
-// Rank-K checkpoint rewrite of the rows this lane holds:
+// Commit coefficients cs = w_j x_j[r] live in LDS as [hf][c][j][m] for row
+// r = 2(c + 4m) + hf, so the 8 coefficients one chunk needs for entry j are
+// two contiguous 16-byte reads (the same address across a half-wave).
+template <int KMAX>
+__device__ __forceinline__ int cs_index(int hf, int c, int j, int m) {
+    return ((hf * kChunks + c) * KMAX + j) * kPerChunk + m;
+}
+
+// Rewrite the 8 rows of chunk c in place:
 //   S_new[r] = lam * S0[r] + sum_j cs[r][j] * B_j[4c..4c+3]
-// cs (LDS, per wave) holds w_j x_j[r] for every row r, zero for j >= K.
-// B_j slices arrive as stored (raw) and are widened on the fly.
+// (cs zero for j >= K).  Entry-outer order keeps one widened B_j slice and
+// 8 coefficients live at a time.
 template <typename TIn, int KMAX>
-__device__ __forceinline__ void commit_rows(float4 (&st)[32], float lam,
-                                            const float (*cs)[KMAX + 4],
-                                            const typename io<TIn>::raw4 (&Bj)[KMAX],
-                                            int hf, float *dst) {
+__device__ __forceinline__ void commit_chunk(float4 (&st)[kPerChunk], int c, float lam,
+                                             const float *cs, const typename io<TIn>::raw4 (&Bj)[KMAX],
+                                             int hf, float *dst) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const float *crow = cs[2 * i + hf];
-        float4 n = make_float4(lam * st[i].x, lam * st[i].y, lam * st[i].z, lam * st[i].w);
-#pragma unroll
-        for (int q = 0; q < KMAX / 4; ++q) {
-            float4 cf = *reinterpret_cast<const float4 *>(crow + 4 * q);
-            const float4 b0 = io<TIn>::widen(Bj[4 * q]), b1 = io<TIn>::widen(Bj[4 * q + 1]);
-            const float4 b2 = io<TIn>::widen(Bj[4 * q + 2]), b3 = io<TIn>::widen(Bj[4 * q + 3]);
-            n.x += cf.x * b0.x + cf.y * b1.x + cf.z * b2.x + cf.w * b3.x;
-            n.y += cf.x * b0.y + cf.y * b1.y + cf.z * b2.y + cf.w * b3.y;
-            n.z += cf.x * b0.z + cf.y * b1.z + cf.z * b2.z + cf.w * b3.z;
-            n.w += cf.x * b0.w + cf.y * b1.w + cf.z * b2.w + cf.w * b3.w;
-        }
-        *reinterpret_cast<float4 *>(dst + (size_t)i * 2 * kN) = n;
+    for (int m = 0; m < kPerChunk; ++m) {
+        st[m].x *= lam; st[m].y *= lam; st[m].z *= lam; st[m].w *= lam;
     }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        const float4 b = io<TIn>::widen_here(Bj[j]);
+        const float *cp = cs + cs_index<KMAX>(hf, c, j, 0);
+        const float4 c0 = *reinterpret_cast<const float4 *>(cp);
+        const float4 c1 = *reinterpret_cast<const float4 *>(cp + 4);
+        const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int m = 0; m < kPerChunk; ++m) {
+            st[m].x += cf[m] * b.x;
+            st[m].y += cf[m] * b.y;
+            st[m].z += cf[m] * b.z;
+            st[m].w += cf[m] * b.w;
+        }
+        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound hoisted LDS reads
+    }
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m)
+        stream_store4(dst + (size_t)chunk_index(c, m) * 2 * kN, st[m]);
 }
 
 // ------------------------------------------------------------------------
@@ -107,13 +128,14 @@ __global__ void __launch_bounds__(256) replay_step_kernel(ReplayParams a) {
     __shared__ float s_gram[KMAX];
     __shared__ float s_w[kMaxHpw][KMAX];
     __shared__ float s_cy[kMaxHpw][KMAX];
-    __shared__ float s_cs[kMaxHpw][kP][KMAX + 4];
+    __shared__ float s_cs[kMaxHpw][kP * KMAX];
 
     const Slot s = slot_of(a);
     float *sp = state_ptr(a.ckpt, s, a.H);
 
-    float4 st[32];
-    load_state(st, sp);
+    float4 buf[kNB][kPerChunk];
+#pragma unroll
+    for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
 
     int k = a.pos[s.b];
     if (k < 0 || k > a.L - 1) {
@@ -177,35 +199,40 @@ __global__ void __launch_bounds__(256) replay_step_kernel(ReplayParams a) {
     }
     __syncthreads();
 
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = dot4(st[i], C4);
-    reduce_scatter32(v, s.lane);
-
-    float yacc = lam * v[0];
+    // the part of y that does not read the checkpoint
+    float ybuf = Dh * xcur;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
         const float term = s_cy[s.wave][j] * xv[j];
-        yacc += (j < K) ? term : 0.f;   // select: entries beyond K never leak (even NaN)
+        ybuf += (j < K) ? term : 0.f;   // select: entries beyond K never leak (even NaN)
     }
-    yacc += Dh * xcur;
-    a.y[(size_t)s.b * HP + (size_t)s.h * kP + s.prow] = yacc;
-
+    typename io<TIn>::raw4 Bj[KMAX];
     if (commit) {
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             const float cf = s_w[s.wave][j] * xv[j];
-            s_cs[s.wave][s.prow][j] = (j < K) ? cf : 0.f;
-        }
-        typename io<TIn>::raw4 Bj[KMAX];
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
+            s_cs[s.wave][cs_index<KMAX>(s.hf, s.c & 3, j, s.c >> 2)] = (j < K) ? cf : 0.f;
             const TIn *pb = (j < k) ? bb + (size_t)j * GN : Bin;
             Bj[j] = io<TIn>::load_raw4(pb + 4 * s.c);
         }
-        __syncthreads();
-        commit_rows<TIn, KMAX>(st, lam, s_cs[s.wave], Bj, s.hf, sp);
-    } else {
+    }
+    __syncthreads();
+
+    float r[kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        float4 (&cur)[kPerChunk] = buf[c % kNB];
+        float v[kPerChunk];
+#pragma unroll
+        for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4);
+        r[c] = chunk_reduce8(v, s.lane);
+        if (commit) commit_chunk<TIn, KMAX>(cur, c, lam, s_cs[s.wave], Bj, s.hf, sp);
+        if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
+    }
+    const float y0 = chunk_combine4(r, s.lane);
+    a.y[(size_t)s.b * HP + (size_t)s.h * kP + s.prow] = lam * y0 + ybuf;
+
+    if (!commit) {
         // append the token at entry k
         TIn *xw = reinterpret_cast<TIn *>(a.xbuf) + ((size_t)s.b * a.Lcap + k) * HP + (size_t)s.h * kP;
         io<TIn>::copy1(xw + s.lane, xin + s.lane);
@@ -235,8 +262,9 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
 
     const Slot s = slot_of(a);
     float *sp = state_ptr(a.ckpt, s, a.H);
-    float4 st[32];
-    load_state(st, sp);
+    float4 buf[kNB][kPerChunk];
+#pragma unroll
+    for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
 
     int k = a.pos[s.b];
     if (k < 0 || k > a.L - 1) {
@@ -263,11 +291,11 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
         const TIn *px = (j < k) ? xb + (size_t)j * HP + s.prow : xin + (size_t)t * HP + s.prow;
         xv[j] = io<TIn>::load1(px);
     }
-    float xcur[T];
+    float ybuf[T];
     float4 C4[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        xcur[t] = io<TIn>::load1(xin + (size_t)t * HP + s.prow);
+        ybuf[t] = io<TIn>::load1(xin + (size_t)t * HP + s.prow);
         C4[t] = io<TIn>::load4(Cin + (size_t)t * GN + 4 * s.c);
     }
     const float Ah = a.A[s.h], Dh = a.D[s.h];
@@ -312,21 +340,36 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
     }
     __syncthreads();
 
+    // the parts of the outputs that do not read the checkpoint
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        float v[32];
-#pragma unroll
-        for (int i = 0; i < 32; ++i) v[i] = dot4(st[i], C4[t]);
-        reduce_scatter32(v, s.lane);
-        float yacc = s_lam[s.wave][t] * v[0];
         const int Kt = k + t + 1;
+        float acc = Dh * ybuf[t];
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             const float term = s_cy[s.wave][t][j] * xv[j];
-            yacc += (j < Kt) ? term : 0.f;   // later drafts never reach output t
+            acc += (j < Kt) ? term : 0.f;   // later drafts never reach output t
         }
-        yacc += Dh * xcur[t];
-        a.y[((size_t)s.b * T + t) * HP + (size_t)s.h * kP + s.prow] = yacc;
+        ybuf[t] = acc;
+    }
+
+    float r[T][kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        float4 (&cur)[kPerChunk] = buf[c % kNB];
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            float v[kPerChunk];
+#pragma unroll
+            for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4[t]);
+            r[t][c] = chunk_reduce8(v, s.lane);
+        }
+        if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const float y0 = chunk_combine4(r[t], s.lane);
+        a.y[((size_t)s.b * T + t) * HP + (size_t)s.h * kP + s.prow] = s_lam[s.wave][t] * y0 + ybuf[t];
     }
 
     // append the T drafts at entries k .. k+T-1 (position is not advanced)
@@ -357,7 +400,7 @@ template <typename TIn, int KMAX, bool ACCEPT>
 __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
     __shared__ float s_l[kMaxHpw][KMAX];
     __shared__ float s_w[kMaxHpw][KMAX];
-    __shared__ float s_cs[kMaxHpw][kP][KMAX + 4];
+    __shared__ float s_cs[kMaxHpw][kP * KMAX];
 
     const Slot s = slot_of(a);
     int k = a.pos[s.b];
@@ -378,8 +421,9 @@ __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
 
     if (commit) {
         float *sp = state_ptr(a.ckpt, s, a.H);
-        float4 st[32];
-        load_state(st, sp);
+        float4 buf[kNB][kPerChunk];
+#pragma unroll
+        for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
 
         const size_t HP = (size_t)a.H * kP, GN = (size_t)a.G * kN;
         const TIn *xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)s.b * a.Lcap * HP + (size_t)s.h * kP;
@@ -418,10 +462,15 @@ __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             const float cf = s_w[s.wave][j] * xv[j];
-            s_cs[s.wave][s.prow][j] = (j < K) ? cf : 0.f;
+            s_cs[s.wave][cs_index<KMAX>(s.hf, s.c & 3, j, s.c >> 2)] = (j < K) ? cf : 0.f;
         }
         __syncthreads();
-        commit_rows<TIn, KMAX>(st, lam, s_cs[s.wave], Bj, s.hf, sp);
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) {
+            float4 (&cur)[kPerChunk] = buf[c % kNB];
+            commit_chunk<TIn, KMAX>(cur, c, lam, s_cs[s.wave], Bj, s.hf, sp);
+            if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
+        }
     }
     publish_position(a, s.b, commit ? 0 : K, commit);
 }
