@@ -66,10 +66,29 @@ def main():
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-steps", type=int, default=16)
+    ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="write the counter summary from two rocprofv3 --pmc runs of --probe")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
+                    help="write the kernel-trace summary of a rocprofv3 --kernel-trace --stats run")
     ap.add_argument("--probe", action="store_true",
                     help="short fixed run for profiler counters: 16 warm-up + 16 replay steps, "
                          "16 recurrent steps, then 3 plain 1 GiB device copies (calibration)")
     args = ap.parse_args()
+
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace,
+                        command="rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace -o trace -- "
+                                "python -u bench.py --steps 64 --no-extras --no-cpu-baseline",
+                        title="Kernel trace: replay step vs recurrent step, 4B-class layers, batch 256",
+                        workload="batch 256, 4 stacked SSM layers, H=96, G=8, P=64, N=128, L=16, fp32 "
+                                 "checkpoint, bf16 inputs; 16 warm-up + 64 timed + 64 per-launch-timed "
+                                 "steps per path, x 4 layers.")
+        return
+    if args.summarize_counters:
+        cmd = ("rocprofv3 --pmc COUNTER -f csv -d gpurun_out/pmc_COUNTER -o pmc -- "
+               "python -u bench.py --probe")
+        summarize_counters(*args.summarize_counters, command=cmd)
+        return
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the ReplaySSM decode step "
@@ -378,22 +397,116 @@ def cpu_baseline(w, steps, log, slots=None):
             "seconds": round(total, 2)}
 
 
+TRAFFIC_MD = os.path.join(ROOT, "profiles", "replay_step_4b_b256_counters.md")
+KERNEL_SOURCES = ("replay_kernels.hip", "device_common.h")
+
+
+def _kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, "state_space_recurrence_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
 def _load_traffic():
-    """HBM traffic of the replay step kernel from the committed rocprofv3
-    counter summary, if one matching the current kernel source exists."""
-    path = os.path.join(ROOT, "profiles", "replay_step_4b_b256_traffic.json")
-    if not os.path.exists(path):
+    """HBM bytes per launch of the replay step kernel from the committed
+    rocprofv3 counter summary -- only if it was taken on the current kernel
+    source (else null)."""
+    if not os.path.exists(TRAFFIC_MD):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_MD):
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].strip().split(": ", 1)
+            kv[k.strip("`")] = v.strip().strip("`")
+    if kv.get("kernel_source_sha256_16") != _kernel_source_hash():
         return None
     try:
-        d = json.load(open(path))
-        import hashlib
-        src = os.path.join(ROOT, "state_space_recurrence_amd", "csrc", "replay_kernels.hip")
-        h = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
-        if d.get("kernel_source_sha256_16") != h:
-            return None
-        return d.get("traffic_bytes_per_launch")
-    except Exception:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
         return None
+
+
+def summarize_trace(stats_csv: str, out_md: str, command: str, title: str, workload: str) -> None:
+    """Kernel-trace summary (rocprofv3 --kernel-trace --stats) of the library's kernels."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# {title}", "", "Command (from the repository root):", "", f"    {command}", "",
+             f"Workload: {workload}", "",
+             "| kernel | calls | avg us | min us | max us | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        n = r["Name"]
+        if "rssm" not in n:
+            continue
+        short = n.split("(anonymous namespace)::")[-1].split("(rssm")[0]
+        lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
+                     f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    lines.append("")
+    open(out_md, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, out_md: str, command: str) -> None:
+    """Turn two rocprofv3 --pmc runs of `bench.py --probe` (FETCH_SIZE, then
+    WRITE_SIZE) into the counter summary: per-dispatch KiB of the replay step
+    and recurrent kernels, calibrated by the 1 GiB device copies of the probe
+    (scale = known bytes / counter bytes of the copy)."""
+    import csv
+    copy_bytes = float(1 << 30)
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        copies = [float(r["Counter_Value"]) for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        rep = [float(r["Counter_Value"]) for r in rows if "replay_step_kernel" in r["Kernel_Name"]]
+        rec = [float(r["Counter_Value"]) for r in rows if "recurrent_kernel" in r["Kernel_Name"]]
+        return copies, rep, rec
+
+    fc, frep, frec = per_kernel(fetch_csv, "FETCH_SIZE")
+    wc, wrep, wrec = per_kernel(write_csv, "WRITE_SIZE")
+    # the probe's last three copies are the 1 GiB calibration copies
+    fcal = copy_bytes / (sum(fc[-3:]) / 3 * 1024)
+    wcal = copy_bytes / (sum(wc[-3:]) / 3 * 1024)
+    avg = lambda v: sum(v) / len(v)
+    f_rep, w_rep = avg(frep) * 1024 * fcal, avg(wrep) * 1024 * wcal
+    f_rec, w_rec = avg(frec) * 1024 * fcal, avg(wrec) * 1024 * wcal
+    import synth
+    w = synth.WORKLOADS["4b"]
+    algo = replay_bytes_per_token(w.heads, w.groups, L=w.interval) * w.batch
+    algo_rec = recurrent_bytes_per_token(w.heads, w.groups) * w.batch
+    lines = [
+        "# HBM traffic counters: replay step vs recurrent step, 4B-class layers, batch 256",
+        "",
+        "Commands (from the repository root; one counter per run):",
+        "",
+        f"    {command.replace('COUNTER', 'FETCH_SIZE')}",
+        f"    {command.replace('COUNTER', 'WRITE_SIZE')}",
+        "",
+        "`bench.py --probe` runs 32 replay steps (2 whole intervals, 2 fused commits per layer) and",
+        "16 recurrent steps on the 4 stacked layers (batch 256, H=96, G=8, P=64, N=128, L=16, fp32",
+        "checkpoint, bf16 inputs), then three plain 1 GiB device copies used as calibration.",
+        "",
+        "| quantity | FETCH_SIZE | WRITE_SIZE |",
+        "|---|---|---|",
+        f"| 1 GiB copy, counter KiB per dispatch | {avg(fc[-3:]):.0f} | {avg(wc[-3:]):.0f} |",
+        f"| calibration scale (known bytes / counter bytes) | {fcal:.4f} | {wcal:.4f} |",
+        f"| replay step, scaled MB per launch (avg of {len(frep)}) | {f_rep/1e6:.1f} | {w_rep/1e6:.1f} |",
+        f"| recurrent step, scaled MB per launch (avg of {len(frec)}) | {f_rec/1e6:.1f} | {w_rec/1e6:.1f} |",
+        "",
+        f"Replay step: measured {(f_rep + w_rep)/1e6:.1f} MB per launch vs algorithmic {algo/1e6:.1f} MB "
+        f"(ratio {(f_rep + w_rep)/algo:.3f}).",
+        f"Recurrent step: measured {(f_rec + w_rec)/1e6:.1f} MB per launch vs algorithmic {algo_rec/1e6:.1f} MB "
+        f"(ratio {(f_rec + w_rec)/algo_rec:.3f}).",
+        f"State-transfer bytes per token, recurrent / replay (measured): {(f_rec + w_rec)/(f_rep + w_rep):.3f}.",
+        "",
+        f"- kernel_source_sha256_16: `{_kernel_source_hash()}`",
+        f"- traffic_bytes_per_launch: `{f_rep + w_rep:.0f}`",
+        f"- fetch_scale: `{fcal:.4f}`",
+        f"- write_scale: `{wcal:.4f}`",
+        "",
+    ]
+    open(out_md, "w").write("\n".join(lines))
+    print("\n".join(lines))
 
 
 if __name__ == "__main__":
