@@ -38,7 +38,7 @@ def decode_run(S0, x, Bm, Cm, dt, A, D, groups: int, L: int):
     return np.concatenate(ys, axis=0), cks
 
 
-def spec_run(S0, x, Bm, Cm, dt, A, D, n_keep, groups: int, L: int):
+def spec_run(S0, x, Bm, Cm, dt, A, D, n_keep, groups: int, L: int, keep_states: bool = True):
     """Speculative decoding over R rounds of T draft positions.
 
     x [R, T, batch, H, P]; Bm, Cm [R, T, batch, G, N]; dt [R, T, batch, H];
@@ -52,7 +52,8 @@ def spec_run(S0, x, Bm, Cm, dt, A, D, n_keep, groups: int, L: int):
       y      [R, T, batch, H, P]  outputs of every draft position,
       pos    [R, batch]           position count after each round,
       commit [R, batch]           whether the checkpoint was rewritten,
-      state  list of R arrays     true state after each round (fp64)."""
+      state  list of R arrays     true state after each round (fp64); only the
+                                  last round's when keep_states is False."""
     R, T, batch = x.shape[0], x.shape[1], x.shape[2]
     n_keep = np.asarray(n_keep, dtype=np.int32)
     S = _f64(S0)
@@ -66,7 +67,8 @@ def spec_run(S0, x, Bm, Cm, dt, A, D, n_keep, groups: int, L: int):
         ys.append(y)
         poss.append(pos.copy())
         commits.append(c)
-        states.append(S.copy())
+        if keep_states or r == R - 1:
+            states.append(S.copy())
     return {"y": np.stack(ys), "pos": np.stack(poss), "commit": np.stack(commits),
             "state": states}
 

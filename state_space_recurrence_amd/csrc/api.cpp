@@ -141,9 +141,9 @@ int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x, c
 int replayssm_verify(const rssm_desc *desc, const rssm_state *st, int32_t T, const void *x,
                      const void *B, const void *C, const void *dt, float *y, hipStream_t stream) {
     RSSM_TRY(check_desc(desc));
-    RSSM_TRY(check_state(desc, st));
     if (T < 1 || T > desc->max_draft)
         return fail(RSSM_E_CAPACITY, "verify: T = %d outside 1..max_draft (%d)", T, desc->max_draft);
+    RSSM_TRY(check_state(desc, st));
     if (desc->batch == 0) return RSSM_OK;
     if (!x || !B || !C || !dt || !y) return fail(RSSM_E_ARG, "verify: an input/output pointer is NULL");
     rssm::ReplayParams p = replay_params(desc, st);
@@ -160,9 +160,9 @@ int replayssm_verify(const rssm_desc *desc, const rssm_state *st, int32_t T, con
 int replayssm_accept(const rssm_desc *desc, const rssm_state *st, const int32_t *n_keep, int32_t T,
                      hipStream_t stream) {
     RSSM_TRY(check_desc(desc));
-    RSSM_TRY(check_state(desc, st));
     if (T < 1 || T > desc->max_draft)
         return fail(RSSM_E_CAPACITY, "accept: T = %d outside 1..max_draft (%d)", T, desc->max_draft);
+    RSSM_TRY(check_state(desc, st));
     if (desc->batch == 0) return RSSM_OK;
     if (!n_keep) return fail(RSSM_E_ARG, "accept: n_keep is NULL");
     rssm::ReplayParams p = replay_params(desc, st);

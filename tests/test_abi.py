@@ -1,0 +1,119 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "replayssm.h")
+
+
+@pytest.fixture(scope="module")
+def rs():
+    import state_space_recurrence_amd as rs
+    if not os.path.exists(rs.LIB_PATH):
+        from state_space_recurrence_amd import build
+        build.build()
+    rs.lib()
+    return rs
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(replayssm_\w+)\s*\(", src)))
+
+
+def test_header_declares_the_calls():
+    names = _declared()
+    for n in ("replayssm_step", "replayssm_verify", "replayssm_accept", "replayssm_commit",
+              "replayssm_recurrent_step"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(rs):
+    L = rs.lib()
+    missing = [n for n in _declared() if not hasattr(L, n)]
+    assert not missing, missing
+
+
+def _desc(rs, **kw):
+    d = dict(batch=4, heads=8, head_dim=64, d_state=128, groups=1, interval=16, max_draft=1,
+             in_dtype=rs.F32)
+    d.update(kw)
+    return rs._make_desc(d["batch"], d["heads"], d["head_dim"], d["d_state"], d["groups"],
+                         d["interval"], d["max_draft"], d["in_dtype"],
+                         ckpt_dtype=d.get("ckpt_dtype", rs.F32), out_dtype=d.get("out_dtype", rs.NONE),
+                         shared_lowp=d.get("shared_lowp", 0))
+
+
+@pytest.mark.parametrize("kw,code", [
+    ({}, 0),
+    ({"head_dim": 32}, -2),
+    ({"d_state": 64}, -2),
+    ({"heads": 6, "groups": 4}, -1),
+    ({"groups": 0}, -1),
+    ({"batch": -1}, -1),
+    ({"interval": 0}, -1),
+    ({"max_draft": 0}, -3),
+    ({"max_draft": 9}, -3),
+    ({"interval": 30, "max_draft": 4}, -3),
+    ({"in_dtype": 2}, -2),
+    ({"shared_lowp": 2}, -1),
+])
+def test_descriptor_validation(rs, kw, code):
+    L = rs.lib()
+    d = _desc(rs, **kw)
+    assert L.replayssm_check_desc(ctypes.byref(d)) == code
+    if code:
+        assert L.replayssm_last_error().decode()
+
+
+def test_null_arguments_rejected_before_launch(rs):
+    L = rs.lib()
+    d = _desc(rs)
+    st = rs.RssmState()
+    assert L.replayssm_step(None, ctypes.byref(st), None, None, None, None, None, None) == -1
+    assert L.replayssm_step(ctypes.byref(d), None, None, None, None, None, None, None) == -1
+    assert L.replayssm_step(ctypes.byref(d), ctypes.byref(st), None, None, None, None, None, None) == -1
+    assert "ckpt" in L.replayssm_last_error().decode()
+    assert L.replayssm_commit(ctypes.byref(d), ctypes.byref(st), None) == -1
+    assert L.replayssm_recurrent_step(ctypes.byref(d), None, None, None, None, None, None, None, None,
+                                      None) == -1
+
+
+def test_draft_count_checked(rs):
+    L = rs.lib()
+    d = _desc(rs, max_draft=5)
+    st = rs.RssmState()
+    assert L.replayssm_verify(ctypes.byref(d), ctypes.byref(st), 6, None, None, None, None, None, None) == -3
+    assert L.replayssm_verify(ctypes.byref(d), ctypes.byref(st), 0, None, None, None, None, None, None) == -3
+    assert L.replayssm_accept(ctypes.byref(d), ctypes.byref(st), None, 9, None) == -3
+    assert L.replayssm_recurrent_accept(ctypes.byref(d), None, None, 7, None) == -3
+
+
+def test_empty_batch_is_a_noop_without_device(rs):
+    L = rs.lib()
+    d = _desc(rs, batch=0)
+    st = rs.RssmState()
+    assert L.replayssm_step(ctypes.byref(d), ctypes.byref(st), None, None, None, None, None, None) == 0
+    assert L.replayssm_commit(ctypes.byref(d), ctypes.byref(st), None) == 0
+
+
+def test_buffer_capacity_and_strings(rs):
+    L = rs.lib()
+    assert L.replayssm_buffer_capacity(ctypes.byref(_desc(rs, interval=16, max_draft=5))) == 20
+    assert L.replayssm_buffer_capacity(ctypes.byref(_desc(rs, head_dim=7))) == 0
+    for code in (0, -1, -2, -3, -4, -5):
+        assert L.replayssm_status_string(code)
+    assert L.replayssm_version().decode().startswith("replayssm")
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    import state_space_recurrence_amd as rs
+    monkeypatch.setattr(rs, "_LIB", None)
+    monkeypatch.setattr(rs, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(rs.ReplaySSMError, match="missing"):
+        rs.lib()
