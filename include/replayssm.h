@@ -56,6 +56,25 @@
  *
  * Supported: P = 64, N = 128; in_dtype F32 or BF16; H % G == 0;
  * 1 <= L, 1 <= Tmax <= 8, Lcap <= 32.
+ *
+ * State formats (rssm_desc ckpt_dtype / out_dtype / shared_lowp):
+ *   F32  / NONE / 0 : fp32 checkpoint (outputs and updates).
+ *   BF16 or FP8_E4M3 / FP4_E2M1 / 0 : precision split (section 4): outputs
+ *       read the FP4 copy; a commit forms the new state in fp32 from the
+ *       update checkpoint and the buffer, stores it stochastically rounded
+ *       into the update checkpoint and re-quantises the FP4 copy from the same
+ *       fp32 values, so the copy's rounding never reaches later updates.
+ *   NONE / FP4_E2M1 / 1 : the FP4 copy is the only state (ablation).
+ *   BF16 or FP8_E4M3 / NONE / 0 : one rounded checkpoint for both.
+ * Rounding: bf16 / E4M3 (OCP "FN", unscaled, saturating at 448) by
+ * stochastic rounding -- up to the upper neighbour iff r16 / 2^16 <
+ * (|v| - lo) / (hi - lo), r16 the 16-bit half (e mod 8) of Philox4x32-10
+ * with key = seed and counter = (e / 8, interval, layer_id, 0), e the flat
+ * element index in [B,H,P,N] and interval the index of the interval the
+ * written state starts (intv[b] at load_checkpoint, intv[b] + 1 at a
+ * commit).  FP4: E2M1 codes with one E4M3 scale RNE(amax / 6) per 32
+ * consecutive elements of a row, codes RNE(|v| / scale) saturating at 6.
+ * B*H*P*N must be < 2^32 for the low-precision formats.
  */
 #ifndef REPLAYSSM_H_
 #define REPLAYSSM_H_
@@ -96,16 +115,16 @@ typedef struct rssm_desc {
     int32_t interval;     /* L: tokens per checkpoint interval (article: 16) */
     int32_t max_draft;    /* Tmax: largest T of a speculative round (1 if unused) */
     int32_t in_dtype;     /* rssm_dtype of x, B, C, dt and the buffers: F32 | BF16 */
-    int32_t ckpt_dtype;   /* checkpoint: F32, or BF16 / FP8_E4M3 (update checkpoint of the split) */
-    int32_t out_dtype;    /* NONE: outputs read ckpt; FP4_E2M1: separate output copy */
-    int32_t shared_lowp;  /* 1: the FP4 output copy is the only state (ablation) */
+    int32_t ckpt_dtype;   /* checkpoint: F32, or BF16 / FP8_E4M3 (stochastically rounded); NONE when shared_lowp */
+    int32_t out_dtype;    /* NONE: outputs read ckpt; FP4_E2M1: separate output copy (needs a BF16/FP8 ckpt) */
+    int32_t shared_lowp;  /* 1: the FP4 output copy is the only state (ablation; ckpt_dtype NONE) */
     int32_t layer_id;     /* stochastic-rounding stream: layer index */
     uint64_t seed;        /* stochastic-rounding stream: key */
 } rssm_desc;
 
 /* Device buffers of one layer (host struct of device pointers). */
 typedef struct rssm_state {
-    void *ckpt;           /* [B,H,P,N] ckpt_dtype; NULL when shared_lowp */
+    void *ckpt;           /* [B,H,P,N] ckpt_dtype (2, 1 or 4 bytes per element); NULL when shared_lowp */
     void *out_q;          /* [B,H,P,N/2] u8 when out_dtype == FP4_E2M1, else NULL */
     void *out_scale;      /* [B,H,P,N/32] u8 (E4M3) when out_dtype == FP4_E2M1 */
     void *xbuf;           /* [B,Lcap,H,P] in_dtype */

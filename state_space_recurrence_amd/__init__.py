@@ -136,17 +136,37 @@ class LayerState:
     Snapshot / restore of the whole logical state is a copy of these tensors.
     """
 
+    #: state formats: name -> (ckpt_dtype, out_dtype, shared_lowp)
+    FORMATS = {
+        "f32": (F32, NONE, 0),            # fp32 checkpoint (the article's performance setting)
+        "split-bf16": (BF16, FP4_E2M1, 0),  # bf16 SR update checkpoint + FP4 output copy
+        "split-e4m3": (FP8_E4M3, FP4_E2M1, 0),  # E4M3 SR update checkpoint + FP4 output copy
+        "shared-fp4": (NONE, FP4_E2M1, 1),  # the FP4 copy is the only state (ablation)
+        "low-bf16": (BF16, NONE, 0),      # one bf16 SR checkpoint for outputs and updates
+        "low-e4m3": (FP8_E4M3, NONE, 0),  # one E4M3 SR checkpoint for outputs and updates
+    }
+
     def __init__(self, batch: int, heads: int, groups: int, A: torch.Tensor, D: torch.Tensor, *,
                  head_dim: int = 64, d_state: int = 128, interval: int = 16, max_draft: int = 1,
                  in_dtype: torch.dtype = torch.bfloat16, device="cuda", layer_id: int = 0,
-                 seed: int = 0):
+                 seed: int = 0, state_format: str = "f32", debug_prequant: bool = False):
         self.batch, self.heads, self.groups = batch, heads, groups
         self.head_dim, self.d_state, self.interval, self.max_draft = head_dim, d_state, interval, max_draft
         self.in_dtype = in_dtype
         self.layer_id, self.seed = layer_id, seed
         self.lcap = buffer_capacity(interval, max_draft)
+        self.state_format = state_format
+        ck, od, sh = self.FORMATS[state_format]
         dev = torch.device(device)
-        self.ckpt = torch.zeros(batch, heads, head_dim, d_state, dtype=torch.float32, device=dev)
+        shape = (batch, heads, head_dim, d_state)
+        ck_torch = {F32: torch.float32, BF16: torch.int16, FP8_E4M3: torch.uint8}
+        self.ckpt = torch.zeros(shape, dtype=ck_torch[ck], device=dev) if ck != NONE else None
+        if od == FP4_E2M1:
+            self.out_q = torch.zeros(batch, heads, head_dim, d_state // 2, dtype=torch.uint8, device=dev)
+            self.out_scale = torch.zeros(batch, heads, head_dim, d_state // 32, dtype=torch.uint8, device=dev)
+        else:
+            self.out_q = self.out_scale = None
+        self.debug_prequant = torch.zeros(shape, dtype=torch.float32, device=dev) if debug_prequant else None
         self.xbuf = torch.zeros(batch, self.lcap, heads, head_dim, dtype=in_dtype, device=dev)
         self.bbuf = torch.zeros(batch, self.lcap, groups, d_state, dtype=in_dtype, device=dev)
         self.dtbuf = torch.zeros(batch, self.lcap, heads, dtype=in_dtype, device=dev)
@@ -158,20 +178,22 @@ class LayerState:
         self.A = A.to(device=dev, dtype=torch.float32).contiguous()
         self.D = D.to(device=dev, dtype=torch.float32).contiguous()
         self._desc = _make_desc(batch, heads, head_dim, d_state, groups, interval, max_draft,
-                                in_dtype, layer_id=layer_id, seed=seed)
+                                in_dtype, ckpt_dtype=ck, out_dtype=od, shared_lowp=sh,
+                                layer_id=layer_id, seed=seed)
         _check(lib().replayssm_check_desc(ctypes.byref(self._desc)))
 
     def desc(self) -> RssmDesc:
         return self._desc
 
     def cstate(self) -> RssmState:
-        return RssmState(_ptr(self.ckpt), None, None, _ptr(self.xbuf), _ptr(self.bbuf),
-                         _ptr(self.dtbuf), _ptr(self.pos), _ptr(self.intv), _ptr(self.work),
-                         _ptr(self.A), _ptr(self.D), None)
+        return RssmState(_ptr(self.ckpt), _ptr(self.out_q), _ptr(self.out_scale), _ptr(self.xbuf),
+                         _ptr(self.bbuf), _ptr(self.dtbuf), _ptr(self.pos), _ptr(self.intv),
+                         _ptr(self.work), _ptr(self.A), _ptr(self.D), _ptr(self.debug_prequant))
 
     def tensors(self):
-        return {"ckpt": self.ckpt, "xbuf": self.xbuf, "bbuf": self.bbuf, "dtbuf": self.dtbuf,
-                "pos": self.pos, "intv": self.intv}
+        t = {"ckpt": self.ckpt, "out_q": self.out_q, "out_scale": self.out_scale, "xbuf": self.xbuf,
+             "bbuf": self.bbuf, "dtbuf": self.dtbuf, "pos": self.pos, "intv": self.intv}
+        return {k: v for k, v in t.items() if v is not None}
 
     def snapshot(self):
         return {k: v.clone() for k, v in self.tensors().items()}
@@ -235,7 +257,9 @@ def commit(ls: LayerState, stream=None) -> None:
 
 
 def load_checkpoint(ls: LayerState, src: torch.Tensor, stream=None) -> None:
-    """Set the checkpoint from an fp32 state [B,H,P,N] and reset positions."""
+    """Set the checkpoint from an fp32 state [B,H,P,N] and reset positions
+    (quantising into the layer's state format; the rounding stream index is
+    the slot's current intv)."""
     _need(src, (ls.batch, ls.heads, ls.head_dim, ls.d_state), torch.float32, "src")
     st = ls.cstate()
     _check(lib().replayssm_load_checkpoint(ctypes.byref(ls._desc), ctypes.byref(st), _ptr(src),

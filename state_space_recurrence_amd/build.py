@@ -31,7 +31,10 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libreplayssm)")
 
 
-COMMON = ["-O3", "-std=c++17", "-fPIC", "-I", INCLUDE, "-I", CSRC,
+# -ffp-contract=on: a*b+c is fused only inside one expression, never across
+# statements, so the same source arithmetic compiles to the same roundings in
+# every kernel that inlines it (results do not depend on the calling kernel).
+COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=on", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-Wno-unused-command-line-argument"]
 

@@ -37,6 +37,15 @@ int heads_per_wg(const rssm_desc *d) {
     return hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
 }
 
+// Low-precision mode of a descriptor (rssm::SplitMode), or -1 for the fp32
+// checkpoint path.
+int split_mode(const rssm_desc *d) {
+    if (d->shared_lowp) return rssm::kSharedFP4;
+    if (d->ckpt_dtype == RSSM_BF16) return d->out_dtype == RSSM_FP4_E2M1 ? rssm::kSplitBF16 : rssm::kLowBF16;
+    if (d->ckpt_dtype == RSSM_FP8_E4M3) return d->out_dtype == RSSM_FP4_E2M1 ? rssm::kSplitE4M3 : rssm::kLowE4M3;
+    return -1;
+}
+
 int check_desc(const rssm_desc *d) {
     if (!d) return fail(RSSM_E_ARG, "desc is NULL");
     if (d->batch < 0) return fail(RSSM_E_ARG, "batch %d < 0", d->batch);
@@ -54,27 +63,34 @@ int check_desc(const rssm_desc *d) {
         return fail(RSSM_E_CAPACITY, "interval + max_draft - 1 = %d exceeds %d", lcap_of(d), kMaxLcap);
     if (d->in_dtype != RSSM_F32 && d->in_dtype != RSSM_BF16)
         return fail(RSSM_E_UNSUPPORTED, "in_dtype %d: only F32 and BF16 inputs", d->in_dtype);
-    if (d->ckpt_dtype != RSSM_F32 && d->ckpt_dtype != RSSM_BF16 && d->ckpt_dtype != RSSM_FP8_E4M3)
-        return fail(RSSM_E_UNSUPPORTED, "ckpt_dtype %d", d->ckpt_dtype);
-    if (d->out_dtype != RSSM_NONE && d->out_dtype != RSSM_FP4_E2M1)
-        return fail(RSSM_E_UNSUPPORTED, "out_dtype %d", d->out_dtype);
     if (d->shared_lowp != 0 && d->shared_lowp != 1)
         return fail(RSSM_E_ARG, "shared_lowp must be 0 or 1");
-    if (d->shared_lowp && d->out_dtype != RSSM_FP4_E2M1)
-        return fail(RSSM_E_ARG, "shared_lowp requires out_dtype FP4_E2M1");
-    if (d->ckpt_dtype == RSSM_F32 && d->out_dtype != RSSM_NONE)
-        return fail(RSSM_E_UNSUPPORTED, "an FP4 output copy needs a BF16/FP8 update checkpoint (or shared_lowp)");
-    if (d->ckpt_dtype != RSSM_F32 || d->out_dtype != RSSM_NONE)
-        return fail(RSSM_E_UNSUPPORTED, "the precision-split formats are not built in this library yet");
+    if (d->out_dtype != RSSM_NONE && d->out_dtype != RSSM_FP4_E2M1)
+        return fail(RSSM_E_UNSUPPORTED, "out_dtype %d: only NONE or FP4_E2M1", d->out_dtype);
+    if (d->shared_lowp) {
+        if (d->out_dtype != RSSM_FP4_E2M1 || d->ckpt_dtype != RSSM_NONE)
+            return fail(RSSM_E_ARG, "shared_lowp needs out_dtype FP4_E2M1 and ckpt_dtype NONE "
+                                    "(the FP4 copy is the only state)");
+    } else {
+        if (d->ckpt_dtype != RSSM_F32 && d->ckpt_dtype != RSSM_BF16 && d->ckpt_dtype != RSSM_FP8_E4M3)
+            return fail(RSSM_E_UNSUPPORTED, "ckpt_dtype %d: F32, BF16 or FP8_E4M3", d->ckpt_dtype);
+        if (d->ckpt_dtype == RSSM_F32 && d->out_dtype != RSSM_NONE)
+            return fail(RSSM_E_UNSUPPORTED, "an FP4 output copy goes with a BF16 / FP8 update checkpoint");
+    }
     if ((int64_t)d->batch * d->n_heads > (int64_t)1 << 24)
         return fail(RSSM_E_ARG, "batch * n_heads too large");
+    if (split_mode(d) >= 0 && (int64_t)d->batch * d->n_heads * d->head_dim * d->d_state > 0xFFFFFFFFll)
+        return fail(RSSM_E_ARG, "low-precision state: B*H*P*N must fit the 32-bit element index of the "
+                                "rounding stream");
     return RSSM_OK;
 }
 
 int check_state(const rssm_desc *d, const rssm_state *s) {
     if (!s) return fail(RSSM_E_ARG, "state is NULL");
     if (d->batch == 0) return RSSM_OK;
-    if (!s->ckpt) return fail(RSSM_E_ARG, "state->ckpt is NULL");
+    if (!d->shared_lowp && !s->ckpt) return fail(RSSM_E_ARG, "state->ckpt is NULL");
+    if (d->out_dtype == RSSM_FP4_E2M1 && (!s->out_q || !s->out_scale))
+        return fail(RSSM_E_ARG, "state->out_q / out_scale are NULL with an FP4 output copy");
     if (!s->xbuf || !s->bbuf || !s->dtbuf) return fail(RSSM_E_ARG, "state buffers are NULL");
     if (!s->pos || !s->intv || !s->work) return fail(RSSM_E_ARG, "state pos/intv/work is NULL");
     if (!s->A || !s->D) return fail(RSSM_E_ARG, "state A/D is NULL");
@@ -100,6 +116,12 @@ rssm::ReplayParams replay_params(const rssm_desc *d, const rssm_state *s) {
     p.T = 1;
     p.hpw = heads_per_wg(d);
     p.wg_per_slot = d->n_heads / p.hpw;
+    p.u = s->ckpt;
+    p.oq = static_cast<uint8_t *>(s->out_q);
+    p.os = static_cast<uint8_t *>(s->out_scale);
+    p.dbg = s->debug_prequant;
+    p.seed = d->seed;
+    p.layer = d->layer_id;
     return p;
 }
 
@@ -135,7 +157,10 @@ int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x, c
     p.Cm = C;
     p.dt = dt;
     p.y = y;
-    return hip_status(rssm::launch_replay_step(p, desc->in_dtype == RSSM_BF16, stream), "replay step launch");
+    const bool bf = desc->in_dtype == RSSM_BF16;
+    const int mode = split_mode(desc);
+    if (mode >= 0) return hip_status(rssm::launch_split_step(p, bf, mode, stream), "split step launch");
+    return hip_status(rssm::launch_replay_step(p, bf, stream), "replay step launch");
 }
 
 int replayssm_verify(const rssm_desc *desc, const rssm_state *st, int32_t T, const void *x,
@@ -153,8 +178,10 @@ int replayssm_verify(const rssm_desc *desc, const rssm_state *st, int32_t T, con
     p.dt = dt;
     p.y = y;
     p.T = T;
-    return hip_status(rssm::launch_replay_verify(p, desc->in_dtype == RSSM_BF16, stream),
-                      "replay verify launch");
+    const bool bf = desc->in_dtype == RSSM_BF16;
+    const int mode = split_mode(desc);
+    if (mode >= 0) return hip_status(rssm::launch_split_verify(p, bf, mode, stream), "split verify launch");
+    return hip_status(rssm::launch_replay_verify(p, bf, stream), "replay verify launch");
 }
 
 int replayssm_accept(const rssm_desc *desc, const rssm_state *st, const int32_t *n_keep, int32_t T,
@@ -168,8 +195,10 @@ int replayssm_accept(const rssm_desc *desc, const rssm_state *st, const int32_t 
     rssm::ReplayParams p = replay_params(desc, st);
     p.n_keep = n_keep;
     p.T = T;
-    return hip_status(rssm::launch_replay_commit(p, desc->in_dtype == RSSM_BF16, true, stream),
-                      "accept launch");
+    const bool bf = desc->in_dtype == RSSM_BF16;
+    const int mode = split_mode(desc);
+    if (mode >= 0) return hip_status(rssm::launch_split_commit(p, bf, mode, true, stream), "split accept launch");
+    return hip_status(rssm::launch_replay_commit(p, bf, true, stream), "accept launch");
 }
 
 int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t stream) {
@@ -177,8 +206,10 @@ int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t st
     RSSM_TRY(check_state(desc, st));
     if (desc->batch == 0) return RSSM_OK;
     rssm::ReplayParams p = replay_params(desc, st);
-    return hip_status(rssm::launch_replay_commit(p, desc->in_dtype == RSSM_BF16, false, stream),
-                      "commit launch");
+    const bool bf = desc->in_dtype == RSSM_BF16;
+    const int mode = split_mode(desc);
+    if (mode >= 0) return hip_status(rssm::launch_split_commit(p, bf, mode, false, stream), "split commit launch");
+    return hip_status(rssm::launch_replay_commit(p, bf, false, stream), "commit launch");
 }
 
 int replayssm_load_checkpoint(const rssm_desc *desc, const rssm_state *st, const float *src,
@@ -187,6 +218,14 @@ int replayssm_load_checkpoint(const rssm_desc *desc, const rssm_state *st, const
     RSSM_TRY(check_state(desc, st));
     if (desc->batch == 0) return RSSM_OK;
     if (!src) return fail(RSSM_E_ARG, "load_checkpoint: src is NULL");
+    const int mode = split_mode(desc);
+    if (mode >= 0) {
+        rssm::ReplayParams p = replay_params(desc, st);
+        p.src = src;
+        p.dbg = nullptr;
+        RSSM_TRY(hip_status(rssm::launch_split_load(p, mode, stream), "load_checkpoint quantise"));
+        return hip_status(rssm::launch_zero_pos(st->pos, desc->batch, stream), "load_checkpoint pos reset");
+    }
     const size_t bytes = (size_t)desc->batch * desc->n_heads * desc->head_dim * desc->d_state * sizeof(float);
     RSSM_TRY(hip_status(hipMemcpyAsync(st->ckpt, src, bytes, hipMemcpyDeviceToDevice, stream),
                         "load_checkpoint copy"));

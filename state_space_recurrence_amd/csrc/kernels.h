@@ -26,6 +26,23 @@ struct ReplayParams {
     int batch, H, G, L, Lcap, T;
     int hpw;                // heads (waves) per workgroup
     int wg_per_slot;        // H / hpw
+    // precision split (ignored by the fp32 kernels)
+    void *u;                // update checkpoint [B,H,P,N]: bf16 (u16) or E4M3 (u8); NULL when shared
+    uint8_t *oq;            // FP4 output copy codes [B,H,P,N/2]
+    uint8_t *os;            // FP4 output copy scales [B,H,P,N/32] (E4M3)
+    float *dbg;             // optional pre-rounding dump [B,H,P,N] fp32
+    const float *src;       // load_checkpoint source [B,H,P,N] fp32
+    uint64_t seed;
+    int layer;
+};
+
+// Low-precision state modes of the precision split.
+enum SplitMode {
+    kSplitBF16 = 0,   // outputs read the FP4 copy; updates read/write a bf16 checkpoint (SR)
+    kSplitE4M3 = 1,   // same with an E4M3 update checkpoint
+    kSharedFP4 = 2,   // the FP4 copy is the only state (outputs and updates)
+    kLowBF16 = 3,     // one bf16 checkpoint serves outputs and updates (no copy)
+    kLowE4M3 = 4,     // one E4M3 checkpoint serves outputs and updates (no copy)
 };
 
 // Arguments of the conventional (recurrent) baseline kernels.
@@ -44,6 +61,10 @@ hipError_t launch_replay_step(const ReplayParams &p, bool in_bf16, hipStream_t s
 hipError_t launch_replay_verify(const ReplayParams &p, bool in_bf16, hipStream_t s);
 hipError_t launch_replay_commit(const ReplayParams &p, bool in_bf16, bool accept, hipStream_t s);
 hipError_t launch_zero_pos(int32_t *pos, int batch, hipStream_t s);
+hipError_t launch_split_step(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
+hipError_t launch_split_verify(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
+hipError_t launch_split_commit(const ReplayParams &p, bool in_bf16, int mode, bool accept, hipStream_t s);
+hipError_t launch_split_load(const ReplayParams &p, int mode, hipStream_t s);
 hipError_t launch_recurrent(const RecurrentParams &p, bool in_bf16, bool pool, hipStream_t s);
 hipError_t launch_recurrent_accept(int32_t *sel, const int32_t *n_keep, int batch, int T,
                                    int Tmax, hipStream_t s);

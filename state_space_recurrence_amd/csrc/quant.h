@@ -1,0 +1,205 @@
+// quant.h -- low-precision state formats of the precision split on gfx950.
+//
+// Article ("NVIDIA ReplaySSM: hybrid model SSM decoding with a state buffer"),
+// section 4: a high-precision checkpoint for updates, a separate low-precision
+// copy for outputs (4-bit float), and updates stored in 16- or 8-bit floats
+// with stochastic rounding (a rounding to one of the two neighbouring
+// representable values with probability set by the distance).
+//
+// Formats (little-endian, row-major like the fp32 checkpoint):
+//   bf16   : the upper 16 bits of an fp32.
+//   E4M3   : OCP FP8 E4M3 ("FN"): bias 7, no infinities, S.1111.111 = NaN,
+//            max 448, subnormal step 2^-9.  Stored unscaled.
+//   FP4    : OCP MX E2M1 {0, .5, 1, 1.5, 2, 3, 4, 6} x sign, two codes per
+//            byte (even element in the low nibble), one E4M3 scale per 32
+//            consecutive elements of a row; scale = RNE_E4M3(amax / 6),
+//            code = RNE_E2M1(|v| / scale) saturating at 6 (zero when the
+//            scale is zero).
+// Stochastic rounding: with lo <= |v| < hi the neighbouring magnitudes and
+// r16 a 16-bit draw, round up iff r16 / 2^16 < (|v| - lo) / (hi - lo);
+// sign kept; saturating at the largest finite value; NaN -> canonical NaN.
+// The draw for element e (flat index ((slot*H + h)*P + p)*N + n of the
+// layer) when the state starting interval i is written:
+//   Philox4x32-10 (Salmon et al., SC'11), key = (seed lo, seed hi),
+//   counter = (e >> 3, i, layer, 0); r16 = 16-bit half (e & 7) of the
+//   128-bit output, words in order, low half first.
+//
+// Everything here works on integer bit patterns and exact fp32 products
+// (threshold products t * s have at most 7 significant bits), so results
+// are exact and independent of division rounding.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rssm {
+
+// ------------------------------------------------------------------ Philox --
+struct Philox4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                                 uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return {c0, c1, c2, c3};
+}
+
+// The four 16-bit draws for elements e0..e0+3 (e0 a multiple of 4).
+__device__ __forceinline__ void sr_draws4(uint64_t seed, uint32_t layer, uint32_t interval, uint32_t e0,
+                                          uint32_t (&r)[4]) {
+    const Philox4 o = philox4x32_10(e0 >> 3, interval, layer, 0, (uint32_t)seed, (uint32_t)(seed >> 32));
+    const uint32_t wa = (e0 & 4) ? o.z : o.x;
+    const uint32_t wb = (e0 & 4) ? o.w : o.y;
+    r[0] = wa & 0xFFFFu;
+    r[1] = wa >> 16;
+    r[2] = wb & 0xFFFFu;
+    r[3] = wb >> 16;
+}
+
+// ------------------------------------------------------------------- bf16 --
+__device__ __forceinline__ float bf16_decode(uint32_t code16) { return __uint_as_float(code16 << 16); }
+
+__device__ __forceinline__ uint32_t bf16_sr(float v, uint32_t r16) {
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    if (mag > 0x7F800000u) return 0x7FC0u;                     // NaN
+    const uint32_t sign = (bits >> 16) & 0x8000u;
+    if (mag == 0x7F800000u) return sign | 0x7F7Fu;             // inf saturates
+    uint32_t code = mag >> 16;
+    if (r16 < (mag & 0xFFFFu)) code += 1;                       // carries into the exponent
+    if (code > 0x7F7Fu) code = 0x7F7Fu;                         // saturate instead of inf
+    return sign | code;
+}
+
+// ------------------------------------------------------------------- E4M3 --
+__device__ __forceinline__ float e4m3_decode(uint32_t code8) {
+    const uint32_t s = (code8 & 0x80u) << 24;
+    const uint32_t e = (code8 >> 3) & 0xFu, m = code8 & 7u;
+    if (e == 0xFu && m == 7u) return __uint_as_float(0x7FC00000u);
+    float v;
+    if (e == 0) v = (float)m * 0.001953125f;                      // m * 2^-9
+    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));     // 2^(e-7) * (1 + m/8)
+    return __uint_as_float(__float_as_uint(v) | s);
+}
+
+// Magnitude (fp32 bits, finite, < 448) -> (grid multiple k, quantum exponent
+// qe) with k * 2^qe <= |v| and the dropped part D over s bits.
+struct GridSplit {
+    uint32_t lo;     // |v| truncated onto the E4M3 grid, in units of 2^qe
+    uint32_t rem;    // dropped bits (value rem * 2^(qe - s))
+    int s;           // number of dropped bits (>= 20)
+    int qe;          // quantum exponent: -9 in the subnormal range, e - 3 above
+};
+
+__device__ __forceinline__ GridSplit e4m3_split(uint32_t mag) {
+    const int E = (int)(mag >> 23);
+    const uint32_t M = E ? ((mag & 0x7FFFFFu) | 0x800000u) : (mag & 0x7FFFFFu);
+    const int u = E ? E - 150 : -149;                 // exponent of the fp32 ulp
+    const int qe = (E - 127 >= -6) ? (E - 127 - 3) : -9;
+    const int s = qe - u;
+    GridSplit g;
+    g.s = s;
+    g.qe = qe;
+    g.lo = s >= 32 ? 0u : (M >> s);
+    g.rem = s >= 32 ? M : (M & ((1u << s) - 1u));
+    return g;
+}
+
+// E4M3 code of magnitude k * 2^qe (k on the grid of that binade or below).
+__device__ __forceinline__ uint32_t e4m3_encode_grid(uint32_t k, int qe) {
+    if (qe == -9) return k;                                  // subnormals; k == 8 is 2^-6
+    return ((uint32_t)(qe + 3 + 7) << 3) + (k - 8u);         // k in [8, 16]
+}
+
+constexpr uint32_t kE4M3MaxBits = 0x43E00000u;   // 448.0f
+
+__device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t r16) {
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    if (mag > 0x7F800000u) return 0x7Fu;                      // NaN
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    if (mag >= kE4M3MaxBits) return sign | 0x7Eu;              // saturate at 448
+    const GridSplit g = e4m3_split(mag);
+    // up iff r16 * 2^s < rem * 2^16  (s >= 20 here)
+    const int sh = g.s - 16;
+    const bool up = sh >= 40 ? (r16 == 0u && g.rem != 0u) : (((uint64_t)r16 << sh) < (uint64_t)g.rem);
+    uint32_t code = e4m3_encode_grid(g.lo + (up ? 1u : 0u), g.qe);
+    if (code > 0x7Eu) code = 0x7Eu;
+    return sign | code;
+}
+
+// Round-to-nearest-even of a non-negative finite fp32 magnitude to E4M3,
+// saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_rne_mag(float m) {
+    const uint32_t mag = __float_as_uint(m);
+    if (mag >= kE4M3MaxBits) return 0x7Eu;
+    const GridSplit g = e4m3_split(mag);
+    // compare rem with half a quantum (2^(s-1)); ties to even k
+    bool up;
+    if (g.s >= 33) up = false;                          // rem < 2^24 <= half quantum
+    else {
+        const uint64_t half = (uint64_t)1 << (g.s - 1);
+        up = (uint64_t)g.rem > half || ((uint64_t)g.rem == half && (g.lo & 1u));
+    }
+    uint32_t code = e4m3_encode_grid(g.lo + (up ? 1u : 0u), g.qe);
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// ------------------------------------------------------------------- FP4 --
+__device__ __forceinline__ float e2m1_decode(uint32_t code4) {
+    // magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6
+    const uint32_t e = (code4 >> 1) & 3u, m = code4 & 1u;
+    const float mag = e == 0 ? 0.5f * (float)m : __uint_as_float(((e + 126u) << 23) | (m << 22));
+    return (code4 & 8u) ? -mag : mag;
+}
+
+// Scale code of a 32-element block from its max magnitude: RNE_E4M3(amax/6),
+// decided exactly: start from the rounded quotient and fix the result with
+// exact comparisons against 6 x the midpoints between neighbouring codes.
+__device__ __forceinline__ uint32_t fp4_scale_code(float amax) {
+    uint32_t c = e4m3_rne_mag(amax / 6.0f);
+    // step up while amax is beyond the midpoint to the next code
+    if (c < 0x7Eu) {
+        const float mid6 = 3.0f * (e4m3_decode(c) + e4m3_decode(c + 1));   // 6 * midpoint, exact
+        if (amax > mid6 || (amax == mid6 && (c & 1u))) c += 1;
+    }
+    if (c > 0u) {
+        const float mid6 = 3.0f * (e4m3_decode(c - 1) + e4m3_decode(c));
+        if (amax < mid6 || (amax == mid6 && (c & 1u))) c -= 1;
+    }
+    return c;
+}
+
+// E2M1 code (sign in bit 3) of v against scale s > 0, by exact threshold
+// comparisons of |v| with t * s, t in {.25, .75, 1.25, 1.75, 2.5, 3.5, 5};
+// midpoints go to the even mantissa (0, 1, 2, 4).
+struct Fp4Thresholds {
+    float t025, t075, t125, t175, t250, t350, t500;
+};
+
+__device__ __forceinline__ Fp4Thresholds fp4_thresholds(float s) {
+    return {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
+}
+
+__device__ __forceinline__ uint32_t fp4_encode(float v, const Fp4Thresholds &t, bool zero_scale) {
+    const float a = fabsf(v);
+    uint32_t k = (a > t.t025) + (a >= t.t075) + (a > t.t125) + (a >= t.t175) + (a > t.t250) +
+                 (a >= t.t350) + (a > t.t500);
+    if (zero_scale) k = 0;
+    return k | ((__float_as_uint(v) >> 28) & 8u);
+}
+
+}  // namespace rssm

@@ -1,0 +1,472 @@
+// replay_common.h -- pieces shared by the fp32 and the low-precision replay
+// kernels: workgroup -> (slot, head) mapping, position publication, the
+// per-chunk commit of fp32 rows and the LDS layout of commit coefficients.
+#pragma once
+
+#include "device_common.h"
+#include "kernels.h"
+
+namespace rssm {
+namespace {
+
+constexpr int kMaxHpw = 4;
+constexpr int kNB = 2;   // checkpoint chunks in flight per wave
+
+struct Slot {
+    int b, tile, wave, lane, h, g, c, hf, prow, hpg;
+};
+
+__device__ __forceinline__ Slot slot_of(const ReplayParams &a) {
+    Slot s;
+    const int wg = xcd_remap(blockIdx.x, gridDim.x);
+    s.b = wg / a.wg_per_slot;
+    s.tile = wg - s.b * a.wg_per_slot;
+    s.wave = threadIdx.x >> 6;
+    s.lane = threadIdx.x & 63;
+    s.h = s.tile * a.hpw + s.wave;
+    s.hpg = a.H / a.G;
+    s.g = (s.tile * a.hpw) / s.hpg;
+    s.c = s.lane & 31;
+    s.hf = s.lane >> 5;
+    s.prow = 2 * s.c + s.hf;
+    return s;
+}
+
+// Lane base pointer into head (b,h) of an fp32 state: row hf, columns 4c..;
+// value index i adds i * 2 rows.
+__device__ __forceinline__ float *state_ptr(float *base, const Slot &s, int H) {
+    return base + ((size_t)(s.b * H + s.h) * kP + s.hf) * kN + 4 * s.c;
+}
+
+__device__ __forceinline__ void load_chunk(float4 (&buf)[kPerChunk], const float *p, int c) {
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m)
+        buf[m] = stream_load4(p + (size_t)chunk_index(c, m) * 2 * kN);
+}
+
+// Last-arriving workgroup of slot b publishes the slot's new position (and
+// interval count).  Every workgroup of the slot read pos[b] before arriving.
+__device__ __forceinline__ void publish_position(const ReplayParams &a, int b, int new_pos,
+                                                 bool committed) {
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int old = atomicAdd(&a.work[b], 1);
+        if (old == a.wg_per_slot - 1) {
+            a.work[b] = 0;
+            a.pos[b] = new_pos;
+            if (committed) a.intv[b] += 1;
+        }
+    }
+}
+
+// Commit coefficients cs = w_j x_j[r] live in LDS as [hf][c][j][m] for row
+// r = 2(c + 4m) + hf, so the 8 coefficients one chunk needs for entry j are
+// two contiguous 16-byte reads (the same address across a half-wave).
+template <int KMAX>
+__device__ __forceinline__ int cs_index(int hf, int c, int j, int m) {
+    return ((hf * kChunks + c) * KMAX + j) * kPerChunk + m;
+}
+
+// Rewrite the 8 rows of chunk c in place:
+//   S_new[r] = lam * S0[r] + sum_j cs[r][j] * B_j[4c..4c+3]
+// (cs zero for j >= K).  Entry-outer order keeps one widened B_j slice and
+// 8 coefficients live at a time.
+template <typename TIn, int KMAX>
+__device__ __forceinline__ void commit_chunk(float4 (&st)[kPerChunk], int c, float lam,
+                                             const float *cs, const typename io<TIn>::raw4 (&Bj)[KMAX],
+                                             int hf, float *dst) {
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m) {
+        st[m].x *= lam; st[m].y *= lam; st[m].z *= lam; st[m].w *= lam;
+    }
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        const float4 b = io<TIn>::widen_here(Bj[j]);
+        const float *cp = cs + cs_index<KMAX>(hf, c, j, 0);
+        const float4 c0 = *reinterpret_cast<const float4 *>(cp);
+        const float4 c1 = *reinterpret_cast<const float4 *>(cp + 4);
+        const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+        for (int m = 0; m < kPerChunk; ++m) {
+            st[m].x += cf[m] * b.x;
+            st[m].y += cf[m] * b.y;
+            st[m].z += cf[m] * b.z;
+            st[m].w += cf[m] * b.w;
+        }
+        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound hoisted LDS reads
+    }
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m)
+        stream_store4(dst + (size_t)chunk_index(c, m) * 2 * kN, st[m]);
+}
+
+
+// ------------------------------------------------------------------------
+// Standard-step prologue: everything that does not read the checkpoint.
+// ------------------------------------------------------------------------
+template <int KMAX>
+struct StepSmem {
+    float l[kMaxHpw][KMAX];        // A dt_j
+    float dt[kMaxHpw][KMAX];       // dt_j
+    float gram[KMAX];              // B_j . C  (one group per workgroup)
+    float w[kMaxHpw][KMAX];        // w_j = dt_j exp(sum_{j<i<K} l_i), zero for j >= K
+    float cy[kMaxHpw][KMAX];       // w_j gram_j, zero for j >= K
+    float cs[kMaxHpw][kP * KMAX];  // commit coefficients w_j x_j[r] (cs_index layout)
+};
+
+struct StepIn {
+    int k, K;
+    bool commit;
+    size_t HP, GN;
+    const void *xin, *Bin, *Cin, *dtin, *xb, *bb, *db;   // typed by the caller
+};
+
+// Reads pos (clamped into 0..L-1, flagged otherwise) and sets the slot's
+// input / buffer pointers.
+template <typename TIn>
+__device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s) {
+    StepIn in;
+    int k = a.pos[s.b];
+    if (k < 0 || k > a.L - 1) {
+        if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrPos);
+        k = k < 0 ? 0 : a.L - 1;
+    }
+    in.k = k;
+    in.K = k + 1;
+    in.commit = (in.K == a.L);
+    in.HP = (size_t)a.H * kP;
+    in.GN = (size_t)a.G * kN;
+    in.xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.b * in.HP + (size_t)s.h * kP;
+    in.Bin = reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.b * in.GN + (size_t)s.g * kN;
+    in.Cin = reinterpret_cast<const TIn *>(a.Cm) + (size_t)s.b * in.GN + (size_t)s.g * kN;
+    in.dtin = reinterpret_cast<const TIn *>(a.dt) + (size_t)s.b * a.H + s.h;
+    in.xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)s.b * a.Lcap * in.HP + (size_t)s.h * kP;
+    in.bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * in.GN + (size_t)s.g * kN;
+    in.db = reinterpret_cast<const TIn *>(a.dtbuf) + (size_t)s.b * a.Lcap * a.H + s.h;
+    return in;
+}
+
+// Decay prep, Gram row, replay weights and the buffer part of the output for
+// row `prow` of this lane; on commit steps also the commit coefficients (LDS)
+// and this lane's B_j slices (columns 4c..4c+3, raw).  Returns Lambda_K in
+// *lam and sum_j w_j g_j x_j[prow] + D x[prow] in *ybuf.
+template <typename TIn, int KMAX>
+__device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot &s, const StepIn &in,
+                                              int prow, StepSmem<KMAX> &sm, float *lam, float *ybuf,
+                                              typename io<TIn>::raw4 (&Bj)[KMAX]) {
+    const int k = in.k, K = in.K;
+    const TIn *xin = static_cast<const TIn *>(in.xin);
+    const TIn *Bin = static_cast<const TIn *>(in.Bin);
+    const TIn *Cin = static_cast<const TIn *>(in.Cin);
+    const TIn *xb = static_cast<const TIn *>(in.xb);
+    const TIn *bb = static_cast<const TIn *>(in.bb);
+    const TIn *db = static_cast<const TIn *>(in.db);
+
+    float xv[KMAX];   // x_j[prow] of every entry (entry k is the current token)
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        const TIn *px = (j < k) ? xb + (size_t)j * in.HP + prow : xin + prow;
+        xv[j] = io<TIn>::load1(px);
+    }
+    const float xcur = io<TIn>::load1(xin + prow);
+    const float Ah = a.A[s.h], Dh = a.D[s.h];
+
+    if (s.lane < K) {
+        const TIn *pd = (s.lane < k) ? db + (size_t)s.lane * a.H : static_cast<const TIn *>(in.dtin);
+        const float d = io<TIn>::load1(pd);
+        sm.dt[s.wave][s.lane] = d;
+        sm.l[s.wave][s.lane] = Ah * d;
+    }
+    {   // Gram row g_j = B_j . C, 16 lanes x 8 elements per dot
+        const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4, ngrp = blockDim.x >> 4;
+        const float4 c0 = io<TIn>::load4(Cin + 8 * t16), c1 = io<TIn>::load4(Cin + 8 * t16 + 4);
+        for (int j = grp; j < K; j += ngrp) {
+            const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin;
+            const float4 b0 = io<TIn>::load4(pb + 8 * t16), b1 = io<TIn>::load4(pb + 8 * t16 + 4);
+            const float acc = row16_sum(dot4(b0, c0) + dot4(b1, c1));
+            if (t16 == 0) sm.gram[j] = acc;
+        }
+    }
+    __syncthreads();
+
+    float tot = 0.f;
+    for (int i = 0; i < K; ++i) tot += sm.l[s.wave][i];
+    *lam = expf(tot);
+    if (s.lane < KMAX) {
+        float wj = 0.f, cy = 0.f;
+        if (s.lane < K) {
+            float suf = 0.f;
+            for (int i = s.lane + 1; i < K; ++i) suf += sm.l[s.wave][i];
+            wj = sm.dt[s.wave][s.lane] * expf(suf);
+            cy = wj * sm.gram[s.lane];
+        }
+        sm.w[s.wave][s.lane] = wj;
+        sm.cy[s.wave][s.lane] = cy;
+    }
+    __syncthreads();
+
+    float yb = Dh * xcur;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        const float term = sm.cy[s.wave][j] * xv[j];
+        yb += (j < K) ? term : 0.f;   // select: entries beyond K never leak (even NaN)
+    }
+    *ybuf = yb;
+    if (in.commit) {
+        // row prow of the commit coefficients; any lane -> row bijection fills them all
+        const int i = prow >> 1, hf = prow & 1;
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const float cf = sm.w[s.wave][j] * xv[j];
+            sm.cs[s.wave][cs_index<KMAX>(hf, i & 3, j, i >> 2)] = (j < K) ? cf : 0.f;
+            const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin;
+            Bj[j] = io<TIn>::load_raw4(pb + 4 * s.c);
+        }
+    }
+    __syncthreads();
+}
+
+// Append the current token at buffer entry k (x and dt per head; B once per
+// group, by the group's first workgroup).
+template <typename TIn>
+__device__ __forceinline__ void step_append(const ReplayParams &a, const Slot &s, const StepIn &in) {
+    const TIn *xin = static_cast<const TIn *>(in.xin);
+    const TIn *Bin = static_cast<const TIn *>(in.Bin);
+    TIn *xw = reinterpret_cast<TIn *>(a.xbuf) + ((size_t)s.b * a.Lcap + in.k) * in.HP + (size_t)s.h * kP;
+    io<TIn>::copy1(xw + s.lane, xin + s.lane);
+    if (s.lane == 0) {
+        TIn *dw = reinterpret_cast<TIn *>(a.dtbuf) + ((size_t)s.b * a.Lcap + in.k) * a.H + s.h;
+        io<TIn>::copy1(dw, static_cast<const TIn *>(in.dtin));
+    }
+    if (s.wave == 0 && (s.tile * a.hpw) % s.hpg == 0) {
+        TIn *bw = reinterpret_cast<TIn *>(a.bbuf) + ((size_t)s.b * a.Lcap + in.k) * in.GN + (size_t)s.g * kN;
+        io<TIn>::copy1(bw + s.lane, Bin + s.lane);
+        io<TIn>::copy1(bw + s.lane + 64, Bin + s.lane + 64);
+    }
+}
+
+
+// ------------------------------------------------------------------------
+// Speculative-verify prologue.
+// ------------------------------------------------------------------------
+template <int KMAX, int T>
+struct VerifySmem {
+    float l[kMaxHpw][KMAX];
+    float dt[kMaxHpw][KMAX];
+    float gram[T][KMAX];
+    float cy[kMaxHpw][T][KMAX];
+    float lam[kMaxHpw][T];
+};
+
+struct VerifyIn {
+    int k, KL;
+    size_t HP, GN;
+    const void *xin, *Bin, *Cin, *dtin, *xb, *bb, *db;
+};
+
+template <typename TIn, int T>
+__device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const Slot &s) {
+    VerifyIn in;
+    int k = a.pos[s.b];
+    if (k < 0 || k > a.L - 1) {
+        if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrPos);
+        k = k < 0 ? 0 : a.L - 1;
+    }
+    in.k = k;
+    in.KL = k + T;   // entries once all drafts are appended
+    in.HP = (size_t)a.H * kP;
+    in.GN = (size_t)a.G * kN;
+    // token-axis inputs [B,T,...]
+    in.xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.b * T * in.HP + (size_t)s.h * kP;
+    in.Bin = reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.b * T * in.GN + (size_t)s.g * kN;
+    in.Cin = reinterpret_cast<const TIn *>(a.Cm) + (size_t)s.b * T * in.GN + (size_t)s.g * kN;
+    in.dtin = reinterpret_cast<const TIn *>(a.dt) + (size_t)s.b * T * a.H + s.h;
+    in.xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)s.b * a.Lcap * in.HP + (size_t)s.h * kP;
+    in.bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * in.GN + (size_t)s.g * kN;
+    in.db = reinterpret_cast<const TIn *>(a.dtbuf) + (size_t)s.b * a.Lcap * a.H + s.h;
+    return in;
+}
+
+// Weights, decays and the buffer part of every draft output for row prow:
+// ybuf[t] = sum_{j < k+t+1} w_tj (B_j . C_t) x_j[prow] + D x_t[prow];
+// Lambda_t is left in sm.lam[wave][t].
+template <typename TIn, int KMAX, int T>
+__device__ __forceinline__ void verify_prologue(const ReplayParams &a, const Slot &s, const VerifyIn &in,
+                                                int prow, VerifySmem<KMAX, T> &sm, float (&ybuf)[T]) {
+    const int k = in.k, KL = in.KL;
+    const TIn *xin = static_cast<const TIn *>(in.xin);
+    const TIn *Bin = static_cast<const TIn *>(in.Bin);
+    const TIn *Cin = static_cast<const TIn *>(in.Cin);
+    const TIn *dtin = static_cast<const TIn *>(in.dtin);
+    const TIn *xb = static_cast<const TIn *>(in.xb);
+    const TIn *bb = static_cast<const TIn *>(in.bb);
+    const TIn *db = static_cast<const TIn *>(in.db);
+
+    float xv[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        int t = j - k;
+        t = t < 0 ? 0 : (t > T - 1 ? T - 1 : t);
+        const TIn *px = (j < k) ? xb + (size_t)j * in.HP + prow : xin + (size_t)t * in.HP + prow;
+        xv[j] = io<TIn>::load1(px);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) ybuf[t] = io<TIn>::load1(xin + (size_t)t * in.HP + prow);
+    const float Ah = a.A[s.h], Dh = a.D[s.h];
+
+    if (s.lane < KL) {
+        const TIn *pd = (s.lane < k) ? db + (size_t)s.lane * a.H : dtin + (size_t)(s.lane - k) * a.H;
+        const float d = io<TIn>::load1(pd);
+        sm.dt[s.wave][s.lane] = d;
+        sm.l[s.wave][s.lane] = Ah * d;
+    }
+    {   // Gram g[t][j] = B_j . C_t for every draft t and entry j < KL
+        const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4, ngrp = blockDim.x >> 4;
+        for (int d = grp; d < T * KL; d += ngrp) {
+            const int t = d / KL, j = d - t * KL;
+            const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin + (size_t)(j - k) * in.GN;
+            const TIn *pc = Cin + (size_t)t * in.GN;
+            const float4 b0 = io<TIn>::load4(pb + 8 * t16), b1 = io<TIn>::load4(pb + 8 * t16 + 4);
+            const float4 c0 = io<TIn>::load4(pc + 8 * t16), c1 = io<TIn>::load4(pc + 8 * t16 + 4);
+            const float acc = row16_sum(dot4(b0, c0) + dot4(b1, c1));
+            if (t16 == 0) sm.gram[t][j] = acc;
+        }
+    }
+    __syncthreads();
+
+    if (s.lane < KMAX) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int Kt = k + t + 1;
+            float cy = 0.f;
+            if (s.lane < Kt) {
+                float suf = 0.f;
+                for (int i = s.lane + 1; i < Kt; ++i) suf += sm.l[s.wave][i];
+                cy = sm.dt[s.wave][s.lane] * expf(suf) * sm.gram[t][s.lane];
+            }
+            sm.cy[s.wave][t][s.lane] = cy;
+        }
+    }
+    if (s.lane < T) {
+        float tot = 0.f;
+        for (int i = 0; i < k + s.lane + 1; ++i) tot += sm.l[s.wave][i];
+        sm.lam[s.wave][s.lane] = expf(tot);
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int Kt = k + t + 1;
+        float acc = Dh * ybuf[t];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const float term = sm.cy[s.wave][t][j] * xv[j];
+            acc += (j < Kt) ? term : 0.f;   // later drafts never reach output t
+        }
+        ybuf[t] = acc;
+    }
+}
+
+// Append the T drafts at entries k .. k+T-1 (the position is not advanced).
+template <typename TIn, int T>
+__device__ __forceinline__ void verify_append(const ReplayParams &a, const Slot &s, const VerifyIn &in) {
+    const TIn *xin = static_cast<const TIn *>(in.xin);
+    const TIn *Bin = static_cast<const TIn *>(in.Bin);
+    const TIn *dtin = static_cast<const TIn *>(in.dtin);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        TIn *xw = reinterpret_cast<TIn *>(a.xbuf) + ((size_t)s.b * a.Lcap + in.k + t) * in.HP + (size_t)s.h * kP;
+        io<TIn>::copy1(xw + s.lane, xin + (size_t)t * in.HP + s.lane);
+    }
+    if (s.lane < T) {
+        TIn *dw = reinterpret_cast<TIn *>(a.dtbuf) + ((size_t)s.b * a.Lcap + in.k + s.lane) * a.H + s.h;
+        io<TIn>::copy1(dw, dtin + (size_t)s.lane * a.H);
+    }
+    if (s.wave == 0 && (s.tile * a.hpw) % s.hpg == 0) {
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            TIn *bw = reinterpret_cast<TIn *>(a.bbuf) + ((size_t)s.b * a.Lcap + in.k + t) * in.GN + (size_t)s.g * kN;
+            io<TIn>::copy1(bw + s.lane, Bin + (size_t)t * in.GN + s.lane);
+            io<TIn>::copy1(bw + s.lane + 64, Bin + (size_t)t * in.GN + s.lane + 64);
+        }
+    }
+}
+
+// ------------------------------------------------------------------------
+// Accept / flush prologue: how many entries to fold and whether to commit.
+// ------------------------------------------------------------------------
+template <int KMAX>
+struct CommitSmem {
+    float l[kMaxHpw][KMAX];
+    float w[kMaxHpw][KMAX];
+    float cs[kMaxHpw][kP * KMAX];
+};
+
+template <bool ACCEPT>
+__device__ __forceinline__ int commit_count(const ReplayParams &a, const Slot &s, bool *commit) {
+    int k = a.pos[s.b];
+    if (k < 0 || k > a.L - 1) {
+        if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrPos);
+        k = k < 0 ? 0 : a.L - 1;
+    }
+    int nk = 0;
+    if (ACCEPT) {
+        nk = a.n_keep[s.b];
+        if (nk < 0 || nk > a.T) {
+            if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrKeep);
+            nk = nk < 0 ? 0 : a.T;
+        }
+    }
+    const int K = k + nk;
+    *commit = ACCEPT ? (K >= a.L) : (K > 0);
+    return K;
+}
+
+// Lambda_K, commit coefficients (LDS) and this lane's B_j slices for folding
+// all K buffered entries (K >= 1).
+template <typename TIn, int KMAX>
+__device__ __forceinline__ float commit_prologue(const ReplayParams &a, const Slot &s, int K,
+                                                 CommitSmem<KMAX> &sm,
+                                                 typename io<TIn>::raw4 (&Bj)[KMAX]) {
+    const size_t HP = (size_t)a.H * kP, GN = (size_t)a.G * kN;
+    const TIn *xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)s.b * a.Lcap * HP + (size_t)s.h * kP;
+    const TIn *bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * GN + (size_t)s.g * kN;
+    const TIn *db = reinterpret_cast<const TIn *>(a.dtbuf) + (size_t)s.b * a.Lcap * a.H + s.h;
+    const float Ah = a.A[s.h];
+
+    float xv[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        const int jj = j < K ? j : K - 1;
+        xv[j] = io<TIn>::load1(xb + (size_t)jj * HP + s.prow);
+        Bj[j] = io<TIn>::load_raw4(bb + (size_t)jj * GN + 4 * s.c);
+    }
+    float dl = 0.f;
+    if (s.lane < K) {
+        dl = io<TIn>::load1(db + (size_t)s.lane * a.H);
+        sm.l[s.wave][s.lane] = Ah * dl;
+    }
+    __syncthreads();
+    float tot = 0.f;
+    for (int i = 0; i < K; ++i) tot += sm.l[s.wave][i];
+    if (s.lane < KMAX) {
+        float wj = 0.f;
+        if (s.lane < K) {
+            float suf = 0.f;
+            for (int i = s.lane + 1; i < K; ++i) suf += sm.l[s.wave][i];
+            wj = dl * expf(suf);
+        }
+        sm.w[s.wave][s.lane] = wj;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        const float cf = sm.w[s.wave][j] * xv[j];
+        sm.cs[s.wave][cs_index<KMAX>(s.hf, s.c & 3, j, s.c >> 2)] = (j < K) ? cf : 0.f;
+    }
+    __syncthreads();
+    return expf(tot);
+}
+
+}  // namespace
+}  // namespace rssm

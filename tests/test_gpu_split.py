@@ -1,0 +1,264 @@
+"""GPU parity of the precision split (article section 4) against the oracle.
+
+Bars:
+* quantised bytes (update checkpoint, FP4 codes and scales) bit-exact against
+  the oracle's independent quantisers applied to the same fp32 values;
+* outputs within 2e-5 * max(1, |y|) of the oracle recurrence replayed from
+  the exactly decoded output source;
+* the fp32 commit values (dumped before rounding) within 2e-5 * max(1, |S|)
+  of the oracle recurrence replayed from the decoded update checkpoint.
+The free-running low-precision trajectory is a measurement (drift), not a
+parity check: commit values differ from the oracle's fp64 ones by ~1 ulp, so
+the teacher-forced scheme re-anchors the oracle on the GPU's stored bytes at
+every interval.
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_close, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+SPLIT_FORMATS = ["split-bf16", "split-e4m3", "shared-fp4", "low-bf16", "low-e4m3"]
+SEED, LAYER = 0x5EED_0000_1234_ABCD, 3
+
+
+@pytest.fixture(scope="module")
+def rs():
+    need_gpu()
+    import state_space_recurrence_amd as rs
+    rs.lib()
+    return rs
+
+
+def _ufmt(fmt):
+    return {"split-bf16": "bf16", "low-bf16": "bf16", "split-e4m3": "e4m3", "low-e4m3": "e4m3"}.get(fmt)
+
+
+def _decode_u(fmt, ckpt):
+    u = ckpt.cpu().numpy()
+    if _ufmt(fmt) == "bf16":
+        return oracle.bf16_decode_array(u.view(np.uint16))
+    return oracle.e4m3_decode_array(u)
+
+
+def _decode_o(ls):
+    return oracle.fp4_dequantize(ls.out_q.cpu().numpy(), ls.out_scale.cpu().numpy())
+
+
+def _sources(fmt, ls):
+    """(decoded state the outputs read, decoded state the updates read)."""
+    if fmt == "shared-fp4":
+        o = _decode_o(ls)
+        return o, o
+    u = _decode_u(fmt, ls.ckpt)
+    if fmt.startswith("split"):
+        return _decode_o(ls), u
+    return u, u
+
+
+def _check_quantised(fmt, ls, values, interval):
+    """The GPU's stored bytes equal the oracle's quantisation of `values`."""
+    v = values.cpu().numpy().astype(np.float32)
+    if _ufmt(fmt):
+        ref = oracle.sr_quantize(v.reshape(-1), _ufmt(fmt), SEED, LAYER, interval).reshape(v.shape)
+        got = ls.ckpt.cpu().numpy()
+        got = got.view(np.uint16) if _ufmt(fmt) == "bf16" else got
+        bad = np.argwhere(got != ref)
+        assert bad.size == 0, f"{fmt}: {len(bad)} update-checkpoint codes differ, first {bad[:3].tolist()}"
+    if fmt.startswith("split") or fmt == "shared-fp4":
+        codes, scales = oracle.fp4_quantize(v)
+        assert np.array_equal(ls.out_scale.cpu().numpy(), scales), f"{fmt}: FP4 scales differ"
+        assert np.array_equal(ls.out_q.cpu().numpy(), codes), f"{fmt}: FP4 codes differ"
+
+
+def _special_state(shape, gen):
+    """fp32 values exercising the quantisers: normal spread, tiny (E4M3
+    subnormal / underflow), large (near and beyond 448), signed zeros, exact
+    FP4 thresholds relative to a block scale, bf16 ties of the low 16 bits."""
+    S = torch.randn(shape, generator=gen) * 0.1
+    flat = S.view(-1, 128)
+    n = flat.shape[0]
+    flat[0:n:7] *= 1e-4
+    flat[1:n:7] *= 3e3
+    flat[2:n:7, :16] = 0.0
+    flat[2:n:7, 16:32] = -0.0
+    # one block per row with amax exactly 6 (scale 1.0) and values on the thresholds
+    thr = torch.tensor([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, -0.25, -0.75, -1.25, -1.75, -2.5, -3.5,
+                        -5.0, -6.0] * 2)
+    flat[3:n:7, 32:64] = thr
+    # values whose dropped bf16 bits are exactly 0x8000 (a stochastic-rounding midpoint)
+    mid = (torch.randn(n // 7 + 1, 32).view(torch.int32) & ~0xFFFF | 0x8000).view(torch.float32)
+    flat[4:n:7, 64:96] = mid[: flat[4:n:7].shape[0]]
+    return S.contiguous()
+
+
+@pytest.mark.parametrize("fmt", SPLIT_FORMATS)
+def test_load_checkpoint_quantisers_bit_exact(rs, fmt):
+    B, H, G = 5, 8, 2
+    A, D = torch.full((H,), -1.0), torch.zeros(H)
+    ls = rs.LayerState(B, H, G, A, D, in_dtype=torch.float32, state_format=fmt, seed=SEED, layer_id=LAYER)
+    g = torch.Generator().manual_seed(11)
+    S = _special_state((B, H, 64, 128), g)
+    for interval in (0, 7):
+        ls.intv.fill_(interval)
+        rs.load_checkpoint(ls, S.cuda())
+        torch.cuda.synchronize()
+        _check_quantised(fmt, ls, S, interval)
+        assert ls.pos.cpu().tolist() == [0] * B
+
+
+def _run_intervals(rs, fmt, w, batch, n_intervals, tail, layer=0):
+    """Standard decoding with teacher-forced oracle checks at every interval."""
+    L = w.interval
+    steps = n_intervals * L + tail
+    A, D = synth.layer_params(w, layer)
+    S0 = synth.init_state(w, layer, batch=batch)
+    x, Bm, Cm, dt = synth.token_inputs(w, layer, steps, batch=batch)
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=L, in_dtype=x.dtype, state_format=fmt,
+                       seed=SEED, layer_id=LAYER, debug_prequant=True)
+    rs.load_checkpoint(ls, S0.cuda())
+    xs, Bs, Cs, ds = (t.cuda() for t in (x, Bm, Cm, dt))
+    t = 0
+    for it in range(n_intervals + 1):
+        n = L if it < n_intervals else tail
+        if n == 0:
+            break
+        out_src, upd_src = _sources(fmt, ls)
+        ys = [rs.step(ls, xs[t + i], Bs[t + i], Cs[t + i], ds[t + i]).cpu() for i in range(n)]
+        sl = slice(t, t + n)
+        _, y_ref = oracle.recurrent(out_src, x[sl], Bm[sl], Cm[sl], dt[sl], A, D, w.groups)
+        for i in range(n):
+            assert_close(ys[i], y_ref[i], f"{fmt} y at step {t + i}")
+        if n == L:   # the step that closed the interval committed
+            S_new, _ = oracle.recurrent(upd_src, x[sl], Bm[sl], Cm[sl], dt[sl], A, D, w.groups)
+            dump = ls.debug_prequant.cpu()
+            assert_close(dump, S_new, f"{fmt} commit values of interval {it}")
+            _check_quantised(fmt, ls, dump, it + 1)
+            assert ls.intv.cpu().tolist() == [it + 1] * batch
+        t += n
+    rs.check_device_errors(ls)
+    return ls
+
+
+@pytest.mark.parametrize("fmt", SPLIT_FORMATS)
+def test_split_decode_teacher_forced(rs, fmt):
+    w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
+    _run_intervals(rs, fmt, w, batch=3, n_intervals=3, tail=5)
+
+
+def test_split_decode_4b_layout(rs):
+    """The 4B-class head layout (H=96, G=8), bf16 inputs, split-bf16."""
+    w = synth.WORKLOADS["split"]
+    _run_intervals(rs, "split-bf16", w, batch=2, n_intervals=2, tail=3)
+
+
+def test_update_checkpoint_ignores_output_copy(rs):
+    """Article section 4: the output copy is not used for the next update.
+    Bit-exact: the bf16 update checkpoint evolves identically with the FP4
+    copy (split) and without it (one bf16 checkpoint)."""
+    w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
+    batch, steps = 3, 3 * w.interval + 4
+    A, D = synth.layer_params(w, 1)
+    S0 = synth.init_state(w, 1, batch=batch).cuda()
+    x, Bm, Cm, dt = (t.cuda() for t in synth.token_inputs(w, 1, steps, batch=batch))
+    cks = []
+    for fmt in ("split-bf16", "low-bf16"):
+        ls = rs.LayerState(batch, w.heads, w.groups, A, D, in_dtype=x.dtype, state_format=fmt, seed=SEED,
+                           layer_id=LAYER)
+        rs.load_checkpoint(ls, S0)
+        for t in range(steps):
+            rs.step(ls, x[t], Bm[t], Cm[t], dt[t])
+        cks.append(ls.ckpt.clone())
+    assert torch.equal(cks[0], cks[1])
+
+
+@pytest.mark.parametrize("fmt", ["split-bf16", "split-e4m3", "shared-fp4"])
+def test_split_speculative_rounds(rs, fmt):
+    """Verify reads the output source; accept commits from the update source
+    once the position count reaches L (teacher-forced at every commit)."""
+    w = dataclasses.replace(synth.WORKLOADS["spec"], heads=16, groups=2, in_dtype="bf16")
+    batch, R = 4, 14
+    T = w.drafts + 1
+    A, D = synth.layer_params(w, 0)
+    S0 = synth.init_state(w, 0, batch=batch)
+    x, Bm, Cm, dt = synth.token_inputs(w, 0, R, batch=batch, tokens=T)
+    nk = synth.n_keep(w, R, batch=batch)
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=w.interval, max_draft=T, in_dtype=x.dtype,
+                       state_format=fmt, seed=SEED, layer_id=LAYER, debug_prequant=True)
+    rs.load_checkpoint(ls, S0.cuda())
+    bt = lambda t: t.transpose(0, 1).contiguous().cuda()
+    out_src, upd_src = _sources(fmt, ls)
+    hist = [[] for _ in range(batch)]   # accepted (round, position) since the last commit
+    pos = np.zeros(batch, dtype=int)
+    for r in range(R):
+        y = rs.verify(ls, bt(x[r]), bt(Bm[r]), bt(Cm[r]), bt(dt[r])).cpu()
+        for b in range(batch):
+            idx = hist[b]
+            xs = torch.stack([x[rr, tt, b] for rr, tt in idx] + [x[r, tt, b] for tt in range(T)])[:, None]
+            Bs = torch.stack([Bm[rr, tt, b] for rr, tt in idx] + [Bm[r, tt, b] for tt in range(T)])[:, None]
+            Cs = torch.stack([Cm[rr, tt, b] for rr, tt in idx] + [Cm[r, tt, b] for tt in range(T)])[:, None]
+            ds = torch.stack([dt[rr, tt, b] for rr, tt in idx] + [dt[r, tt, b] for tt in range(T)])[:, None]
+            _, yref = oracle.recurrent(out_src[b:b + 1], xs, Bs, Cs, ds, A, D, w.groups)
+            assert_close(y[b], yref[len(idx):, 0], f"{fmt} verify round {r} slot {b}")
+        rs.accept(ls, nk[r].cuda(), T)
+        new_pos = pos + nk[r].numpy()
+        committed = new_pos >= w.interval
+        dump = ls.debug_prequant.cpu()
+        out_next, upd_next = _sources(fmt, ls)
+        for b in range(batch):
+            hist[b] += [(r, tt) for tt in range(int(nk[r, b]))]
+            if committed[b]:
+                idx = hist[b]
+                xs = torch.stack([x[rr, tt, b] for rr, tt in idx])[:, None]
+                Bs = torch.stack([Bm[rr, tt, b] for rr, tt in idx])[:, None]
+                Cs = torch.stack([Cm[rr, tt, b] for rr, tt in idx])[:, None]
+                ds = torch.stack([dt[rr, tt, b] for rr, tt in idx])[:, None]
+                S_new, _ = oracle.recurrent(upd_src[b:b + 1], xs, Bs, Cs, ds, A, D, w.groups)
+                assert_close(dump[b:b + 1], S_new, f"{fmt} commit values slot {b} round {r}")
+                hist[b] = []
+        if committed.any():
+            # bytes of committed slots == oracle quantisation of their dumped values
+            for b in np.nonzero(committed)[0]:
+                v = dump[b].numpy().astype(np.float32)
+                interval = int(ls.intv[b])
+                e0 = b * w.heads * 64 * 128
+                if _ufmt(fmt):
+                    ref = oracle.sr_quantize(v.reshape(-1), _ufmt(fmt), SEED, LAYER, interval, elem0=e0)
+                    got = ls.ckpt[b].cpu().numpy().reshape(-1)
+                    got = got.view(np.uint16) if _ufmt(fmt) == "bf16" else got
+                    assert np.array_equal(got, ref), f"{fmt} update bytes slot {b} round {r}"
+                codes, scales = oracle.fp4_quantize(v)
+                assert np.array_equal(ls.out_q[b].cpu().numpy(), codes), f"{fmt} FP4 codes slot {b}"
+                assert np.array_equal(ls.out_scale[b].cpu().numpy(), scales), f"{fmt} FP4 scales slot {b}"
+        # sources for the next round: committed slots re-anchor on the new bytes
+        for b in range(batch):
+            if committed[b]:
+                out_src[b], upd_src[b] = out_next[b], upd_next[b]
+        pos = np.where(committed, 0, new_pos)
+        assert np.array_equal(ls.pos.cpu().numpy(), pos)
+    rs.check_device_errors(ls)
+
+
+def test_split_drift_ordering(rs):
+    """Sanity (article section 4, not a parity bar): outputs drift less from
+    the fp32 trajectory with the split than with one shared FP4 state."""
+    w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
+    batch, steps = 4, 8 * w.interval
+    A, D = synth.layer_params(w, 0)
+    S0 = synth.init_state(w, 0, batch=batch).cuda()
+    x, Bm, Cm, dt = (t.cuda() for t in synth.token_inputs(w, 0, steps, batch=batch))
+    ys = {}
+    for fmt in ("f32", "split-bf16", "shared-fp4"):
+        ls = rs.LayerState(batch, w.heads, w.groups, A, D, in_dtype=x.dtype, state_format=fmt, seed=SEED)
+        rs.load_checkpoint(ls, S0)
+        ys[fmt] = torch.stack([rs.step(ls, x[t], Bm[t], Cm[t], dt[t]).clone() for t in range(steps)])
+    ref = ys["f32"]
+    drift = {f: float((ys[f] - ref)[-w.interval:].norm() / ref[-w.interval:].norm()) for f in ys if f != "f32"}
+    print("drift over the last interval:", drift)
+    assert drift["split-bf16"] < drift["shared-fp4"]
