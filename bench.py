@@ -52,6 +52,22 @@ def replay_bytes_per_token(H, G, P=64, N=128, L=16, in_bytes=2, state_bytes=4):
     return state + state / L + cur + entry * (L - 1) / L + entry * (L - 1) / 2 + y
 
 
+def split_bytes_per_token(fmt, H, G, P=64, N=128, L=16, in_bytes=2):
+    """Replay step with a low-precision state (same buffer/input/output terms
+    as the fp32 replay): every step reads the output source; once per
+    interval the commit reads the update source and writes it (and the FP4
+    copy).  Bytes per element: bf16 2, E4M3 1, FP4 copy 0.5 + 1/32 scale."""
+    fp4 = 0.5 + 1.0 / 32
+    src = {"split-bf16": (fp4, 2, 2 + fp4), "split-e4m3": (fp4, 1, 1 + fp4),
+           "shared-fp4": (fp4, fp4, fp4), "low-bf16": (2, 0, 2), "low-e4m3": (1, 0, 1)}[fmt]
+    out_read, upd_read, commit_write = src
+    elems = H * P * N
+    entry = (H * P + G * N + H) * in_bytes
+    cur = (H * P + 2 * G * N + H) * in_bytes
+    return (elems * (out_read + (upd_read + commit_write) / L) + cur + entry * (L - 1) / L
+            + entry * (L - 1) / 2 + H * P * 4)
+
+
 def recurrent_bytes_per_token(H, G, P=64, N=128, in_bytes=2, state_bytes=4):
     """Conventional step: state read + written every token, inputs read, y written."""
     return 2 * H * P * N * state_bytes + (H * P + 2 * G * N + H) * in_bytes + H * P * 4
@@ -251,6 +267,7 @@ def main():
         log(f"[bench] 120b: replay {r['replay_tokens_per_s']:.0f} tok/s, "
             f"recurrent {r['recurrent_tokens_per_s']:.0f} tok/s")
         extras["spec_batch512"] = run_spec(rs, L, torch, synth, dev, stream, sh, log)
+        extras["split_batch256"] = run_split(rs, L, torch, synth, dev, stream, sh, log)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -365,6 +382,86 @@ def run_spec(rs, L, torch, synth, dev, stream, sh, log, rounds=64, warm=8):
         f"recurrent {out['recurrent_kept_tokens_per_s']:.0f} ({out['replay_speedup_vs_recurrent']:.2f}x)")
     del pools, layers
     torch.cuda.empty_cache()
+    return out
+
+
+def run_split(rs, L, torch, synth, dev, stream, sh, log, steps=256, warm=16, drift_steps=512):
+    """Precision split on the 4B-class shape (batch 256, 4 layers, L=16):
+    decode tokens/s per state format, and the output drift of each format
+    against the fp32-state trajectory on identical inputs (relative L2 norm
+    of y over all slots/heads/rows of all layers, per step)."""
+    w = synth.WORKLOADS["split"]
+    fmts = ["split-bf16", "split-e4m3", "shared-fp4", "low-bf16", "low-e4m3"]
+    nin = 64
+    ins = [synth.token_inputs(w, l, nin, device=dev) for l in range(w.layers)]
+    params = [synth.layer_params(w, l, device=dev) for l in range(w.layers)]
+    S0 = [synth.init_state(w, l, device=dev) for l in range(w.layers)]
+    seed = 0x5EED
+
+    def make(fmt):
+        out = []
+        for l in range(w.layers):
+            ls = rs.LayerState(w.batch, w.heads, w.groups, *params[l], interval=w.interval,
+                               in_dtype=ins[l][0].dtype, device=dev, layer_id=l, seed=seed,
+                               state_format=fmt)
+            rs.load_checkpoint(ls, S0[l])
+            out.append((ls, ls.desc(), ls.cstate()))
+        return out
+
+    def loop(layers, t0, n, y):
+        for i in range(n):
+            t = (t0 + i) % nin
+            for li, (ls, d, st) in enumerate(layers):
+                x, Bm, Cm, dt = ins[li]
+                rc = L.replayssm_step(ctypes.byref(d), ctypes.byref(st), x[t].data_ptr(), Bm[t].data_ptr(),
+                                      Cm[t].data_ptr(), dt[t].data_ptr(), y[li].data_ptr(), sh)
+                if rc:
+                    raise RuntimeError(L.replayssm_last_error().decode())
+
+    out = {"batch": w.batch, "layers": w.layers, "heads": w.heads, "steps": steps}
+    ys = [torch.empty(w.batch, w.heads, 64, device=dev) for _ in range(w.layers)]
+    for fmt in fmts:
+        layers = make(fmt)
+        loop(layers, 0, warm, ys)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        loop(layers, warm, steps, ys)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sec = e0.elapsed_time(e1) / 1e3
+        bpt = split_bytes_per_token(fmt, w.heads, w.groups, L=w.interval)
+        out[fmt] = {"tokens_per_s": w.batch * steps / sec, "ms_per_step": sec / steps * 1e3,
+                    "bytes_per_token_layer": bpt,
+                    "GBps_stack": bpt * w.batch * w.layers * steps / sec / 1e9}
+        log(f"[bench] {fmt}: {out[fmt]['tokens_per_s']:.0f} tok/s ({out[fmt]['GBps_stack']:.0f} GB/s)")
+        del layers
+    # drift vs the fp32 trajectory, all formats stepped together on the same inputs
+    def drift(tag):
+        runs = {f: make(f) for f in ["f32"] + fmts}
+        yb = {f: [torch.empty(w.batch, w.heads, 64, device=dev) for _ in range(w.layers)] for f in runs}
+        curve = {f: [] for f in fmts}
+        for t in range(drift_steps):
+            for f, layers in runs.items():
+                loop(layers, t, 1, yb[f])
+            ref = torch.stack(yb["f32"])
+            rn = float(ref.norm())
+            for f in curve:
+                curve[f].append(float((torch.stack(yb[f]) - ref).norm()) / rn)
+        out[f"drift_{tag}_last64_mean"] = {f: sum(c[-64:]) / 64 for f, c in curve.items()}
+        out[f"drift_{tag}_every64"] = {f: [round(sum(c[i:i + 64]) / 64, 6) for i in range(0, len(c), 64)]
+                                      for f, c in curve.items()}
+        log(f"[bench] drift {tag} (last 64 steps): "
+            + ", ".join(f"{f} {v:.5f}" for f, v in out[f"drift_{tag}_last64_mean"].items()))
+        del runs
+        torch.cuda.empty_cache()
+
+    drift("workload")
+    # Long-memory variant: the same inputs with every A scaled by 1/100, so the
+    # state remembers ~30-500 tokens instead of ~1-5 and rounding errors that
+    # feed back into updates have time to accumulate.
+    params[:] = [(A * 0.01, D) for A, D in params]
+    drift("long_memory")
     return out
 
 

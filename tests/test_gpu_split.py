@@ -247,10 +247,14 @@ def test_split_speculative_rounds(rs, fmt):
 
 def test_split_drift_ordering(rs):
     """Sanity (article section 4, not a parity bar): outputs drift less from
-    the fp32 trajectory with the split than with one shared FP4 state."""
+    the fp32 trajectory with the split than with one shared FP4 state.  The
+    decay rates are scaled down 100x so the state has a long memory (with the
+    workload's rates it forgets within a few tokens and all formats drift
+    alike)."""
     w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
     batch, steps = 4, 8 * w.interval
     A, D = synth.layer_params(w, 0)
+    A = A * 0.01
     S0 = synth.init_state(w, 0, batch=batch).cuda()
     x, Bm, Cm, dt = (t.cuda() for t in synth.token_inputs(w, 0, steps, batch=batch))
     ys = {}
