@@ -150,7 +150,7 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
 // row `prow` of this lane; on commit steps also the commit coefficients (LDS)
 // and this lane's B_j slices (columns 4c..4c+3, raw).  Returns Lambda_K in
 // *lam and sum_j w_j g_j x_j[prow] + D x[prow] in *ybuf.
-template <typename TIn, int KMAX>
+template <typename TIn, int KMAX, bool LOAD_BJ = true>
 __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot &s, const StepIn &in,
                                               int prow, StepSmem<KMAX> &sm, float *lam, float *ybuf,
                                               typename io<TIn>::raw4 (&Bj)[KMAX]) {
@@ -219,8 +219,10 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
         for (int j = 0; j < KMAX; ++j) {
             const float cf = sm.w[s.wave][j] * xv[j];
             sm.cs[s.wave][cs_index<KMAX>(hf, i & 3, j, i >> 2)] = (j < K) ? cf : 0.f;
-            const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin;
-            Bj[j] = io<TIn>::load_raw4(pb + 4 * s.c);
+            if (LOAD_BJ) {
+                const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin;
+                Bj[j] = io<TIn>::load_raw4(pb + 4 * s.c);
+            }
         }
     }
     __syncthreads();
@@ -245,6 +247,22 @@ __device__ __forceinline__ void step_append(const ReplayParams &a, const Slot &s
     }
 }
 
+
+// Stage the group's B entries 0..KMAX-1 of a commit into LDS as fp32 (the
+// workgroup's heads share one group): entries j < nbuf from the buffer, entry
+// nbuf (when < K) from the current input, entries >= K zero.  Visible after
+// the next __syncthreads.
+template <typename TIn, int KMAX>
+__device__ __forceinline__ void stage_B(float (*sB)[kN], const TIn *bb, const TIn *Bin, size_t GN, int nbuf,
+                                        int K) {
+#pragma unroll 4
+    for (int q = threadIdx.x; q < KMAX * kN / 4; q += blockDim.x) {
+        const int j = q / (kN / 4), n = 4 * (q - j * (kN / 4));
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < K) v = io<TIn>::load4((j < nbuf ? bb + (size_t)j * GN : Bin) + n);
+        *reinterpret_cast<float4 *>(&sB[j][n]) = v;
+    }
+}
 
 // ------------------------------------------------------------------------
 // Speculative-verify prologue.
@@ -424,7 +442,7 @@ __device__ __forceinline__ int commit_count(const ReplayParams &a, const Slot &s
 
 // Lambda_K, commit coefficients (LDS) and this lane's B_j slices for folding
 // all K buffered entries (K >= 1).
-template <typename TIn, int KMAX>
+template <typename TIn, int KMAX, bool LOAD_BJ = true>
 __device__ __forceinline__ float commit_prologue(const ReplayParams &a, const Slot &s, int K,
                                                  CommitSmem<KMAX> &sm,
                                                  typename io<TIn>::raw4 (&Bj)[KMAX]) {
@@ -439,7 +457,7 @@ __device__ __forceinline__ float commit_prologue(const ReplayParams &a, const Sl
     for (int j = 0; j < KMAX; ++j) {
         const int jj = j < K ? j : K - 1;
         xv[j] = io<TIn>::load1(xb + (size_t)jj * HP + s.prow);
-        Bj[j] = io<TIn>::load_raw4(bb + (size_t)jj * GN + 4 * s.c);
+        if (LOAD_BJ) Bj[j] = io<TIn>::load_raw4(bb + (size_t)jj * GN + 4 * s.c);
     }
     float dl = 0.f;
     if (s.lane < K) {

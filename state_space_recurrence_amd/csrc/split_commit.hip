@@ -9,14 +9,18 @@ namespace {
 template <typename TIn, int KMAX, bool ACCEPT, int MODE>
 __global__ void __launch_bounds__(256) split_commit_kernel(ReplayParams a) {
     __shared__ CommitSmem<KMAX> sm;
+    __shared__ float sB[KMAX][kN];
     const Slot s = slot_of(a);
     bool commit;
     const int K = commit_count<ACCEPT>(a, s, &commit);
     const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;
     if (commit) {
-        typename io<TIn>::raw4 Bj[KMAX];
-        const float lam = commit_prologue<TIn, KMAX>(a, s, K, sm, Bj);
-        commit_head<TIn, KMAX, MODE>(a, s, lam, sm.cs[s.wave], Bj, interval);
+        const size_t GN = (size_t)a.G * kN;
+        const TIn *bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * GN + (size_t)s.g * kN;
+        stage_B<TIn, KMAX>(sB, bb, bb, GN, K, K);
+        typename io<TIn>::raw4 unused[KMAX];
+        const float lam = commit_prologue<TIn, KMAX, false>(a, s, K, sm, unused);
+        commit_head<KMAX, MODE>(a, s, lam, sm.cs[s.wave], sB, interval);
     }
     publish_position(a, s.b, commit ? 0 : K, commit);
 }

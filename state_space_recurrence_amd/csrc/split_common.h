@@ -137,18 +137,23 @@ __device__ __forceinline__ void quantize_store_row(const ReplayParams &a, size_t
 }
 
 // New state rows of chunk q (rows 2(q + 4m) + hf) from the decoded source
-// rows: S_new = lam * U + sum_j cs[r][j] B_j, then rounded and stored.
-template <typename TIn, int KMAX, int MODE>
+// rows: S_new = lam * U + sum_j cs[r][j] B_j (B_j staged in LDS as fp32),
+// then rounded and stored.
+template <int KMAX, int MODE>
 __device__ __forceinline__ void commit_chunk_q(const ReplayParams &a, const Slot &s, float4 (&st)[kPerChunk],
-                                               int q, float lam, const float *cs,
-                                               const typename io<TIn>::raw4 (&Bj)[KMAX], uint32_t interval) {
+                                               int q, float lam, const float *cs, const float (*sB)[kN],
+                                               uint32_t interval) {
 #pragma unroll
     for (int m = 0; m < kPerChunk; ++m) {
         st[m].x *= lam; st[m].y *= lam; st[m].z *= lam; st[m].w *= lam;
     }
+    // An opaque column offset per chunk: the B_j reads are redone for every
+    // chunk instead of being hoisted and held (64 VGPRs) across chunks.
+    int col = 4 * s.c;
+    asm volatile("" : "+v"(col));
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-        const float4 b = io<TIn>::widen_here(Bj[j]);
+        const float4 b = *reinterpret_cast<const float4 *>(&sB[j][col]);
         const float *cp = cs + cs_index<KMAX>(s.hf, q, j, 0);
         const float4 c0 = *reinterpret_cast<const float4 *>(cp);
         const float4 c1 = *reinterpret_cast<const float4 *>(cp + 4);
@@ -160,19 +165,25 @@ __device__ __forceinline__ void commit_chunk_q(const ReplayParams &a, const Slot
             st[m].z += cf[m] * b.z;
             st[m].w += cf[m] * b.w;
         }
+        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound hoisted LDS reads
     }
+    // all rows of the chunk are complete before any is rounded (keeps the
+    // rounding streams from being interleaved with, and stretching, the FMAs)
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m) asm volatile("" : "+v"(st[m].x), "+v"(st[m].y), "+v"(st[m].z), "+v"(st[m].w));
 #pragma unroll
     for (int m = 0; m < kPerChunk; ++m) {
         const size_t row = ((size_t)s.b * a.H + s.h) * kP + 2 * chunk_index(q, m) + s.hf;
         quantize_store_row<MODE>(a, row, s.c, s.lane, st[m], interval);
+        __builtin_amdgcn_sched_barrier(0);   // one row's rounding stream at a time
     }
 }
 
 // Rewrites the whole head from its source (U, or O for the shared mode),
 // streaming the source rows chunk by chunk with kNB chunks in flight.
-template <typename TIn, int KMAX, int MODE>
+template <int KMAX, int MODE>
 __device__ __forceinline__ void commit_head(const ReplayParams &a, const Slot &s, float lam, const float *cs,
-                                            const typename io<TIn>::raw4 (&Bj)[KMAX], uint32_t interval) {
+                                            const float (*sB)[kN], uint32_t interval) {
     constexpr int UB = ModeTraits<MODE>::ubits;
     const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
     typename Raw4<UB>::T raw[kNB][kPerChunk];
@@ -190,7 +201,7 @@ __device__ __forceinline__ void commit_head(const ReplayParams &a, const Slot &s
             for (int m = 0; m < kPerChunk; ++m)
                 raw[q % kNB][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q + kNB, m), s.c);
         }
-        commit_chunk_q<TIn, KMAX, MODE>(a, s, st, q, lam, cs, Bj, interval);
+        commit_chunk_q<KMAX, MODE>(a, s, st, q, lam, cs, sB, interval);
     }
 }
 
@@ -241,26 +252,27 @@ __device__ __forceinline__ float reduce_scatter16(float (&v)[16], int lane) {
     return v[0];
 }
 
-// y0[t] = deq(O) . C_t for this lane's row 4cq + rg, every draft t; each row's
-// codes are decoded once.
+// y0[t] = deq(O) . C_t for this lane's row 4cq + rg, every draft t.  The
+// codes are re-decoded per draft (4 packed conversions per 8 values) rather
+// than held decoded across drafts (128 VGPRs).
 template <int T>
 __device__ __forceinline__ void fp4_rows_dot(const Fp4Rows &o, const float (&c8)[T][8], int lane, float (&y0)[T]) {
-    float v[T][16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        float d[8];
-        e2m1_decode8(o.code[i], d);
-        const float sc = e4m3_decode(o.scale[i]);
+    for (int t = 0; t < T; ++t) {
+        float v[16];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
+        for (int i = 0; i < 16; ++i) {
+            uint32_t w = o.code[i], sraw = o.scale[i];
+            if (T > 1) asm volatile("" : "+v"(w), "+v"(sraw));   // fresh decode per draft
+            float d[8];
+            e2m1_decode8(w, d);
             float acc = 0.f;
 #pragma unroll
             for (int n = 0; n < 8; ++n) acc += d[n] * c8[t][n];
-            v[t][i] = acc * sc;
+            v[i] = acc * e4m3_decode(sraw);
         }
+        y0[t] = reduce_scatter16(v, lane);
     }
-#pragma unroll
-    for (int t = 0; t < T; ++t) y0[t] = reduce_scatter16(v[t], lane);
 }
 
 // y0[t] = deq(U) . C_t for this lane's row 2c + hf, every draft t, from the
@@ -273,7 +285,12 @@ __device__ __forceinline__ void rows4_dot(const typename Raw4<UB>::T (&raw)[32],
     for (int q = 0; q < kChunks; ++q) {
         float4 st[kPerChunk];
 #pragma unroll
-        for (int m = 0; m < kPerChunk; ++m) st[m] = decode_row4<UB>(raw[chunk_index(q, m)]);
+        for (int m = 0; m < kPerChunk; ++m) {
+            typename Raw4<UB>::T rw = raw[chunk_index(q, m)];
+            if constexpr (UB == 16) asm volatile("" : "+v"(rw.x), "+v"(rw.y));   // decode chunk by chunk
+            else asm volatile("" : "+v"(rw));
+            st[m] = decode_row4<UB>(rw);
+        }
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             float v[kPerChunk];

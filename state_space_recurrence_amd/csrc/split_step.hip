@@ -11,6 +11,7 @@ __global__ void __launch_bounds__(256) split_step_kernel(ReplayParams a) {
     using MT = ModeTraits<MODE>;
     constexpr int UB = MT::ubits;
     __shared__ StepSmem<KMAX> sm;
+    __shared__ float sB[KMAX][kN];   // the group's B entries, staged on commit steps
 
     const Slot s = slot_of(a);
     const int prow = MT::fp4_out ? fp4_prow(s.lane) : s.prow;
@@ -18,46 +19,55 @@ __global__ void __launch_bounds__(256) split_step_kernel(ReplayParams a) {
 
     // output-source rows are requested first; the prologue runs under them
     Fp4Rows o;
-    typename Raw4<UB>::T raw[32];   // rows 2i + hf of the update source (low modes)
+    typename Raw4<UB>::T raw[kNB][kPerChunk];   // update-source chunks (low modes)
     if constexpr (MT::fp4_out) {
         fp4_rows_load(a, s, o);
     } else {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) raw[i] = load_row4<UB>(a, hrow + 2 * i, s.c);
+        for (int q = 0; q < kNB; ++q)
+#pragma unroll
+            for (int m = 0; m < kPerChunk; ++m) raw[q][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q, m), s.c);
     }
 
     const StepIn in = step_inputs<TIn>(a, s);
     const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;
+    if (in.commit)
+        stage_B<TIn, KMAX>(sB, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.Bin), in.GN, in.k,
+                           in.K);
     float lam, ybuf;
-    typename io<TIn>::raw4 Bj[KMAX];
-    step_prologue<TIn, KMAX>(a, s, in, prow, sm, &lam, &ybuf, Bj);
+    typename io<TIn>::raw4 unused[KMAX];
+    step_prologue<TIn, KMAX, false>(a, s, in, prow, sm, &lam, &ybuf, unused);
 
-    float y0[1];
     if constexpr (MT::fp4_out) {
-        float c8[1][8];
+        float c8[1][8], y0[1];
         load_c8<TIn>(static_cast<const TIn *>(in.Cin), s.lane & 15, c8[0]);
         fp4_rows_dot<1>(o, c8, s.lane, y0);
+        a.y[(size_t)s.b * in.HP + (size_t)s.h * kP + prow] = lam * y0[0] + ybuf;
+        if (in.commit) commit_head<KMAX, MODE>(a, s, lam, sm.cs[s.wave], sB, interval);
     } else {
-        const float4 C4[1] = {io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c)};
-        rows4_dot<UB, 1>(raw, C4, s.lane, y0);
-    }
-    a.y[(size_t)s.b * in.HP + (size_t)s.h * kP + prow] = lam * y0[0] + ybuf;
-
-    if (in.commit) {
-        if constexpr (MT::fp4_out) {
-            commit_head<TIn, KMAX, MODE>(a, s, lam, sm.cs[s.wave], Bj, interval);
-        } else {
+        const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
+        float r[kChunks];
 #pragma unroll
-            for (int q = 0; q < kChunks; ++q) {
-                float4 st[kPerChunk];
+        for (int q = 0; q < kChunks; ++q) {
+            float4 st[kPerChunk];
 #pragma unroll
-                for (int m = 0; m < kPerChunk; ++m) st[m] = decode_row4<UB>(raw[chunk_index(q, m)]);
-                commit_chunk_q<TIn, KMAX, MODE>(a, s, st, q, lam, sm.cs[s.wave], Bj, interval);
+            for (int m = 0; m < kPerChunk; ++m) st[m] = decode_row4<UB>(raw[q % kNB][m]);
+            if (q + kNB < kChunks) {
+#pragma unroll
+                for (int m = 0; m < kPerChunk; ++m)
+                    raw[q % kNB][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q + kNB, m), s.c);
             }
+            float v[kPerChunk];
+#pragma unroll
+            for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(st[m], C4);
+            r[q] = chunk_reduce8(v, s.lane);
+            if (in.commit) commit_chunk_q<KMAX, MODE>(a, s, st, q, lam, sm.cs[s.wave], sB, interval);
         }
-    } else {
-        step_append<TIn>(a, s, in);
+        const float y0 = chunk_combine4(r, s.lane);
+        a.y[(size_t)s.b * in.HP + (size_t)s.h * kP + prow] = lam * y0 + ybuf;
     }
+
+    if (!in.commit) step_append<TIn>(a, s, in);
     publish_position(a, s.b, in.commit ? 0 : in.K, in.commit);
 }
 
