@@ -191,6 +191,31 @@ def main():
         d = [a.elapsed_time(b) * 1e3 for a, b in events]
         return sum(d) / len(d)
 
+    def graph_timing(layers, w, y, t0, reps=16):
+        """Launch-bound small batches: one interval (L steps x layers) captured
+        in a HIP graph and replayed, so host launch cost leaves the timing."""
+        g = torch.cuda.CUDAGraph()
+        s2 = torch.cuda.Stream()
+        s2.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s2):
+            with torch.cuda.graph(g, stream=s2):
+                for i in range(w.interval):
+                    for li, lay in enumerate(layers):
+                        x, Bm, Cm, dt = lay["in"]
+                        t = (t0 + i) % x.shape[0]
+                        rs.step(lay["ls"], x[t], Bm[t], Cm[t], dt[t], y=y[li])
+        torch.cuda.current_stream().wait_stream(s2)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (reps * w.interval)
+        return {"graph_us_per_step": us, "graph_tokens_per_s": y[0].shape[0] / us * 1e6}
+
     def run_standard(w, batch, steps, warmup, with_recurrent=True, per_launch=True):
         n_in = min(steps + warmup, 64) if batch <= 32 else steps + warmup
         layers = make_layers(w, batch, n_in)
@@ -215,6 +240,8 @@ def main():
                 ev = []
                 recurrent_loop(layers, states, warmup + steps, 4 * w.interval, y, ev)
                 out["recurrent_kernel_avg_us"] = per_launch_us(ev)
+        if batch <= 8:
+            out.update(graph_timing(layers, w, y, warmup))
         rb = replay_bytes_per_token(w.heads, w.groups, L=w.interval)
         cb = recurrent_bytes_per_token(w.heads, w.groups)
         out["replay_bytes_per_token_layer"] = rb

@@ -67,6 +67,59 @@ __global__ void __launch_bounds__(256) replay_step_kernel(ReplayParams a) {
 }
 
 // ------------------------------------------------------------------------
+// Small-batch step: one workgroup per head, its 4 waves each stream one
+// chunk (16 rows) of the head's checkpoint, so a batch-1 step spreads over
+// H workgroups x 4 waves instead of H/4 workgroups.  Same arithmetic per row
+// as replay_step_kernel (bit-identical results).
+// ------------------------------------------------------------------------
+template <typename TIn, int KMAX>
+__global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
+    __shared__ StepSmem<KMAX> sm;
+    __shared__ float s_r[kChunks][kWave];
+
+    Slot s;
+    {
+        const int wg = xcd_remap(blockIdx.x, gridDim.x);
+        s.b = wg / a.H;
+        s.tile = wg - s.b * a.H;
+        s.h = s.tile;
+        s.wave = threadIdx.x >> 6;     // = the chunk this wave streams
+        s.lane = threadIdx.x & 63;
+        s.hpg = a.H / a.G;
+        s.g = s.h / s.hpg;
+        s.c = s.lane & 31;
+        s.hf = s.lane >> 5;
+        s.prow = 2 * s.c + s.hf;
+    }
+    const int q = s.wave;
+    float *sp = state_ptr(a.ckpt, s, a.H);
+    float4 cur[kPerChunk];
+    load_chunk(cur, sp, q);
+
+    const StepIn in = step_inputs<TIn>(a, s);
+    const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
+    float lam, ybuf;
+    typename io<TIn>::raw4 Bj[KMAX];
+    step_prologue<TIn, KMAX>(a, s, in, s.prow, sm, &lam, &ybuf, Bj);
+
+    float v[kPerChunk];
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4);
+    s_r[q][s.lane] = chunk_reduce8(v, s.lane);
+    if (in.commit) commit_chunk<TIn, KMAX>(cur, q, lam, sm.cs[s.wave], Bj, s.hf, sp);
+    __syncthreads();
+    if (q == 0) {
+        float r[kChunks];
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) r[c] = s_r[c][s.lane];
+        const float y0 = chunk_combine4(r, s.lane);
+        a.y[(size_t)s.b * in.HP + (size_t)s.h * kP + s.prow] = lam * y0 + ybuf;
+        if (!in.commit) step_append<TIn>(a, s, in);
+    }
+    publish_position(a, s.b, in.commit ? 0 : in.K, in.commit);
+}
+
+// ------------------------------------------------------------------------
 // Speculative verify: outputs of T draft positions, no state written.
 // ------------------------------------------------------------------------
 template <typename TIn, int KMAX, int T>
@@ -145,8 +198,27 @@ __global__ void zero_pos_kernel(int32_t *pos, int n) {
 
 // ---------------------------------------------------------------- launchers --
 
-hipError_t launch_replay_step(const ReplayParams &p, bool in_bf16, hipStream_t stream) {
-    if (p.batch == 0) return hipSuccess;
+// Below this many head-tile workgroups the chip is under-filled and the
+// per-head row split is used instead.
+constexpr int kRowSplitBelow = 512;
+
+hipError_t launch_replay_step(const ReplayParams &p0, bool in_bf16, hipStream_t stream) {
+    if (p0.batch == 0) return hipSuccess;
+    if (p0.batch * p0.wg_per_slot < kRowSplitBelow) {
+        ReplayParams p = p0;
+        p.hpw = 1;
+        p.wg_per_slot = p.H;
+        dim3 grid(p.batch * p.H), block(256);
+        if (p.Lcap <= 16) {
+            if (in_bf16) hipLaunchKernelGGL((replay_step_rows_kernel<uint16_t, 16>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((replay_step_rows_kernel<float, 16>), grid, block, 0, stream, p);
+        } else {
+            if (in_bf16) hipLaunchKernelGGL((replay_step_rows_kernel<uint16_t, 32>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((replay_step_rows_kernel<float, 32>), grid, block, 0, stream, p);
+        }
+        return hipGetLastError();
+    }
+    const ReplayParams &p = p0;
     dim3 grid(p.batch * p.wg_per_slot), block(64 * p.hpw);
     if (p.Lcap <= 16) {
         if (in_bf16) hipLaunchKernelGGL((replay_step_kernel<uint16_t, 16>), grid, block, 0, stream, p);

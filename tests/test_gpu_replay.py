@@ -158,3 +158,66 @@ def test_position_out_of_range_is_flagged(rs):
     with pytest.raises(rs.ReplaySSMError, match="device"):
         rs.check_device_errors(ls)
     rs.check_device_errors(ls)   # sticky flag was cleared by the read
+
+
+def test_row_split_and_tile_kernels_agree_bitwise(rs):
+    """Small batches run the per-head row-split step kernel, large ones the
+    head-tile kernel; both do the same per-row arithmetic, so the slots they
+    share give bit-identical outputs and checkpoints (and match the oracle)."""
+    w = synth.WORKLOADS["tiny"]
+    big, small, steps = 300, 3, 2 * w.interval + 3     # 600 vs 6 workgroups
+    A, D = synth.layer_params(w, 0)
+    S0 = synth.init_state(w, 0, batch=big)
+    x, Bm, Cm, dt = synth.token_inputs(w, 0, steps, batch=big)
+    outs = {}
+    for b in (big, small):
+        ls = rs.LayerState(b, w.heads, w.groups, A, D, in_dtype=x.dtype)
+        rs.load_checkpoint(ls, S0[:b].contiguous().cuda())
+        ys = [rs.step(ls, x[t, :b].contiguous().cuda(), Bm[t, :b].contiguous().cuda(),
+                      Cm[t, :b].contiguous().cuda(), dt[t, :b].contiguous().cuda()).cpu() for t in range(steps)]
+        outs[b] = (torch.stack(ys), ls.ckpt.cpu())
+    assert torch.equal(outs[big][0][:, :small], outs[small][0])
+    assert torch.equal(outs[big][1][:small], outs[small][1])
+    sl = [0, 151, big - 1]
+    y_ref, cks = oracle.decode_run(S0[sl], x[:, sl], Bm[:, sl], Cm[:, sl], dt[:, sl], A, D, w.groups, w.interval)
+    for t in range(steps):
+        assert_close(outs[big][0][t, sl], y_ref[t], f"y step {t} (head-tile kernel)")
+    assert_close(outs[big][1][sl], cks[-1], "checkpoint (head-tile kernel)")
+
+
+def test_step_inside_hip_graph(rs):
+    """One interval of steps captured in a HIP graph and replayed three
+    times, with eager work and syncs between replays: every replay matches
+    eager execution of the same sequence bit for bit."""
+    w = synth.WORKLOADS["tiny"]
+    A, D = synth.layer_params(w, 0)
+    S0 = synth.init_state(w, 0).cuda()
+    x, Bm, Cm, dt = (t.cuda() for t in synth.token_inputs(w, 0, w.interval, stream=9))
+    L = w.interval
+    # eager reference: the same L inputs three times
+    ref = rs.LayerState(w.batch, w.heads, w.groups, A, D, in_dtype=x.dtype)
+    rs.load_checkpoint(ref, S0)
+    eager = [[rs.step(ref, x[t], Bm[t], Cm[t], dt[t]).clone() for t in range(L)] for _ in range(3)]
+    # graph
+    ls = rs.LayerState(w.batch, w.heads, w.groups, A, D, in_dtype=x.dtype)
+    rs.load_checkpoint(ls, S0)
+    ys = [torch.empty(w.batch, w.heads, 64, device="cuda") for _ in range(L)]
+    snap = ls.snapshot()
+    g = torch.cuda.CUDAGraph()
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s2):
+        with torch.cuda.graph(g, stream=s2):
+            for t in range(L):
+                rs.step(ls, x[t], Bm[t], Cm[t], dt[t], y=ys[t])
+    torch.cuda.current_stream().wait_stream(s2)
+    torch.cuda.synchronize()
+    ls.restore(snap)           # capture does not execute; start from the loaded state
+    for r in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for t in range(L):
+            assert torch.equal(ys[t], eager[r][t]), (r, t)
+        _ = (ls.ckpt * 1.0).sum().item()   # unrelated eager work between replays
+    assert torch.equal(ls.ckpt, ref.ckpt)
+    assert ls.pos.cpu().tolist() == ref.pos.cpu().tolist()
