@@ -84,21 +84,35 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=16)
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="write the counter summary from two rocprofv3 --pmc runs of --probe")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("STATS_CSV", "OUT_MD"),
-                    help="write the kernel-trace summary of a rocprofv3 --kernel-trace --stats run")
+    ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "RUN"),
+                    help="write the kernel-trace summary of a rocprofv3 --kernel-trace --stats run "
+                         "(RUN: 'headline' or 'all')")
     ap.add_argument("--probe", action="store_true",
                     help="short fixed run for profiler counters: 16 warm-up + 16 replay steps, "
                          "16 recurrent steps, then 3 plain 1 GiB device copies (calibration)")
     args = ap.parse_args()
 
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace,
-                        command="rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace -o trace -- "
-                                "python -u bench.py --steps 64 --no-extras --no-cpu-baseline",
-                        title="Kernel trace: replay step vs recurrent step, 4B-class layers, batch 256",
-                        workload="batch 256, 4 stacked SSM layers, H=96, G=8, P=64, N=128, L=16, fp32 "
-                                 "checkpoint, bf16 inputs; 16 warm-up + 64 timed + 64 per-launch-timed "
-                                 "steps per path, x 4 layers.")
+        stats, out_md, run = args.summarize_trace
+        if run == "headline":
+            summarize_trace(stats, out_md,
+                            command="rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace -o trace -- "
+                                    "python -u bench.py --steps 64 --no-extras --no-cpu-baseline",
+                            title="Kernel trace: replay step vs recurrent step, 4B-class layers, batch 256",
+                            workload="batch 256, 4 stacked SSM layers, H=96, G=8, P=64, N=128, L=16, fp32 "
+                                     "checkpoint, bf16 inputs; 16 warm-up + 64 timed + 64 per-launch-timed "
+                                     "steps per path, x 4 layers (plus the HBM probe launches).")
+        else:
+            summarize_trace(stats, out_md,
+                            command="rocprofv3 --kernel-trace --stats -f csv -d gpurun_out/trace_all -o trace -- "
+                                    "python -u bench.py --steps 64 --no-cpu-baseline",
+                            title="Kernel trace: every benchmarked path",
+                            workload="4B-class layers at batch 256 (64 timed steps), 1 and 512; 120B-class "
+                                     "(batch 256, 8 layers, 128 heads); speculative verify + accept "
+                                     "(batch 512, 4 drafts) and its per-draft-copy baseline; the precision "
+                                     "split formats (batch 256, 4 layers) and their drift runs.  Kernel names "
+                                     "carry <input type, max buffer entries, ...> template arguments; "
+                                     "split modes 0..4 = split-bf16, split-e4m3, shared-fp4, low-bf16, low-e4m3.")
         return
     if args.summarize_counters:
         cmd = ("rocprofv3 --pmc COUNTER -f csv -d gpurun_out/pmc_COUNTER -o pmc -- "
@@ -265,6 +279,28 @@ def main():
         log("[bench] probe done: 32 replay steps, 16 recurrent steps, 3 x 1 GiB copies")
         return
 
+    # ------------------------------------------------- practical HBM ceilings
+    def hbm_ceilings(nbytes=4 << 30, reps=5):
+        src = torch.ones(nbytes // 4, device=dev)
+        dst = torch.empty_like(src)
+        best = {"read": 0.0, "copy": 0.0}
+        for grid in (1024, 2048, 4096):
+            for mode, name in ((0, "read"), (1, "copy")):
+                rs.hbm_probe(mode, src, dst, grid)
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    rs.hbm_probe(mode, src, dst, grid)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                gbps = (nbytes if mode == 0 else 2 * nbytes) * reps / (e0.elapsed_time(e1) * 1e6)
+                best[name] = max(best[name], gbps)
+        del src, dst
+        torch.cuda.empty_cache()
+        return {"read_GBps": round(best["read"], 1), "copy_GBps": round(best["copy"], 1),
+                "probe": "4 GiB grid-stride stream, 16-byte non-temporal loads/stores, best of grids 1024/2048/4096"}
+
     # -------------------------------------------------------------- headline
     log(f"[bench] {w.describe()} batch={args.batch} steps={args.steps} warmup={args.warmup}")
     main_res = run_standard(w, args.batch, args.steps, args.warmup)
@@ -280,6 +316,17 @@ def main():
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "bytes_per_launch": rb * args.batch, "avg_launch_us": round(avg_us, 2)}
 
+    ceil = hbm_ceilings()
+    log(f"[bench] practical HBM ceilings: read {ceil['read_GBps']:.0f} GB/s, copy {ceil['copy_GBps']:.0f} GB/s")
+    roofline["practical_ceiling"] = ceil
+    # the kernel's bytes at the practical rates: read-only steps at the read
+    # ceiling, the commit step's extra state write at the copy ceiling
+    wl = synth.WORKLOADS["4b"]
+    st_bytes = wl.heads * 64 * 128 * 4 * args.batch
+    rest = rb * args.batch - st_bytes - st_bytes / wl.interval
+    t_ideal = ((wl.interval - 1) * (st_bytes + rest) / (ceil["read_GBps"] * 1e9)
+               + (2 * st_bytes + rest) / (ceil["copy_GBps"] * 1e9)) / wl.interval
+    roofline["frac_of_practical"] = round(t_ideal / (avg_us * 1e-6), 4)
     extras = {"recurrent_baseline": {k: main_res[k] for k in main_res if k.startswith("recurrent")},
               "replay_speedup_vs_recurrent": main_res.get("replay_speedup_vs_recurrent")}
     if not args.no_extras:

@@ -231,6 +231,17 @@ const char *replayssm_last_error(void);
  * RSSM_E_HIP. */
 int replayssm_check_device_errors(const rssm_state *st, int32_t batch, hipStream_t stream);
 
+/*
+ * Diagnostic: stream `bytes` (a multiple of 16) through HBM with the same
+ * 16-byte non-temporal accesses as the state-streaming kernels, so callers
+ * can time the practical ceiling next to the kernels' achieved bandwidth.
+ * mode 0 = read src (dst receives grid*256 floats of partial sums and must
+ * hold that many), mode 1 = copy src -> dst (both `bytes` long).  grid
+ * workgroups of 256 threads in a grid-stride loop.  Asynchronous on stream.
+ */
+int replayssm_hbm_probe(int32_t mode, const void *src, void *dst, size_t bytes, int32_t grid,
+                        hipStream_t stream);
+
 /* Library version string. */
 const char *replayssm_version(void);
 

@@ -86,6 +86,8 @@ def lib() -> ctypes.CDLL:
         L.replayssm_last_error.restype = ctypes.c_char_p
         L.replayssm_check_device_errors.argtypes = [_SP, i32, _vp]
         L.replayssm_version.restype = ctypes.c_char_p
+        L.replayssm_hbm_probe.argtypes = [i32, _vp, _vp, ctypes.c_size_t, i32, _vp]
+        L.replayssm_hbm_probe.restype = ctypes.c_int
         for name in ("replayssm_step", "replayssm_verify", "replayssm_accept", "replayssm_commit",
                      "replayssm_load_checkpoint", "replayssm_recurrent_step",
                      "replayssm_recurrent_verify", "replayssm_recurrent_accept",
@@ -264,6 +266,12 @@ def load_checkpoint(ls: LayerState, src: torch.Tensor, stream=None) -> None:
     st = ls.cstate()
     _check(lib().replayssm_load_checkpoint(ctypes.byref(ls._desc), ctypes.byref(st), _ptr(src),
                                            _stream(stream)))
+
+
+def hbm_probe(mode: int, src: torch.Tensor, dst: torch.Tensor, grid: int, stream=None) -> None:
+    """Launch the library's HBM streaming probe (0 = read src, 1 = copy src to dst)."""
+    _check(lib().replayssm_hbm_probe(mode, _ptr(src), _ptr(dst), src.numel() * src.element_size(), grid,
+                                     _stream(stream)))
 
 
 def check_device_errors(ls: LayerState, stream=None) -> None:
