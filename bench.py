@@ -390,20 +390,23 @@ def run_spec(rs, L, torch, synth, dev, stream, sh, log, rounds=64, warm=8):
         ls = rs.LayerState(w.batch, w.heads, w.groups, A, D, interval=w.interval, max_draft=T,
                            in_dtype=x.dtype, device=dev, layer_id=l)
         rs.load_checkpoint(ls, S0)
-        layers.append({"ls": ls, "desc": ls.desc(), "st": ls.cstate(), "S0": S0,
+        ddesc = rs.RssmDesc.from_buffer_copy(ls.desc())
+        ddesc.deferred_commit = 1      # same layer, declared for deferred accepts
+        layers.append({"ls": ls, "desc": ls.desc(), "ddesc": ddesc, "st": ls.cstate(), "S0": S0,
                        "in": (bt(x), bt(Bm), bt(Cm), bt(dt)), "A": ls.A, "D": ls.D})
     y = torch.empty(w.batch, T, w.heads, 64, device=dev)
 
-    def replay_rounds(r0, n):
+    def replay_rounds(r0, n, deferred=False):
+        accept = L.replayssm_accept_deferred if deferred else L.replayssm_accept
         for i in range(n):
             r = (r0 + i) % nin
             for lay in layers:
                 x, Bm, Cm, dt = lay["in"]
-                rc = L.replayssm_verify(ctypes.byref(lay["desc"]), ctypes.byref(lay["st"]), T,
+                d = lay["ddesc"] if deferred else lay["desc"]
+                rc = L.replayssm_verify(ctypes.byref(d), ctypes.byref(lay["st"]), T,
                                         x[r].data_ptr(), Bm[r].data_ptr(), Cm[r].data_ptr(),
                                         dt[r].data_ptr(), y.data_ptr(), sh)
-                rc |= L.replayssm_accept(ctypes.byref(lay["desc"]), ctypes.byref(lay["st"]),
-                                         nk[r].data_ptr(), T, sh)
+                rc |= accept(ctypes.byref(d), ctypes.byref(lay["st"]), nk[r].data_ptr(), T, sh)
                 if rc:
                     raise RuntimeError(L.replayssm_last_error().decode())
 
@@ -419,9 +422,14 @@ def run_spec(rs, L, torch, synth, dev, stream, sh, log, rounds=64, warm=8):
     replay_rounds(0, warm)
     sec = t(replay_rounds, warm, rounds)
     kept = float(nk.double().mean()) * w.batch * rounds
+    # deferred accept: the commit folds into the next round's verify
+    replay_rounds(warm + rounds, warm, True)
+    dsec = t(replay_rounds, 2 * warm + rounds, rounds, True)
     out = {"batch": w.batch, "layers": w.layers, "heads": w.heads, "drafts": w.drafts,
            "rounds": rounds, "replay_ms_per_round": sec / rounds * 1e3,
-           "replay_kept_tokens_per_s": kept / sec}
+           "replay_kept_tokens_per_s": kept / sec,
+           "deferred_ms_per_round": dsec / rounds * 1e3,
+           "deferred_kept_tokens_per_s": kept / dsec}
     # conventional: a pool of T+1 states per slot, one copy written per draft
     pools, sels = [], []
     for lay in layers:
@@ -452,8 +460,10 @@ def run_spec(rs, L, torch, synth, dev, stream, sh, log, rounds=64, warm=8):
     out["recurrent_ms_per_round"] = rsec / rounds * 1e3
     out["recurrent_kept_tokens_per_s"] = kept / rsec
     out["replay_speedup_vs_recurrent"] = rsec / sec
-    log(f"[bench] spec: replay {out['replay_kept_tokens_per_s']:.0f} kept tok/s, "
-        f"recurrent {out['recurrent_kept_tokens_per_s']:.0f} ({out['replay_speedup_vs_recurrent']:.2f}x)")
+    out["deferred_speedup_vs_recurrent"] = rsec / dsec
+    log(f"[bench] spec: replay {out['replay_kept_tokens_per_s']:.0f} kept tok/s (deferred commit "
+        f"{out['deferred_kept_tokens_per_s']:.0f}), recurrent {out['recurrent_kept_tokens_per_s']:.0f} "
+        f"({out['replay_speedup_vs_recurrent']:.2f}x / {out['deferred_speedup_vs_recurrent']:.2f}x)")
     del pools, layers
     torch.cuda.empty_cache()
     return out

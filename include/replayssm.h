@@ -120,6 +120,8 @@ typedef struct rssm_desc {
     int32_t shared_lowp;  /* 1: the FP4 output copy is the only state (ablation; ckpt_dtype NONE) */
     int32_t layer_id;     /* stochastic-rounding stream: layer index */
     uint64_t seed;        /* stochastic-rounding stream: key */
+    int32_t deferred_commit; /* 1: replayssm_accept_deferred may be used on this layer (F32 checkpoint,
+                                max_draft >= 2, L + Tmax <= 32); verify then also runs the fold pass */
 } rssm_desc;
 
 /* Device buffers of one layer (host struct of device pointers). */
@@ -130,7 +132,8 @@ typedef struct rssm_state {
     void *xbuf;           /* [B,Lcap,H,P] in_dtype */
     void *bbuf;           /* [B,Lcap,G,N] in_dtype */
     void *dtbuf;          /* [B,Lcap,H]   in_dtype */
-    int32_t *pos;         /* [B] valid buffer entries since the checkpoint, 0..L-1 at rest */
+    int32_t *pos;         /* [B] valid buffer entries since the checkpoint: 0..L-1 at rest,
+                             up to Lcap after replayssm_accept_deferred */
     int32_t *intv;        /* [B] checkpoints written so far (the rounding stream's interval index) */
     int32_t *work;        /* [B+1] library scratch: per-slot arrival counters + sticky error word; zero-initialise once */
     const float *A;       /* [H] decay rate, A < 0 */
@@ -145,6 +148,9 @@ typedef struct rssm_state {
  * appended at buffer entry k and pos becomes k + 1.  If k + 1 == L the
  * checkpoint is rewritten in the same pass that reads it (S_L from the
  * replayed form above), pos becomes 0 and intv is incremented.
+ * A slot with k >= L (left by replayssm_accept_deferred) is handled the
+ * same way: the output replays all k + 1 tokens and the pass commits them
+ * (pos = 0, intv + 1).
  * x [B,H,P], B, C [B,G,N], dt [B,H] (in_dtype); y [B,H,P] fp32.
  */
 int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x,
@@ -156,6 +162,11 @@ int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x,
  * are appended at buffer entries pos .. pos+T-1 and the outputs of all T
  * positions are produced from the checkpoint and the buffer; no state is
  * written and pos is unchanged.  Requires 1 <= T <= max_draft.
+ * F32 checkpoints only: a slot with pos >= L (left by
+ * replayssm_accept_deferred) has its accepted entries folded into the
+ * checkpoint in the same pass that reads it (a commit: pos = 0, intv + 1),
+ * and its drafts are appended at entries 0 .. T-1 of the next interval.
+ * The outputs are bit-identical to those after an eager accept.
  * x [B,T,H,P], B, C [B,T,G,N], dt [B,T,H] (in_dtype); y [B,T,H,P] fp32.
  */
 int replayssm_verify(const rssm_desc *desc, const rssm_state *st, int32_t T,
@@ -174,8 +185,26 @@ int replayssm_accept(const rssm_desc *desc, const rssm_state *st,
                      const int32_t *n_keep, int32_t T, hipStream_t stream);
 
 /*
+ * Deferred accept (article section 3, with the commit deferred): pos[b] +=
+ * n_keep[b] and nothing else; the checkpoint is not touched.  A slot whose
+ * count reaches L (up to Lcap = L + Tmax - 1 entries) is folded by the next
+ * replayssm_step, replayssm_verify or replayssm_commit on it, inside the pass
+ * that reads the checkpoint anyway, which saves one checkpoint read and
+ * write per interval against replayssm_accept.  Like replayssm_accept it
+ * follows a verify (pos <= L-1 on entry; flagged otherwise).  Requires
+ * desc->deferred_commit = 1 (RSSM_E_ARG otherwise), which in turn requires
+ * an F32 checkpoint and max_draft >= 2 (else RSSM_E_UNSUPPORTED) and
+ * L + Tmax <= 32 (else RSSM_E_CAPACITY: a step on a slot left at Lcap
+ * entries replays Lcap + 1).  Outputs and checkpoints of a verify after a
+ * deferred accept are bit-identical to those after replayssm_accept.
+ */
+int replayssm_accept_deferred(const rssm_desc *desc, const rssm_state *st,
+                              const int32_t *n_keep, int32_t T, hipStream_t stream);
+
+/*
  * Flush: commit every slot with pos > 0 (checkpoint <- state after its
- * buffered tokens, pos = 0, intv + 1).  Slots with pos == 0 are untouched.
+ * buffered tokens, pos = 0, intv + 1), including slots holding up to Lcap
+ * entries after a deferred accept.  Slots with pos == 0 are untouched.
  */
 int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t stream);
 

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "F32", "BF16", "FP8_E4M3", "FP4_E2M1", "NONE", "ReplaySSMError", "lib", "LayerState",
-    "step", "verify", "accept", "commit", "load_checkpoint", "recurrent_step",
+    "step", "verify", "accept", "accept_deferred", "commit", "load_checkpoint", "recurrent_step",
     "recurrent_verify", "recurrent_accept", "buffer_capacity", "check_device_errors",
 ]
 
@@ -40,7 +40,7 @@ class RssmDesc(ctypes.Structure):
         ("d_state", ctypes.c_int32), ("n_groups", ctypes.c_int32), ("interval", ctypes.c_int32),
         ("max_draft", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("ckpt_dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32), ("shared_lowp", ctypes.c_int32), ("layer_id", ctypes.c_int32),
-        ("seed", ctypes.c_uint64),
+        ("seed", ctypes.c_uint64), ("deferred_commit", ctypes.c_int32),
     ]
 
 
@@ -72,6 +72,7 @@ def lib() -> ctypes.CDLL:
         L.replayssm_step.argtypes = [_DP, _SP, _vp, _vp, _vp, _vp, _vp, _vp]
         L.replayssm_verify.argtypes = [_DP, _SP, i32, _vp, _vp, _vp, _vp, _vp, _vp]
         L.replayssm_accept.argtypes = [_DP, _SP, _vp, i32, _vp]
+        L.replayssm_accept_deferred.argtypes = [_DP, _SP, _vp, i32, _vp]
         L.replayssm_commit.argtypes = [_DP, _SP, _vp]
         L.replayssm_load_checkpoint.argtypes = [_DP, _SP, _vp, _vp]
         L.replayssm_recurrent_step.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -88,7 +89,8 @@ def lib() -> ctypes.CDLL:
         L.replayssm_version.restype = ctypes.c_char_p
         L.replayssm_hbm_probe.argtypes = [i32, _vp, _vp, ctypes.c_size_t, i32, _vp]
         L.replayssm_hbm_probe.restype = ctypes.c_int
-        for name in ("replayssm_step", "replayssm_verify", "replayssm_accept", "replayssm_commit",
+        for name in ("replayssm_step", "replayssm_verify", "replayssm_accept", "replayssm_accept_deferred",
+                     "replayssm_commit",
                      "replayssm_load_checkpoint", "replayssm_recurrent_step",
                      "replayssm_recurrent_verify", "replayssm_recurrent_accept",
                      "replayssm_check_desc", "replayssm_check_device_errors"):
@@ -118,10 +120,11 @@ _IN_DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 
 def _make_desc(batch, heads, head_dim, d_state, groups, interval, max_draft, in_dtype,
-               ckpt_dtype=F32, out_dtype=NONE, shared_lowp=0, layer_id=0, seed=0) -> RssmDesc:
+               ckpt_dtype=F32, out_dtype=NONE, shared_lowp=0, layer_id=0, seed=0,
+               deferred_commit=0) -> RssmDesc:
     return RssmDesc(batch, heads, head_dim, d_state, groups, interval, max_draft,
                     _IN_DTYPES[in_dtype] if isinstance(in_dtype, torch.dtype) else int(in_dtype),
-                    ckpt_dtype, out_dtype, shared_lowp, layer_id, seed)
+                    ckpt_dtype, out_dtype, shared_lowp, layer_id, seed, int(deferred_commit))
 
 
 def buffer_capacity(interval: int, max_draft: int = 1) -> int:
@@ -151,7 +154,8 @@ class LayerState:
     def __init__(self, batch: int, heads: int, groups: int, A: torch.Tensor, D: torch.Tensor, *,
                  head_dim: int = 64, d_state: int = 128, interval: int = 16, max_draft: int = 1,
                  in_dtype: torch.dtype = torch.bfloat16, device="cuda", layer_id: int = 0,
-                 seed: int = 0, state_format: str = "f32", debug_prequant: bool = False):
+                 seed: int = 0, state_format: str = "f32", debug_prequant: bool = False,
+                 deferred_commit: bool = False):
         self.batch, self.heads, self.groups = batch, heads, groups
         self.head_dim, self.d_state, self.interval, self.max_draft = head_dim, d_state, interval, max_draft
         self.in_dtype = in_dtype
@@ -181,7 +185,7 @@ class LayerState:
         self.D = D.to(device=dev, dtype=torch.float32).contiguous()
         self._desc = _make_desc(batch, heads, head_dim, d_state, groups, interval, max_draft,
                                 in_dtype, ckpt_dtype=ck, out_dtype=od, shared_lowp=sh,
-                                layer_id=layer_id, seed=seed)
+                                layer_id=layer_id, seed=seed, deferred_commit=deferred_commit)
         _check(lib().replayssm_check_desc(ctypes.byref(self._desc)))
 
     def desc(self) -> RssmDesc:
@@ -250,6 +254,16 @@ def accept(ls: LayerState, n_keep: torch.Tensor, T: int, stream=None) -> None:
     st = ls.cstate()
     _check(lib().replayssm_accept(ctypes.byref(ls._desc), ctypes.byref(st), _ptr(n_keep), T,
                                   _stream(stream)))
+
+
+def accept_deferred(ls: LayerState, n_keep: torch.Tensor, T: int, stream=None) -> None:
+    """Keep the first n_keep[b] verified positions without committing: slots
+    reaching the interval length are folded by their next step / verify /
+    commit (replayssm_accept_deferred; fp32 checkpoints)."""
+    _need(n_keep, (ls.batch,), torch.int32, "n_keep")
+    st = ls.cstate()
+    _check(lib().replayssm_accept_deferred(ctypes.byref(ls._desc), ctypes.byref(st), _ptr(n_keep), T,
+                                           _stream(stream)))
 
 
 def commit(ls: LayerState, stream=None) -> None:

@@ -46,6 +46,10 @@ int split_mode(const rssm_desc *d) {
     return -1;
 }
 
+// Deferred accepts (declared by desc->deferred_commit) can leave up to Lcap
+// entries in a slot; a step on such a slot replays and commits one more.
+bool deferred_ok(const rssm_desc *d) { return d->deferred_commit == 1; }
+
 int check_desc(const rssm_desc *d) {
     if (!d) return fail(RSSM_E_ARG, "desc is NULL");
     if (d->batch < 0) return fail(RSSM_E_ARG, "batch %d < 0", d->batch);
@@ -76,6 +80,17 @@ int check_desc(const rssm_desc *d) {
             return fail(RSSM_E_UNSUPPORTED, "ckpt_dtype %d: F32, BF16 or FP8_E4M3", d->ckpt_dtype);
         if (d->ckpt_dtype == RSSM_F32 && d->out_dtype != RSSM_NONE)
             return fail(RSSM_E_UNSUPPORTED, "an FP4 output copy goes with a BF16 / FP8 update checkpoint");
+    }
+    if (d->deferred_commit != 0 && d->deferred_commit != 1)
+        return fail(RSSM_E_ARG, "deferred_commit must be 0 or 1");
+    if (d->deferred_commit) {
+        if (split_mode(d) >= 0)
+            return fail(RSSM_E_UNSUPPORTED, "deferred_commit: F32 checkpoints only");
+        if (d->max_draft < 2)
+            return fail(RSSM_E_UNSUPPORTED, "deferred_commit: needs max_draft >= 2 (speculative rounds)");
+        if (lcap_of(d) + 1 > kMaxLcap)
+            return fail(RSSM_E_CAPACITY, "deferred_commit: interval + max_draft = %d exceeds %d",
+                        d->interval + d->max_draft, kMaxLcap);
     }
     if ((int64_t)d->batch * d->n_heads > (int64_t)1 << 24)
         return fail(RSSM_E_ARG, "batch * n_heads too large");
@@ -113,6 +128,7 @@ rssm::ReplayParams replay_params(const rssm_desc *d, const rssm_state *s) {
     p.G = d->n_groups;
     p.L = d->interval;
     p.Lcap = lcap_of(d);
+    p.kmax = deferred_ok(d) ? p.Lcap : d->interval - 1;
     p.T = 1;
     p.hpw = heads_per_wg(d);
     p.wg_per_slot = d->n_heads / p.hpw;
@@ -199,6 +215,22 @@ int replayssm_accept(const rssm_desc *desc, const rssm_state *st, const int32_t 
     const int mode = split_mode(desc);
     if (mode >= 0) return hip_status(rssm::launch_split_commit(p, bf, mode, true, stream), "split accept launch");
     return hip_status(rssm::launch_replay_commit(p, bf, true, stream), "accept launch");
+}
+
+int replayssm_accept_deferred(const rssm_desc *desc, const rssm_state *st, const int32_t *n_keep, int32_t T,
+                              hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    if (T < 1 || T > desc->max_draft)
+        return fail(RSSM_E_CAPACITY, "accept_deferred: T = %d outside 1..max_draft (%d)", T, desc->max_draft);
+    if (!deferred_ok(desc))
+        return fail(RSSM_E_ARG, "accept_deferred: the descriptor does not declare deferred_commit");
+    RSSM_TRY(check_state(desc, st));
+    if (desc->batch == 0) return RSSM_OK;
+    if (!n_keep) return fail(RSSM_E_ARG, "accept_deferred: n_keep is NULL");
+    rssm::ReplayParams p = replay_params(desc, st);
+    p.n_keep = n_keep;
+    p.T = T;
+    return hip_status(rssm::launch_defer_accept(p, stream), "deferred accept launch");
 }
 
 int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t stream) {
@@ -340,6 +372,6 @@ int replayssm_hbm_probe(int32_t mode, const void *src, void *dst, size_t bytes, 
                       "hbm probe launch");
 }
 
-const char *replayssm_version(void) { return "replayssm-gfx950 0.2"; }
+const char *replayssm_version(void) { return "replayssm-gfx950 0.3"; }
 
 }  // extern "C"

@@ -16,9 +16,9 @@ struct Slot {
     int b, tile, wave, lane, h, g, c, hf, prow, hpg;
 };
 
-__device__ __forceinline__ Slot slot_of(const ReplayParams &a) {
+// Slot, head tile and lane roles of logical workgroup `wg`.
+__device__ __forceinline__ Slot slot_at(const ReplayParams &a, int wg) {
     Slot s;
-    const int wg = xcd_remap(blockIdx.x, gridDim.x);
     s.b = wg / a.wg_per_slot;
     s.tile = wg - s.b * a.wg_per_slot;
     s.wave = threadIdx.x >> 6;
@@ -30,6 +30,10 @@ __device__ __forceinline__ Slot slot_of(const ReplayParams &a) {
     s.hf = s.lane >> 5;
     s.prow = 2 * s.c + s.hf;
     return s;
+}
+
+__device__ __forceinline__ Slot slot_of(const ReplayParams &a) {
+    return slot_at(a, xcd_remap(blockIdx.x, gridDim.x));
 }
 
 // Lane base pointer into head (b,h) of an fp32 state: row hf, columns 4c..;
@@ -121,19 +125,20 @@ struct StepIn {
     const void *xin, *Bin, *Cin, *dtin, *xb, *bb, *db;   // typed by the caller
 };
 
-// Reads pos (clamped into 0..L-1, flagged otherwise) and sets the slot's
-// input / buffer pointers.
+// Reads pos (clamped into 0..kmax, flagged otherwise) and sets the slot's
+// input / buffer pointers.  kmax is L-1, or Lcap where deferred accepts can
+// leave k >= L entries: the step then replays and commits all k+1.
 template <typename TIn>
-__device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s) {
+__device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s, int kmax) {
     StepIn in;
     int k = a.pos[s.b];
-    if (k < 0 || k > a.L - 1) {
+    if (k < 0 || k > kmax) {
         if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrPos);
-        k = k < 0 ? 0 : a.L - 1;
+        k = k < 0 ? 0 : kmax;
     }
     in.k = k;
     in.K = k + 1;
-    in.commit = (in.K == a.L);
+    in.commit = (in.K >= a.L);   // > L only after a deferred accept
     in.HP = (size_t)a.H * kP;
     in.GN = (size_t)a.G * kN;
     in.xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.b * in.HP + (size_t)s.h * kP;
@@ -283,12 +288,12 @@ struct VerifyIn {
 };
 
 template <typename TIn, int T>
-__device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const Slot &s) {
+__device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const Slot &s, int kmax) {
     VerifyIn in;
     int k = a.pos[s.b];
-    if (k < 0 || k > a.L - 1) {
+    if (k < 0 || k > kmax) {
         if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrPos);
-        k = k < 0 ? 0 : a.L - 1;
+        k = k < 0 ? 0 : kmax;
     }
     in.k = k;
     in.KL = k + T;   // entries once all drafts are appended
@@ -385,8 +390,145 @@ __device__ __forceinline__ void verify_prologue(const ReplayParams &a, const Slo
     }
 }
 
+// ---- Split form of the verify prologue for the verify kernel.  Loads
+// retire in issue order, so a wave waiting for a load issued after the
+// checkpoint chunks also waits for those chunks: verify_preload issues every
+// prologue load (x rows, dt, and the Gram operands B_j / C_t as raw pieces)
+// before the kernel starts the checkpoint stream, and verify_finish consumes
+// them: Gram rows from LDS, then per-wave decay sums and weights in
+// registers.  Arithmetic and summation order are those of verify_prologue,
+// so results are bit-identical to it.
+template <int KMAX, int T>
+constexpr int stage_pieces() { return (KMAX + T) * (kN / 4); }
+template <int KMAX, int T>
+constexpr int stage_iters() { return (stage_pieces<KMAX, T>() + 255) / 256; }
+
+template <typename TIn, int KMAX, int T>
+struct VerifyPre {
+    float xv[KMAX];   // x_j[prow], entry j < KL (clamped past it)
+    float xt[T];      // x_t[prow] of the drafts
+    float d;          // dt of entry `lane` (lane < KL), else 0
+    typename io<TIn>::raw4 g[stage_iters<KMAX, T>()];   // Gram operand pieces
+};
+
+template <int KMAX, int T>
+struct VerifySmemF {
+    float G[KMAX + T][kN];   // rows 0..KL-1: B_j; rows KL..KL+T-1: C_t (fp32)
+    float gram[T][KMAX];
+};
+
+// Gram operand piece q (4 elements): row q/32 of the staged rows.
+template <typename TIn>
+__device__ __forceinline__ const TIn *stage_src(const VerifyIn &in, int q) {
+    const int row = q >> 5, col = 4 * (q & 31);
+    const TIn *bb = static_cast<const TIn *>(in.bb), *Bin = static_cast<const TIn *>(in.Bin);
+    const TIn *Cin = static_cast<const TIn *>(in.Cin);
+    const TIn *p = row < in.k ? bb + (size_t)row * in.GN
+                 : row < in.KL ? Bin + (size_t)(row - in.k) * in.GN
+                 : Cin + (size_t)(row - in.KL) * in.GN;
+    return p + col;
+}
+
+template <typename TIn, int KMAX, int T>
+__device__ __forceinline__ void verify_preload(const ReplayParams &a, const Slot &s, const VerifyIn &in, int prow,
+                                               VerifyPre<TIn, KMAX, T> &pre) {
+    const int k = in.k;
+    const TIn *xin = static_cast<const TIn *>(in.xin);
+    const TIn *xb = static_cast<const TIn *>(in.xb);
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        int t = j - k;
+        t = t < 0 ? 0 : (t > T - 1 ? T - 1 : t);
+        const TIn *px = (j < k) ? xb + (size_t)j * in.HP + prow : xin + (size_t)t * in.HP + prow;
+        pre.xv[j] = io<TIn>::load1(px);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) pre.xt[t] = io<TIn>::load1(xin + (size_t)t * in.HP + prow);
+    pre.d = 0.f;
+    if (s.lane < in.KL) {
+        const TIn *pd = (s.lane < k) ? static_cast<const TIn *>(in.db) + (size_t)s.lane * a.H
+                                     : static_cast<const TIn *>(in.dtin) + (size_t)(s.lane - k) * a.H;
+        pre.d = io<TIn>::load1(pd);
+    }
+    const int nq = (in.KL + T) * (kN / 4);
+#pragma unroll
+    for (int i = 0; i < stage_iters<KMAX, T>(); ++i) {
+        const int q = threadIdx.x + i * blockDim.x;
+        if (q < nq) pre.g[i] = io<TIn>::load_raw4(stage_src<TIn>(in, q));
+    }
+}
+
+// Returns ybuf[t] = sum_{j < k+t+1} w_tj (B_j . C_t) x_j[prow] + D x_t[prow]
+// and lam[t] = Lambda_t (uniform across the wave).
+template <typename TIn, int KMAX, int T>
+__device__ __forceinline__ void verify_finish(const ReplayParams &a, const Slot &s, const VerifyIn &in,
+                                              const VerifyPre<TIn, KMAX, T> &pre, VerifySmemF<KMAX, T> &sm,
+                                              float (&ybuf)[T], float (&lam)[T]) {
+    const int k = in.k, KL = in.KL;
+    const int nq = (KL + T) * (kN / 4);
+#pragma unroll
+    for (int i = 0; i < stage_iters<KMAX, T>(); ++i) {
+        const int q = threadIdx.x + i * blockDim.x;
+        if (q < nq) *reinterpret_cast<float4 *>(&sm.G[q >> 5][4 * (q & 31)]) = io<TIn>::widen(pre.g[i]);
+    }
+    // workgroups narrower than 256 threads stage the remaining pieces directly
+    for (int q = threadIdx.x + stage_iters<KMAX, T>() * blockDim.x; q < nq; q += blockDim.x)
+        *reinterpret_cast<float4 *>(&sm.G[q >> 5][4 * (q & 31)]) = io<TIn>::load4(stage_src<TIn>(in, q));
+    __syncthreads();
+    {   // Gram g[t][j] = B_j . C_t, 16 lanes x 8 elements per dot
+        const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4, ngrp = blockDim.x >> 4;
+        for (int dd = grp; dd < T * KL; dd += ngrp) {
+            const int t = dd / KL, j = dd - t * KL;
+            const float4 b0 = *reinterpret_cast<const float4 *>(&sm.G[j][8 * t16]);
+            const float4 b1 = *reinterpret_cast<const float4 *>(&sm.G[j][8 * t16 + 4]);
+            const float4 c0 = *reinterpret_cast<const float4 *>(&sm.G[KL + t][8 * t16]);
+            const float4 c1 = *reinterpret_cast<const float4 *>(&sm.G[KL + t][8 * t16 + 4]);
+            const float acc = row16_sum(dot4(b0, c0) + dot4(b1, c1));
+            if (t16 == 0) sm.gram[t][j] = acc;
+        }
+    }
+    __syncthreads();
+
+    // Per wave (head): l_i = A dt_i lives in lane i.  Suffix sums
+    // sum_{lane < i <= k+t} l_i and prefix sums sum_{i <= k+t} l_i grow in
+    // ascending i, one entry per step, as the sequential loops add them.
+    const float Dh = a.D[s.h];
+    const float l = a.A[s.h] * pre.d;
+    float suf = 0.f, tot = 0.f;
+    for (int i = 0; i <= k; ++i) {
+        const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
+        tot += li;
+        if (i > s.lane) suf += li;
+    }
+    float cy[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        if (t > 0) {
+            const int i = k + t;
+            const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
+            tot += li;
+            if (i > s.lane) suf += li;
+        }
+        lam[t] = expf(tot);
+        cy[t] = (s.lane < k + t + 1) ? pre.d * expf(suf) * sm.gram[t][s.lane < KMAX ? s.lane : 0] : 0.f;
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int Kt = k + t + 1;
+        float acc = Dh * pre.xt[t];
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cy[t]), j));
+            const float term = cj * pre.xv[j];
+            acc += (j < Kt) ? term : 0.f;
+        }
+        ybuf[t] = acc;
+    }
+}
+
 // Append the T drafts at entries k .. k+T-1 (the position is not advanced).
-template <typename TIn, int T>
+// WRITE_B = false leaves the group's B entries to publish_fold.
+template <typename TIn, int T, bool WRITE_B = true>
 __device__ __forceinline__ void verify_append(const ReplayParams &a, const Slot &s, const VerifyIn &in) {
     const TIn *xin = static_cast<const TIn *>(in.xin);
     const TIn *Bin = static_cast<const TIn *>(in.Bin);
@@ -400,7 +542,7 @@ __device__ __forceinline__ void verify_append(const ReplayParams &a, const Slot 
         TIn *dw = reinterpret_cast<TIn *>(a.dtbuf) + ((size_t)s.b * a.Lcap + in.k + s.lane) * a.H + s.h;
         io<TIn>::copy1(dw, dtin + (size_t)s.lane * a.H);
     }
-    if (s.wave == 0 && (s.tile * a.hpw) % s.hpg == 0) {
+    if (WRITE_B && s.wave == 0 && (s.tile * a.hpw) % s.hpg == 0) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             TIn *bw = reinterpret_cast<TIn *>(a.bbuf) + ((size_t)s.b * a.Lcap + in.k + t) * in.GN + (size_t)s.g * kN;
@@ -422,10 +564,13 @@ struct CommitSmem {
 
 template <bool ACCEPT>
 __device__ __forceinline__ int commit_count(const ReplayParams &a, const Slot &s, bool *commit) {
+    // an accept follows a verify (k <= L-1); a flush also folds the up to
+    // Lcap entries a deferred accept can leave
+    const int kmax = ACCEPT ? a.L - 1 : a.Lcap;
     int k = a.pos[s.b];
-    if (k < 0 || k > a.L - 1) {
+    if (k < 0 || k > kmax) {
         if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrPos);
-        k = k < 0 ? 0 : a.L - 1;
+        k = k < 0 ? 0 : kmax;
     }
     int nk = 0;
     if (ACCEPT) {
@@ -444,7 +589,8 @@ __device__ __forceinline__ int commit_count(const ReplayParams &a, const Slot &s
 // all K buffered entries (K >= 1).
 template <typename TIn, int KMAX, bool LOAD_BJ = true>
 __device__ __forceinline__ float commit_prologue(const ReplayParams &a, const Slot &s, int K,
-                                                 CommitSmem<KMAX> &sm,
+                                                 float (*sl)[KMAX], float (*sw)[KMAX],
+                                                 float (*scs)[kP * KMAX],
                                                  typename io<TIn>::raw4 (&Bj)[KMAX]) {
     const size_t HP = (size_t)a.H * kP, GN = (size_t)a.G * kN;
     const TIn *xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)s.b * a.Lcap * HP + (size_t)s.h * kP;
@@ -462,28 +608,144 @@ __device__ __forceinline__ float commit_prologue(const ReplayParams &a, const Sl
     float dl = 0.f;
     if (s.lane < K) {
         dl = io<TIn>::load1(db + (size_t)s.lane * a.H);
-        sm.l[s.wave][s.lane] = Ah * dl;
+        sl[s.wave][s.lane] = Ah * dl;
     }
     __syncthreads();
     float tot = 0.f;
-    for (int i = 0; i < K; ++i) tot += sm.l[s.wave][i];
+    for (int i = 0; i < K; ++i) tot += sl[s.wave][i];
     if (s.lane < KMAX) {
         float wj = 0.f;
         if (s.lane < K) {
             float suf = 0.f;
-            for (int i = s.lane + 1; i < K; ++i) suf += sm.l[s.wave][i];
+            for (int i = s.lane + 1; i < K; ++i) suf += sl[s.wave][i];
             wj = dl * expf(suf);
         }
-        sm.w[s.wave][s.lane] = wj;
+        sw[s.wave][s.lane] = wj;
     }
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-        const float cf = sm.w[s.wave][j] * xv[j];
-        sm.cs[s.wave][cs_index<KMAX>(s.hf, s.c & 3, j, s.c >> 2)] = (j < K) ? cf : 0.f;
+        const float cf = sw[s.wave][j] * xv[j];
+        scs[s.wave][cs_index<KMAX>(s.hf, s.c & 3, j, s.c >> 2)] = (j < K) ? cf : 0.f;
     }
     __syncthreads();
     return expf(tot);
+}
+
+
+// As commit_chunk, with the group's B entries staged in LDS (sB, zero past
+// K) and the entry loop cut at Kr = K rounded up to 4, so a short fold does
+// not pay for KMAX entries.  `col` = 4c, laundered per chunk by the caller's
+// asm so the B_j reads are redone per chunk instead of held in registers.
+template <int KMAX>
+__device__ __forceinline__ void commit_chunk_lds(float4 (&st)[kPerChunk], int c, float lam, const float *cs,
+                                                 const float (*sB)[kN], int hf, int Kr, float *dst) {
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m) {
+        st[m].x *= lam; st[m].y *= lam; st[m].z *= lam; st[m].w *= lam;
+    }
+    int col = 4 * (threadIdx.x & 31);
+    asm volatile("" : "+v"(col));
+    for (int j0 = 0; j0 < Kr; j0 += 4) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int j = j0 + jj;
+            const float4 b = *reinterpret_cast<const float4 *>(&sB[j][col]);
+            const float *cp = cs + cs_index<KMAX>(hf, c, j, 0);
+            const float4 c0 = *reinterpret_cast<const float4 *>(cp);
+            const float4 c1 = *reinterpret_cast<const float4 *>(cp + 4);
+            const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int m = 0; m < kPerChunk; ++m) {
+                st[m].x += cf[m] * b.x;
+                st[m].y += cf[m] * b.y;
+                st[m].z += cf[m] * b.z;
+                st[m].w += cf[m] * b.w;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m)
+        stream_store4(dst + (size_t)chunk_index(c, m) * 2 * kN, st[m]);
+}
+
+// Partial sums of row pairs of one chunk against T vectors, reduce-scattered
+// so that lane (c, hf) ends with its share of row 2c+hf (see chunk_combine4).
+template <int T>
+__device__ __forceinline__ void chunk_dots(const float4 (&cur)[kPerChunk], const float4 (&C4)[T], int lane,
+                                           float (&r)[T][kChunks], int c) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        float v[kPerChunk];
+#pragma unroll
+        for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4[t]);
+        r[t][c] = chunk_reduce8(v, lane);
+    }
+}
+
+// ------------------------------------------------------------------------
+// Deferred fold.  replayssm_accept_deferred only advances pos, so a slot can
+// hold K = pos >= L accepted entries; the next verify on the slot folds them
+// into the checkpoint in the pass that streams it anyway (each chunk:
+// S_new = Lambda_K S0 + sum_j w_j x_j (x) B_j, stored, then the dots of the
+// drafts against S_new), and the drafts become entries 0..T-1 of the next
+// interval.  Same per-element arithmetic as a commit followed by a verify
+// at pos 0, so results are bit-identical to the eager accept.
+// ------------------------------------------------------------------------
+template <int KMAX, int T>
+struct FoldSmem {
+    float cs[kMaxHpw][kP * KMAX];   // commit coefficients (cs_index layout)
+    float B[KMAX][kN];              // the group's B entries, zero past K
+    union {
+        struct {
+            float l[kMaxHpw][KMAX];
+            float w[kMaxHpw][KMAX];
+        } c;                        // commit prologue scratch, dead once cs is built
+        VerifySmem<KMAX, T> v;      // replay coefficients of the T new tokens
+    } u;
+};
+
+// Commit coefficients of the K buffered entries, then the replay
+// coefficients and buffer part of the outputs of T tokens at positions
+// 0..T-1 (token inputs as laid out for verify).  Returns Lambda_K.
+template <typename TIn, int KMAX, int T>
+__device__ __forceinline__ float fold_prologue(const ReplayParams &a, const Slot &s, int K, const VerifyIn &in,
+                                               FoldSmem<KMAX, T> &sm, float (&ybuf)[T]) {
+    stage_B<TIn, KMAX>(sm.B, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.bb), in.GN, K, K);
+    typename io<TIn>::raw4 unused[KMAX];
+    const float lam = commit_prologue<TIn, KMAX, false>(a, s, K, sm.u.c.l, sm.u.c.w, sm.cs, unused);
+    VerifyIn v = in;
+    v.k = 0;
+    v.KL = T;
+    verify_prologue<TIn, KMAX, T>(a, s, v, s.prow, sm.u.v, ybuf);
+    return lam;
+}
+
+// End of a fold: the last-arriving workgroup of slot b publishes the commit
+// (pos = new_pos, intv + 1) and only then writes the B entries 0..T-1 of all
+// the slot's groups.  Every workgroup of the slot reads B entries 0..K-1 of
+// its group for the fold; a workgroup writing entry 0 earlier would race
+// with the others' reads, while the last arrival knows they are all done.
+// Bin: the slot's [T,G,N] input B (contiguous, as are entries 0..T-1).
+template <typename TIn>
+__device__ __forceinline__ void publish_fold(const ReplayParams &a, int b, int new_pos, const TIn *Bin, int T) {
+    __shared__ int last;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = atomicAdd(&a.work[b], 1);
+        last = old == a.wg_per_slot - 1;
+        if (last) {
+            a.work[b] = 0;
+            a.pos[b] = new_pos;
+            a.intv[b] += 1;
+        }
+    }
+    __syncthreads();
+    if (last) {
+        const size_t GN = (size_t)a.G * kN;
+        TIn *dst = reinterpret_cast<TIn *>(a.bbuf) + (size_t)b * a.Lcap * GN;
+        for (size_t i = threadIdx.x; i < (size_t)T * GN; i += blockDim.x) io<TIn>::copy1(dst + i, Bin + i);
+    }
 }
 
 }  // namespace

@@ -42,7 +42,7 @@ __global__ void __launch_bounds__(256) replay_step_kernel(ReplayParams a) {
 #pragma unroll
     for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
 
-    const StepIn in = step_inputs<TIn>(a, s);
+    const StepIn in = step_inputs<TIn>(a, s, a.kmax);
     const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
     float lam, ybuf;
     typename io<TIn>::raw4 Bj[KMAX];
@@ -96,7 +96,7 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
     float4 cur[kPerChunk];
     load_chunk(cur, sp, q);
 
-    const StepIn in = step_inputs<TIn>(a, s);
+    const StepIn in = step_inputs<TIn>(a, s, a.kmax);
     const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
     float lam, ybuf;
     typename io<TIn>::raw4 Bj[KMAX];
@@ -124,41 +124,84 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
 // ------------------------------------------------------------------------
 template <typename TIn, int KMAX, int T>
 __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
-    __shared__ VerifySmem<KMAX, T> sm;
+    __shared__ VerifySmemF<KMAX, T> sm;
 
     const Slot s = slot_of(a);
+    const VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
+    if (in.k >= a.L) return;   // deferred fold: replay_fold_verify_kernel, launched next
     float *sp = state_ptr(a.ckpt, s, a.H);
-    float4 buf[kNB][kPerChunk];
-#pragma unroll
-    for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
 
-    const VerifyIn in = verify_inputs<TIn, T>(a, s);
+    // prologue loads first (they retire before the checkpoint chunks)
+    VerifyPre<TIn, KMAX, T> pre;
+    verify_preload<TIn, KMAX, T>(a, s, in, s.prow, pre);
     float4 C4[T];
 #pragma unroll
     for (int t = 0; t < T; ++t)
         C4[t] = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN + 4 * s.c);
-    float ybuf[T];
-    verify_prologue<TIn, KMAX, T>(a, s, in, s.prow, sm, ybuf);
+    __builtin_amdgcn_sched_barrier(0);
+    float4 buf[kNB][kPerChunk];
+#pragma unroll
+    for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
+    __builtin_amdgcn_sched_barrier(0);
+
+    float ybuf[T], lam[T];
+    verify_finish<TIn, KMAX, T>(a, s, in, pre, sm, ybuf, lam);
 
     float r[T][kChunks];
 #pragma unroll
     for (int c = 0; c < kChunks; ++c) {
         float4 (&cur)[kPerChunk] = buf[c % kNB];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            float v[kPerChunk];
-#pragma unroll
-            for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4[t]);
-            r[t][c] = chunk_reduce8(v, s.lane);
-        }
+        chunk_dots<T>(cur, C4, s.lane, r, c);
         if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const float y0 = chunk_combine4(r[t], s.lane);
-        a.y[((size_t)s.b * T + t) * in.HP + (size_t)s.h * kP + s.prow] = sm.lam[s.wave][t] * y0 + ybuf[t];
+        a.y[((size_t)s.b * T + t) * in.HP + (size_t)s.h * kP + s.prow] = lam[t] * y0 + ybuf[t];
     }
     verify_append<TIn, T>(a, s, in);
+}
+
+// Verify on the slots a deferred accept left at pos >= L (the others were
+// done by replay_verify_kernel): fold the pos entries into the checkpoint
+// while streaming it, then the drafts are entries 0..T-1 of the next
+// interval (their outputs from the folded rows).  A commit: pos = 0, intv+1.
+// Launched only for layers that declare deferred commits.
+template <typename TIn, int KMAX, int T>
+__global__ void __launch_bounds__(256) replay_fold_verify_kernel(ReplayParams a) {
+    __shared__ FoldSmem<KMAX, T> sm;
+
+    const Slot s = slot_of(a);
+    VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
+    if (in.k < a.L) return;
+    float *sp = state_ptr(a.ckpt, s, a.H);
+    float4 buf[kNB][kPerChunk];
+#pragma unroll
+    for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
+
+    float4 C4[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        C4[t] = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN + 4 * s.c);
+    float ybuf[T];
+    const float lam = fold_prologue<TIn, KMAX, T>(a, s, in.k, in, sm, ybuf);
+    const int Kr = (in.k + 3) & ~3;
+    float r[T][kChunks];
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+        float4 (&cur)[kPerChunk] = buf[c % kNB];
+        commit_chunk_lds<KMAX>(cur, c, lam, sm.cs[s.wave], sm.B, s.hf, Kr, sp);
+        chunk_dots<T>(cur, C4, s.lane, r, c);
+        if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const float y0 = chunk_combine4(r[t], s.lane);
+        a.y[((size_t)s.b * T + t) * in.HP + (size_t)s.h * kP + s.prow] = sm.u.v.lam[s.wave][t] * y0 + ybuf[t];
+    }
+    in.k = 0;
+    verify_append<TIn, T, false>(a, s, in);
+    publish_fold<TIn>(a, s.b, 0, reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.b * T * in.GN, T);
 }
 
 // ------------------------------------------------------------------------
@@ -168,6 +211,7 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
 template <typename TIn, int KMAX, bool ACCEPT>
 __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
     __shared__ CommitSmem<KMAX> sm;
+    __shared__ float sB[KMAX][kN];
 
     const Slot s = slot_of(a);
     bool commit;
@@ -177,16 +221,39 @@ __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
         float4 buf[kNB][kPerChunk];
 #pragma unroll
         for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
-        typename io<TIn>::raw4 Bj[KMAX];
-        const float lam = commit_prologue<TIn, KMAX>(a, s, K, sm, Bj);
+        const size_t GN = (size_t)a.G * kN;
+        const TIn *bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * GN + (size_t)s.g * kN;
+        stage_B<TIn, KMAX>(sB, bb, bb, GN, K, K);
+        typename io<TIn>::raw4 unused[KMAX];
+        const float lam = commit_prologue<TIn, KMAX, false>(a, s, K, sm.l, sm.w, sm.cs, unused);
+        const int Kr = (K + 3) & ~3;
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) {
             float4 (&cur)[kPerChunk] = buf[c % kNB];
-            commit_chunk<TIn, KMAX>(cur, c, lam, sm.cs[s.wave], Bj, s.hf, sp);
+            commit_chunk_lds<KMAX>(cur, c, lam, sm.cs[s.wave], sB, s.hf, Kr, sp);
             if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
         }
     }
     publish_position(a, s.b, commit ? 0 : K, commit);
+}
+
+// Deferred accept: pos += n_keep only; a slot reaching L keeps its entries
+// until the next step, verify or flush on it folds them.
+__global__ void defer_accept_kernel(int32_t *pos, const int32_t *n_keep, int32_t *work, int batch, int L,
+                                    int T) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= batch) return;
+    int k = pos[b];
+    if (k < 0 || k > L - 1) {
+        atomicOr(&work[batch], kErrPos);
+        k = k < 0 ? 0 : L - 1;
+    }
+    int nk = n_keep[b];
+    if (nk < 0 || nk > T) {
+        atomicOr(&work[batch], kErrKeep);
+        nk = nk < 0 ? 0 : T;
+    }
+    pos[b] = k + nk;
 }
 
 __global__ void zero_pos_kernel(int32_t *pos, int n) {
@@ -209,7 +276,7 @@ hipError_t launch_replay_step(const ReplayParams &p0, bool in_bf16, hipStream_t 
         p.hpw = 1;
         p.wg_per_slot = p.H;
         dim3 grid(p.batch * p.H), block(256);
-        if (p.Lcap <= 16) {
+        if (p.kmax + 1 <= 16) {   // a step folds up to kmax + 1 entries
             if (in_bf16) hipLaunchKernelGGL((replay_step_rows_kernel<uint16_t, 16>), grid, block, 0, stream, p);
             else hipLaunchKernelGGL((replay_step_rows_kernel<float, 16>), grid, block, 0, stream, p);
         } else {
@@ -220,7 +287,7 @@ hipError_t launch_replay_step(const ReplayParams &p0, bool in_bf16, hipStream_t 
     }
     const ReplayParams &p = p0;
     dim3 grid(p.batch * p.wg_per_slot), block(64 * p.hpw);
-    if (p.Lcap <= 16) {
+    if (p.kmax + 1 <= 16) {   // a step folds up to kmax + 1 entries
         if (in_bf16) hipLaunchKernelGGL((replay_step_kernel<uint16_t, 16>), grid, block, 0, stream, p);
         else hipLaunchKernelGGL((replay_step_kernel<float, 16>), grid, block, 0, stream, p);
     } else {
@@ -233,8 +300,12 @@ hipError_t launch_replay_step(const ReplayParams &p0, bool in_bf16, hipStream_t 
 template <typename TIn, int KMAX>
 static void launch_verify_t(const ReplayParams &p, dim3 grid, dim3 block, hipStream_t stream) {
     switch (p.T) {
-#define RSSM_VERIFY_CASE(TT) \
-    case TT: hipLaunchKernelGGL((replay_verify_kernel<TIn, KMAX, TT>), grid, block, 0, stream, p); break;
+#define RSSM_VERIFY_CASE(TT)                                                                            \
+    case TT:                                                                                            \
+        hipLaunchKernelGGL((replay_verify_kernel<TIn, KMAX, TT>), grid, block, 0, stream, p);           \
+        if (p.kmax >= p.L)                                                                              \
+            hipLaunchKernelGGL((replay_fold_verify_kernel<TIn, KMAX, TT>), grid, block, 0, stream, p);      \
+        break;
         RSSM_VERIFY_CASE(1)
         RSSM_VERIFY_CASE(2)
         RSSM_VERIFY_CASE(3)
@@ -277,6 +348,13 @@ hipError_t launch_replay_commit(const ReplayParams &p, bool in_bf16, bool accept
         else RSSM_COMMIT(float, 32);
     }
 #undef RSSM_COMMIT
+    return hipGetLastError();
+}
+
+hipError_t launch_defer_accept(const ReplayParams &p, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    hipLaunchKernelGGL(defer_accept_kernel, dim3((p.batch + 255) / 256), dim3(256), 0, stream, p.pos, p.n_keep,
+                       p.work, p.batch, p.L, p.T);
     return hipGetLastError();
 }
 

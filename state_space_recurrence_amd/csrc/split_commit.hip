@@ -19,7 +19,7 @@ __global__ void __launch_bounds__(256) split_commit_kernel(ReplayParams a) {
         const TIn *bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * GN + (size_t)s.g * kN;
         stage_B<TIn, KMAX>(sB, bb, bb, GN, K, K);
         typename io<TIn>::raw4 unused[KMAX];
-        const float lam = commit_prologue<TIn, KMAX, false>(a, s, K, sm, unused);
+        const float lam = commit_prologue<TIn, KMAX, false>(a, s, K, sm.l, sm.w, sm.cs, unused);
         commit_head<KMAX, MODE>(a, s, lam, sm.cs[s.wave], sB, interval);
     }
     publish_position(a, s.b, commit ? 0 : K, commit);

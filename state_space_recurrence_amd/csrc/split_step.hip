@@ -29,7 +29,7 @@ __global__ void __launch_bounds__(256) split_step_kernel(ReplayParams a) {
             for (int m = 0; m < kPerChunk; ++m) raw[q][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q, m), s.c);
     }
 
-    const StepIn in = step_inputs<TIn>(a, s);
+    const StepIn in = step_inputs<TIn>(a, s, a.L - 1);
     const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;
     if (in.commit)
         stage_B<TIn, KMAX>(sB, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.Bin), in.GN, in.k,

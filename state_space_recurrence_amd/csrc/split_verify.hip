@@ -25,7 +25,7 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) raw[i] = load_row4<UB>(a, hrow + 2 * i, s.c);
     }
-    const VerifyIn in = verify_inputs<TIn, T>(a, s);
+    const VerifyIn in = verify_inputs<TIn, T>(a, s, a.L - 1);
     float ybuf[T];
     verify_prologue<TIn, KMAX, T>(a, s, in, prow, sm, ybuf);
 

@@ -46,7 +46,7 @@ def _desc(rs, **kw):
     return rs._make_desc(d["batch"], d["heads"], d["head_dim"], d["d_state"], d["groups"],
                          d["interval"], d["max_draft"], d["in_dtype"],
                          ckpt_dtype=d.get("ckpt_dtype", rs.F32), out_dtype=d.get("out_dtype", rs.NONE),
-                         shared_lowp=d.get("shared_lowp", 0))
+                         shared_lowp=d.get("shared_lowp", 0), deferred_commit=d.get("deferred_commit", 0))
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -62,6 +62,11 @@ def _desc(rs, **kw):
     ({"interval": 30, "max_draft": 4}, -3),
     ({"in_dtype": 2}, -2),
     ({"shared_lowp": 2}, -1),
+    ({"deferred_commit": 1, "max_draft": 5}, 0),
+    ({"deferred_commit": 2, "max_draft": 5}, -1),
+    ({"deferred_commit": 1, "max_draft": 1}, -2),
+    ({"deferred_commit": 1, "max_draft": 5, "ckpt_dtype": 1, "out_dtype": 3}, -2),
+    ({"deferred_commit": 1, "max_draft": 5, "interval": 28}, -3),
 ])
 def test_descriptor_validation(rs, kw, code):
     L = rs.lib()
@@ -91,7 +96,22 @@ def test_draft_count_checked(rs):
     assert L.replayssm_verify(ctypes.byref(d), ctypes.byref(st), 6, None, None, None, None, None, None) == -3
     assert L.replayssm_verify(ctypes.byref(d), ctypes.byref(st), 0, None, None, None, None, None, None) == -3
     assert L.replayssm_accept(ctypes.byref(d), ctypes.byref(st), None, 9, None) == -3
+    assert L.replayssm_accept_deferred(ctypes.byref(d), ctypes.byref(st), None, 6, None) == -3
     assert L.replayssm_recurrent_accept(ctypes.byref(d), None, None, 7, None) == -3
+
+
+def test_deferred_accept_needs_the_declaration(rs):
+    """replayssm_accept_deferred is refused on the host unless the descriptor
+    declares deferred commits (which is itself limited to F32 checkpoints
+    and speculative rounds, see test_descriptor_validation)."""
+    L = rs.lib()
+    st = rs.RssmState()
+    d = _desc(rs, max_draft=5)
+    assert L.replayssm_accept_deferred(ctypes.byref(d), ctypes.byref(st), None, 5, None) == -1
+    assert "deferred_commit" in L.replayssm_last_error().decode()
+    d = _desc(rs, max_draft=5, deferred_commit=1)
+    assert L.replayssm_accept_deferred(ctypes.byref(d), ctypes.byref(st), None, 5, None) == -1
+    assert "state" in L.replayssm_last_error().decode()
 
 
 def test_empty_batch_is_a_noop_without_device(rs):
