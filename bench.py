@@ -340,6 +340,17 @@ def main():
         extras["120b_batch256"] = r
         log(f"[bench] 120b: replay {r['replay_tokens_per_s']:.0f} tok/s, "
             f"recurrent {r['recurrent_tokens_per_s']:.0f} tok/s")
+        import dataclasses
+        sweep = {}
+        for Li in (4, 8, 16, 32, 64):
+            wl_i = dataclasses.replace(w, interval=Li)
+            r = run_standard(wl_i, args.batch, 128, Li, with_recurrent=False, per_launch=False)
+            sweep[str(Li)] = {k: r[k] for k in ("replay_tokens_per_s", "replay_ms_per_step",
+                                                "replay_bytes_per_token_layer", "replay_GBps_stack")}
+        extras["interval_sweep_4b_batch256"] = sweep
+        log("[bench] interval sweep (4b, batch 256): " + ", ".join(
+            f"L={k}: {v['replay_tokens_per_s']:.0f} tok/s ({v['replay_bytes_per_token_layer'] / 1e6:.3f} MB/token/layer)"
+            for k, v in sweep.items()))
         extras["spec_batch512"] = run_spec(rs, L, torch, synth, dev, stream, sh, log)
         extras["split_batch256"] = run_split(rs, L, torch, synth, dev, stream, sh, log)
 

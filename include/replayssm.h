@@ -55,7 +55,9 @@
  *   low nibble);  out_scale [B, H, P, N/32] uint8 (E4M3 scale per 32 elements)
  *
  * Supported: P = 64, N = 128; in_dtype F32 or BF16; H % G == 0;
- * 1 <= L, 1 <= Tmax <= 8, Lcap <= 32.
+ * 1 <= L, 1 <= Tmax <= 8; Lcap <= 64 for step / accept / flush on F32
+ * checkpoints; Lcap <= 32 for verify, deferred commits and the
+ * low-precision formats (RSSM_E_CAPACITY otherwise).
  *
  * State formats (rssm_desc ckpt_dtype / out_dtype / shared_lowp):
  *   F32  / NONE / 0 : fp32 checkpoint (outputs and updates).

@@ -27,7 +27,8 @@ int hip_status(hipError_t e, const char *what) {
     return fail(RSSM_E_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
-constexpr int kMaxLcap = 32;
+constexpr int kMaxLcap = 64;       // step / accept / flush on F32 checkpoints
+constexpr int kMaxLcapVerify = 32; // verify, deferred commits and the low-precision formats
 constexpr int kMaxDraft = 8;
 
 int lcap_of(const rssm_desc *d) { return d->interval + d->max_draft - 1; }
@@ -88,12 +89,15 @@ int check_desc(const rssm_desc *d) {
             return fail(RSSM_E_UNSUPPORTED, "deferred_commit: F32 checkpoints only");
         if (d->max_draft < 2)
             return fail(RSSM_E_UNSUPPORTED, "deferred_commit: needs max_draft >= 2 (speculative rounds)");
-        if (lcap_of(d) + 1 > kMaxLcap)
+        if (lcap_of(d) + 1 > kMaxLcapVerify)
             return fail(RSSM_E_CAPACITY, "deferred_commit: interval + max_draft = %d exceeds %d",
-                        d->interval + d->max_draft, kMaxLcap);
+                        d->interval + d->max_draft, kMaxLcapVerify);
     }
     if ((int64_t)d->batch * d->n_heads > (int64_t)1 << 24)
         return fail(RSSM_E_ARG, "batch * n_heads too large");
+    if (split_mode(d) >= 0 && lcap_of(d) > kMaxLcapVerify)
+        return fail(RSSM_E_CAPACITY, "low-precision state: interval + max_draft - 1 = %d exceeds %d",
+                    lcap_of(d), kMaxLcapVerify);
     if (split_mode(d) >= 0 && (int64_t)d->batch * d->n_heads * d->head_dim * d->d_state > 0xFFFFFFFFll)
         return fail(RSSM_E_ARG, "low-precision state: B*H*P*N must fit the 32-bit element index of the "
                                 "rounding stream");
@@ -184,6 +188,9 @@ int replayssm_verify(const rssm_desc *desc, const rssm_state *st, int32_t T, con
     RSSM_TRY(check_desc(desc));
     if (T < 1 || T > desc->max_draft)
         return fail(RSSM_E_CAPACITY, "verify: T = %d outside 1..max_draft (%d)", T, desc->max_draft);
+    if (lcap_of(desc) > kMaxLcapVerify)
+        return fail(RSSM_E_CAPACITY, "verify: interval + max_draft - 1 = %d exceeds %d", lcap_of(desc),
+                    kMaxLcapVerify);
     RSSM_TRY(check_state(desc, st));
     if (desc->batch == 0) return RSSM_OK;
     if (!x || !B || !C || !dt || !y) return fail(RSSM_E_ARG, "verify: an input/output pointer is NULL");

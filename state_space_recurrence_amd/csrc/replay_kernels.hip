@@ -31,9 +31,15 @@ namespace {
 // ------------------------------------------------------------------------
 // Standard decode step with fused interval commit.
 // ------------------------------------------------------------------------
+// Long intervals (KMAX > 16): the commit step stages the group's B entries in
+// LDS instead of holding KMAX slices per lane in registers.
+template <int KMAX>
+constexpr bool kBInLds = KMAX > 16;
+
 template <typename TIn, int KMAX>
 __global__ void __launch_bounds__(256) replay_step_kernel(ReplayParams a) {
     __shared__ StepSmem<KMAX> sm;
+    __shared__ float sB[kBInLds<KMAX> ? KMAX : 1][kN];
 
     const Slot s = slot_of(a);
     float *sp = state_ptr(a.ckpt, s, a.H);
@@ -46,7 +52,10 @@ __global__ void __launch_bounds__(256) replay_step_kernel(ReplayParams a) {
     const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
     float lam, ybuf;
     typename io<TIn>::raw4 Bj[KMAX];
-    step_prologue<TIn, KMAX>(a, s, in, s.prow, sm, &lam, &ybuf, Bj);
+    if (kBInLds<KMAX> && in.commit)   // visible after the prologue's barriers
+        stage_B<TIn, KMAX>(sB, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.Bin), in.GN, in.k,
+                           in.K);
+    step_prologue<TIn, KMAX, !kBInLds<KMAX>>(a, s, in, s.prow, sm, &lam, &ybuf, Bj);
 
     float r[kChunks];
 #pragma unroll
@@ -56,7 +65,12 @@ __global__ void __launch_bounds__(256) replay_step_kernel(ReplayParams a) {
 #pragma unroll
         for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4);
         r[c] = chunk_reduce8(v, s.lane);
-        if (in.commit) commit_chunk<TIn, KMAX>(cur, c, lam, sm.cs[s.wave], Bj, s.hf, sp);
+        if (in.commit) {
+            if constexpr (kBInLds<KMAX>)
+                commit_chunk_lds<KMAX>(cur, c, lam, sm.cs[s.wave], sB, s.hf, (in.K + 3) & ~3, sp);
+            else
+                commit_chunk<TIn, KMAX>(cur, c, lam, sm.cs[s.wave], Bj, s.hf, sp);
+        }
         if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
     }
     const float y0 = chunk_combine4(r, s.lane);
@@ -76,6 +90,7 @@ template <typename TIn, int KMAX>
 __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
     __shared__ StepSmem<KMAX> sm;
     __shared__ float s_r[kChunks][kWave];
+    __shared__ float sB[kBInLds<KMAX> ? KMAX : 1][kN];
 
     Slot s;
     {
@@ -100,13 +115,21 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
     const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
     float lam, ybuf;
     typename io<TIn>::raw4 Bj[KMAX];
-    step_prologue<TIn, KMAX>(a, s, in, s.prow, sm, &lam, &ybuf, Bj);
+    if (kBInLds<KMAX> && in.commit)
+        stage_B<TIn, KMAX>(sB, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.Bin), in.GN, in.k,
+                           in.K);
+    step_prologue<TIn, KMAX, !kBInLds<KMAX>>(a, s, in, s.prow, sm, &lam, &ybuf, Bj);
 
     float v[kPerChunk];
 #pragma unroll
     for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4);
     s_r[q][s.lane] = chunk_reduce8(v, s.lane);
-    if (in.commit) commit_chunk<TIn, KMAX>(cur, q, lam, sm.cs[s.wave], Bj, s.hf, sp);
+    if (in.commit) {
+        if constexpr (kBInLds<KMAX>)
+            commit_chunk_lds<KMAX>(cur, q, lam, sm.cs[s.wave], sB, s.hf, (in.K + 3) & ~3, sp);
+        else
+            commit_chunk<TIn, KMAX>(cur, q, lam, sm.cs[s.wave], Bj, s.hf, sp);
+    }
     __syncthreads();
     if (q == 0) {
         float r[kChunks];
@@ -269,31 +292,34 @@ __global__ void zero_pos_kernel(int32_t *pos, int n) {
 // per-head row split is used instead.
 constexpr int kRowSplitBelow = 512;
 
+// Buffer entries a kernel instance handles: 16, 32 or 64.
+#define RSSM_KMAX_DISPATCH(N, CALL)                  \
+    do {                                             \
+        if ((N) <= 16) { constexpr int KM_ = 16; CALL; } \
+        else if ((N) <= 32) { constexpr int KM_ = 32; CALL; } \
+        else { constexpr int KM_ = 64; CALL; }       \
+    } while (0)
+
 hipError_t launch_replay_step(const ReplayParams &p0, bool in_bf16, hipStream_t stream) {
     if (p0.batch == 0) return hipSuccess;
+    const int kneed = p0.kmax + 1;   // a step folds up to kmax + 1 entries
     if (p0.batch * p0.wg_per_slot < kRowSplitBelow) {
         ReplayParams p = p0;
         p.hpw = 1;
         p.wg_per_slot = p.H;
         dim3 grid(p.batch * p.H), block(256);
-        if (p.kmax + 1 <= 16) {   // a step folds up to kmax + 1 entries
-            if (in_bf16) hipLaunchKernelGGL((replay_step_rows_kernel<uint16_t, 16>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((replay_step_rows_kernel<float, 16>), grid, block, 0, stream, p);
-        } else {
-            if (in_bf16) hipLaunchKernelGGL((replay_step_rows_kernel<uint16_t, 32>), grid, block, 0, stream, p);
-            else hipLaunchKernelGGL((replay_step_rows_kernel<float, 32>), grid, block, 0, stream, p);
-        }
+        RSSM_KMAX_DISPATCH(kneed, {
+            if (in_bf16) hipLaunchKernelGGL((replay_step_rows_kernel<uint16_t, KM_>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((replay_step_rows_kernel<float, KM_>), grid, block, 0, stream, p);
+        });
         return hipGetLastError();
     }
     const ReplayParams &p = p0;
     dim3 grid(p.batch * p.wg_per_slot), block(64 * p.hpw);
-    if (p.kmax + 1 <= 16) {   // a step folds up to kmax + 1 entries
-        if (in_bf16) hipLaunchKernelGGL((replay_step_kernel<uint16_t, 16>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((replay_step_kernel<float, 16>), grid, block, 0, stream, p);
-    } else {
-        if (in_bf16) hipLaunchKernelGGL((replay_step_kernel<uint16_t, 32>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((replay_step_kernel<float, 32>), grid, block, 0, stream, p);
-    }
+    RSSM_KMAX_DISPATCH(kneed, {
+        if (in_bf16) hipLaunchKernelGGL((replay_step_kernel<uint16_t, KM_>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((replay_step_kernel<float, KM_>), grid, block, 0, stream, p);
+    });
     return hipGetLastError();
 }
 
@@ -335,19 +361,15 @@ hipError_t launch_replay_verify(const ReplayParams &p, bool in_bf16, hipStream_t
 hipError_t launch_replay_commit(const ReplayParams &p, bool in_bf16, bool accept, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
     dim3 grid(p.batch * p.wg_per_slot), block(64 * p.hpw);
-#define RSSM_COMMIT(TIn, KM)                                                                          \
-    do {                                                                                           \
-        if (accept) hipLaunchKernelGGL((replay_commit_kernel<TIn, KM, true>), grid, block, 0, stream, p); \
-        else hipLaunchKernelGGL((replay_commit_kernel<TIn, KM, false>), grid, block, 0, stream, p);      \
-    } while (0)
-    if (p.Lcap <= 16) {
-        if (in_bf16) RSSM_COMMIT(uint16_t, 16);
-        else RSSM_COMMIT(float, 16);
-    } else {
-        if (in_bf16) RSSM_COMMIT(uint16_t, 32);
-        else RSSM_COMMIT(float, 32);
-    }
-#undef RSSM_COMMIT
+    RSSM_KMAX_DISPATCH(p.Lcap, {
+        if (in_bf16) {
+            if (accept) hipLaunchKernelGGL((replay_commit_kernel<uint16_t, KM_, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((replay_commit_kernel<uint16_t, KM_, false>), grid, block, 0, stream, p);
+        } else {
+            if (accept) hipLaunchKernelGGL((replay_commit_kernel<float, KM_, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((replay_commit_kernel<float, KM_, false>), grid, block, 0, stream, p);
+        }
+    });
     return hipGetLastError();
 }
 

@@ -59,7 +59,10 @@ def _desc(rs, **kw):
     ({"interval": 0}, -1),
     ({"max_draft": 0}, -3),
     ({"max_draft": 9}, -3),
-    ({"interval": 30, "max_draft": 4}, -3),
+    ({"interval": 30, "max_draft": 4}, 0),       # Lcap 33: step / flush only
+    ({"interval": 64, "max_draft": 1}, 0),
+    ({"interval": 62, "max_draft": 4}, -3),      # Lcap 65
+    ({"interval": 30, "max_draft": 4, "ckpt_dtype": 1, "out_dtype": 3}, -3),
     ({"in_dtype": 2}, -2),
     ({"shared_lowp": 2}, -1),
     ({"deferred_commit": 1, "max_draft": 5}, 0),
@@ -95,6 +98,8 @@ def test_draft_count_checked(rs):
     st = rs.RssmState()
     assert L.replayssm_verify(ctypes.byref(d), ctypes.byref(st), 6, None, None, None, None, None, None) == -3
     assert L.replayssm_verify(ctypes.byref(d), ctypes.byref(st), 0, None, None, None, None, None, None) == -3
+    d = _desc(rs, interval=30, max_draft=4)      # verify is built for Lcap <= 32
+    assert L.replayssm_verify(ctypes.byref(d), ctypes.byref(st), 2, None, None, None, None, None, None) == -3
     assert L.replayssm_accept(ctypes.byref(d), ctypes.byref(st), None, 9, None) == -3
     assert L.replayssm_accept_deferred(ctypes.byref(d), ctypes.byref(st), None, 6, None) == -3
     assert L.replayssm_recurrent_accept(ctypes.byref(d), None, None, 7, None) == -3
