@@ -352,6 +352,7 @@ def main():
             f"L={k}: {v['replay_tokens_per_s']:.0f} tok/s ({v['replay_bytes_per_token_layer'] / 1e6:.3f} MB/token/layer)"
             for k, v in sweep.items()))
         extras["spec_batch512"] = run_spec(rs, L, torch, synth, dev, stream, sh, log)
+        extras["prefill_4b"] = run_prefill(rs, L, torch, synth, dev, stream, sh, log)
         extras["split_batch256"] = run_split(rs, L, torch, synth, dev, stream, sh, log)
 
     cpu = None
@@ -476,6 +477,76 @@ def run_spec(rs, L, torch, synth, dev, stream, sh, log, rounds=64, warm=8):
         f"{out['deferred_kept_tokens_per_s']:.0f}), recurrent {out['recurrent_kept_tokens_per_s']:.0f} "
         f"({out['replay_speedup_vs_recurrent']:.2f}x / {out['deferred_speedup_vs_recurrent']:.2f}x)")
     del pools, layers
+    torch.cuda.empty_cache()
+    return out
+
+
+# fp32 FMA throughput of the vector ALUs without packed-fp32 instructions
+# (256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz); the kernels are built
+# without v_pk_*_f32, whose 2x is therefore out of reach.
+VALU_FP32_TFLOPS = 78.6
+
+
+def run_prefill(rs, L, torch, synth, dev, stream, sh, log, batch=256, Tp=256, reps=3):
+    """Prompt prefill on the 4B-class layer shape (one layer): prompt tokens/s
+    of replayssm_prefill (outputs of every prompt token + final checkpoint)
+    against decoding the same prompt token by token with the replay step and
+    with the recurrent step.  Algorithmic flops per token and head: the
+    replayed outputs 2PN (S . C_t) and the state update 2PN."""
+    w = synth.WORKLOADS["4b"]
+    A, D = synth.layer_params(w, 0, device=dev)
+    S0 = synth.init_state(w, 0, device=dev, batch=batch)
+    x, Bm, Cm, dt = synth.token_inputs(w, 0, Tp, device=dev, batch=batch)
+    bt = lambda t: t.transpose(0, 1).contiguous()
+    px, pB, pC, pdt = bt(x), bt(Bm), bt(Cm), bt(dt)
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=16, in_dtype=x.dtype, device=dev)
+    y = torch.empty(batch, Tp, w.heads, 64, device=dev)
+
+    def t_of(fn, n):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / n
+
+    pf = lambda: rs.prefill(ls, px, pB, pC, pdt, from_zero=True, y=y)
+    pf()
+    sec = t_of(pf, reps)
+    pso = lambda: rs.prefill(ls, px, pB, None, pdt, from_zero=True, outputs=False)
+    pso()
+    sec_state = t_of(pso, reps)
+    yd = torch.empty(batch, w.heads, 64, device=dev)
+
+    def decode():
+        rs.load_checkpoint(ls, S0)
+        for t in range(Tp):
+            rs.step(ls, x[t], Bm[t], Cm[t], dt[t], y=yd)
+    decode()
+    sec_dec = t_of(decode, 1)
+    st = S0.clone()
+
+    def rec():
+        for t in range(Tp):
+            rs.recurrent_step(st, x[t], Bm[t], Cm[t], dt[t], ls.A, ls.D, groups=w.groups, y=yd)
+    rec()
+    sec_rec = t_of(rec, 1)
+    tok = batch * Tp
+    flops = tok * w.heads * 4.0 * 64 * 128
+    out = {"batch": batch, "prompt_tokens": Tp, "heads": w.heads, "groups": w.groups,
+           "prefill_ms": sec * 1e3, "prefill_tokens_per_s": tok / sec,
+           "prefill_state_only_ms": sec_state * 1e3,
+           "prefill_TFLOPs": flops / sec / 1e12, "valu_fp32_peak_TFLOPs": VALU_FP32_TFLOPS,
+           "prefill_frac_of_valu_peak": flops / sec / 1e12 / VALU_FP32_TFLOPS,
+           "decode_replay_ms": sec_dec * 1e3, "decode_recurrent_ms": sec_rec * 1e3,
+           "prefill_speedup_vs_replay_decode": sec_dec / sec,
+           "prefill_speedup_vs_recurrent_decode": sec_rec / sec}
+    log(f"[bench] prefill (4b layer, batch {batch}, {Tp} tokens): {tok / sec:.0f} tok/s, "
+        f"{out['prefill_TFLOPs']:.1f} TFLOP/s ({out['prefill_frac_of_valu_peak']:.2f} of fp32 VALU), "
+        f"{sec_dec / sec:.1f}x token-by-token replay, {sec_rec / sec:.1f}x recurrent")
+    del ls, x, Bm, Cm, dt, px, pB, pC, pdt, y
     torch.cuda.empty_cache()
     return out
 

@@ -211,6 +211,23 @@ int replayssm_accept_deferred(const rssm_desc *desc, const rssm_state *st,
 int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t stream);
 
 /*
+ * Prefill (the state a slot decodes from summarizes its prompt; article
+ * section 1): the Tp prompt tokens of every slot are run through the
+ * recurrence starting from the checkpoint (from_zero = 0; the buffer must be
+ * empty, pos == 0, flagged otherwise) or from a zero state (from_zero = 1).
+ * The state after the prompt becomes the checkpoint (pos = 0, intv + 1).
+ * When y is not NULL the outputs of all prompt tokens are written.  Each
+ * head's state stays on chip for the whole prompt, which is processed in
+ * 16-token chunks; results are bit-identical to decoding the prompt token
+ * by token with L = 16 and flushing at the end.  F32 checkpoints only.
+ * x [B,Tp,H,P], B, C [B,Tp,G,N], dt [B,Tp,H] (in_dtype); y [B,Tp,H,P] fp32
+ * or NULL (then C may be NULL).
+ */
+int replayssm_prefill(const rssm_desc *desc, const rssm_state *st, int32_t Tp,
+                      int32_t from_zero, const void *x, const void *B,
+                      const void *C, const void *dt, float *y, hipStream_t stream);
+
+/*
  * Load a checkpoint from an fp32 state src [B,H,P,N] (device): writes ckpt
  * (and the output copy when configured), rounding with stream index intv[b]
  * for the split formats, and sets pos = 0.  For F32 checkpoints it is a copy.

@@ -20,7 +20,7 @@ import torch
 
 __all__ = [
     "F32", "BF16", "FP8_E4M3", "FP4_E2M1", "NONE", "ReplaySSMError", "lib", "LayerState",
-    "step", "verify", "accept", "accept_deferred", "commit", "load_checkpoint", "recurrent_step",
+    "step", "verify", "accept", "accept_deferred", "commit", "prefill", "load_checkpoint", "recurrent_step",
     "recurrent_verify", "recurrent_accept", "buffer_capacity", "check_device_errors",
 ]
 
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
         L.replayssm_verify.argtypes = [_DP, _SP, i32, _vp, _vp, _vp, _vp, _vp, _vp]
         L.replayssm_accept.argtypes = [_DP, _SP, _vp, i32, _vp]
         L.replayssm_accept_deferred.argtypes = [_DP, _SP, _vp, i32, _vp]
+        L.replayssm_prefill.argtypes = [_DP, _SP, i32, i32, _vp, _vp, _vp, _vp, _vp, _vp]
         L.replayssm_commit.argtypes = [_DP, _SP, _vp]
         L.replayssm_load_checkpoint.argtypes = [_DP, _SP, _vp, _vp]
         L.replayssm_recurrent_step.argtypes = [_DP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
@@ -90,7 +91,7 @@ def lib() -> ctypes.CDLL:
         L.replayssm_hbm_probe.argtypes = [i32, _vp, _vp, ctypes.c_size_t, i32, _vp]
         L.replayssm_hbm_probe.restype = ctypes.c_int
         for name in ("replayssm_step", "replayssm_verify", "replayssm_accept", "replayssm_accept_deferred",
-                     "replayssm_commit",
+                     "replayssm_commit", "replayssm_prefill",
                      "replayssm_load_checkpoint", "replayssm_recurrent_step",
                      "replayssm_recurrent_verify", "replayssm_recurrent_accept",
                      "replayssm_check_desc", "replayssm_check_device_errors"):
@@ -270,6 +271,30 @@ def commit(ls: LayerState, stream=None) -> None:
     """Flush every slot's buffered tokens into its checkpoint (replayssm_commit)."""
     st = ls.cstate()
     _check(lib().replayssm_commit(ctypes.byref(ls._desc), ctypes.byref(st), _stream(stream)))
+
+
+def prefill(ls: LayerState, x: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None, dt: torch.Tensor, *,
+            from_zero: bool = False, outputs: bool = True, y: torch.Tensor | None = None,
+            stream=None) -> torch.Tensor | None:
+    """Run a prompt of Tp tokens per slot into the checkpoint (replayssm_prefill):
+    x [B,Tp,H,P], B/C [B,Tp,G,N], dt [B,Tp,H]; returns y [B,Tp,H,P] fp32 when
+    ``outputs`` (else None)."""
+    Tp = x.shape[1] if x.dim() == 4 else 0
+    _need(x, (ls.batch, Tp, ls.heads, ls.head_dim), ls.in_dtype, "x")
+    _need(B, (ls.batch, Tp, ls.groups, ls.d_state), ls.in_dtype, "B")
+    _need(dt, (ls.batch, Tp, ls.heads), ls.in_dtype, "dt")
+    if outputs:
+        _need(C, (ls.batch, Tp, ls.groups, ls.d_state), ls.in_dtype, "C")
+        if y is None:
+            y = torch.empty(ls.batch, Tp, ls.heads, ls.head_dim, dtype=torch.float32, device=x.device)
+        _need(y, (ls.batch, Tp, ls.heads, ls.head_dim), torch.float32, "y")
+    else:
+        y = None
+    st = ls.cstate()
+    _check(lib().replayssm_prefill(ctypes.byref(ls._desc), ctypes.byref(st), Tp, int(from_zero), _ptr(x),
+                                   _ptr(B), _ptr(C) if C is not None else None, _ptr(dt), _ptr(y),
+                                   _stream(stream)))
+    return y
 
 
 def load_checkpoint(ls: LayerState, src: torch.Tensor, stream=None) -> None:

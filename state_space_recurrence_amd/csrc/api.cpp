@@ -251,6 +251,29 @@ int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t st
     return hip_status(rssm::launch_replay_commit(p, bf, false, stream), "commit launch");
 }
 
+int replayssm_prefill(const rssm_desc *desc, const rssm_state *st, int32_t Tp, int32_t from_zero, const void *x,
+                      const void *B, const void *C, const void *dt, float *y, hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    if (split_mode(desc) >= 0) return fail(RSSM_E_UNSUPPORTED, "prefill: F32 checkpoints only");
+    if (Tp < 0) return fail(RSSM_E_ARG, "prefill: Tp = %d < 0", Tp);
+    if (from_zero != 0 && from_zero != 1) return fail(RSSM_E_ARG, "prefill: from_zero must be 0 or 1");
+    if ((int64_t)desc->batch * Tp * desc->n_heads > (int64_t)1 << 31)
+        return fail(RSSM_E_ARG, "prefill: batch * Tp * n_heads too large");
+    RSSM_TRY(check_state(desc, st));
+    if (desc->batch == 0 || Tp == 0) return RSSM_OK;
+    if (!x || !B || !dt) return fail(RSSM_E_ARG, "prefill: x / B / dt is NULL");
+    if (y && !C) return fail(RSSM_E_ARG, "prefill: outputs need C");
+    rssm::ReplayParams p = replay_params(desc, st);
+    p.x = x;
+    p.Bm = B;
+    p.Cm = C;
+    p.dt = dt;
+    p.y = y;
+    p.T = Tp;
+    p.from_zero = from_zero;
+    return hip_status(rssm::launch_prefill(p, desc->in_dtype == RSSM_BF16, y != nullptr, stream), "prefill launch");
+}
+
 int replayssm_load_checkpoint(const rssm_desc *desc, const rssm_state *st, const float *src,
                               hipStream_t stream) {
     RSSM_TRY(check_desc(desc));

@@ -25,6 +25,7 @@ struct ReplayParams {
     const int32_t *n_keep;  // [B] (accept)
     int batch, H, G, L, Lcap, T;
     int kmax;               // largest pos a step / verify accepts: L-1, or Lcap with deferred accepts
+    int from_zero;          // prefill: start from a zero state instead of the checkpoint
     int hpw;                // heads (waves) per workgroup
     int wg_per_slot;        // H / hpw
     // precision split (ignored by the fp32 kernels)
@@ -63,6 +64,7 @@ hipError_t launch_replay_verify(const ReplayParams &p, bool in_bf16, hipStream_t
 hipError_t launch_replay_commit(const ReplayParams &p, bool in_bf16, bool accept, hipStream_t s);
 hipError_t launch_zero_pos(int32_t *pos, int batch, hipStream_t s);
 hipError_t launch_defer_accept(const ReplayParams &p, hipStream_t s);
+hipError_t launch_prefill(const ReplayParams &p, bool in_bf16, bool outputs, hipStream_t s);   // p.T = prompt length
 hipError_t launch_split_step(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
 hipError_t launch_split_verify(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
 hipError_t launch_split_commit(const ReplayParams &p, bool in_bf16, int mode, bool accept, hipStream_t s);

@@ -119,6 +119,18 @@ def test_deferred_accept_needs_the_declaration(rs):
     assert "state" in L.replayssm_last_error().decode()
 
 
+def test_prefill_arguments_checked(rs):
+    L = rs.lib()
+    st = rs.RssmState()
+    d = _desc(rs)
+    assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), -1, 0, None, None, None, None, None, None) == -1
+    assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), 4, 2, None, None, None, None, None, None) == -1
+    d = _desc(rs, ckpt_dtype=rs.BF16, out_dtype=rs.FP4_E2M1)
+    assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), 4, 0, None, None, None, None, None, None) == -2
+    d = _desc(rs, batch=0)
+    assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), 4, 0, None, None, None, None, None, None) == 0
+
+
 def test_empty_batch_is_a_noop_without_device(rs):
     L = rs.lib()
     d = _desc(rs, batch=0)

@@ -1,0 +1,117 @@
+"""GPU parity of the prompt prefill (replayssm_prefill).
+
+The state a slot decodes from summarizes its prompt (article "NVIDIA
+ReplaySSM: hybrid model SSM decoding with a state buffer", section 1).  The
+prefill keeps each head's state on chip and processes the prompt in 16-token
+chunks with the replay arithmetic of the decode step, so its outputs and its
+final checkpoint are bit-identical to decoding the prompt token by token
+with L = 16 and flushing at the end; both match the fp64 oracle at 2e-5.
+"""
+import dataclasses
+
+import pytest
+import torch
+
+import oracle
+import synth
+from helpers import assert_close, need_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def rs():
+    need_gpu()
+    import state_space_recurrence_amd as rs
+    rs.lib()
+    return rs
+
+
+def _bt(t):
+    return t.transpose(0, 1).contiguous()
+
+
+def _case(rs, w, batch, Tp, layer=0, stream=21):
+    A, D = synth.layer_params(w, layer)
+    S0 = synth.init_state(w, layer, batch=batch)
+    x, Bm, Cm, dt = synth.token_inputs(w, layer, Tp, batch=batch, stream=stream)
+    return A, D, S0, x, Bm, Cm, dt
+
+
+def _layer(rs, w, batch, A, D, S0, dtype):
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=16, in_dtype=dtype)
+    rs.load_checkpoint(ls, S0.cuda())
+    return ls
+
+
+@pytest.mark.parametrize("wname,batch,Tp", [("tiny", 3, 37), ("tiny", 300, 20), ("4b", 4, 50),
+                                            ("tiny", 2, 5), ("tiny", 2, 16)])
+def test_prefill_equals_decode_and_oracle(rs, wname, batch, Tp):
+    w = synth.WORKLOADS[wname]
+    A, D, S0, x, Bm, Cm, dt = _case(rs, w, batch, Tp)
+    lp = _layer(rs, w, batch, A, D, S0, x.dtype)
+    yp = rs.prefill(lp, _bt(x).cuda(), _bt(Bm).cuda(), _bt(Cm).cuda(), _bt(dt).cuda())
+    rs.check_device_errors(lp)
+    assert lp.pos.cpu().tolist() == [0] * batch
+    assert lp.intv.cpu().tolist() == [1] * batch
+    # token-by-token decode with L = 16, then flush
+    ld = _layer(rs, w, batch, A, D, S0, x.dtype)
+    yd = torch.stack([rs.step(ld, x[t].cuda(), Bm[t].cuda(), Cm[t].cuda(), dt[t].cuda()) for t in range(Tp)], 1)
+    rs.commit(ld)
+    assert torch.equal(yp, yd), "prefill outputs differ from decode"
+    assert torch.equal(lp.ckpt, ld.ckpt), "prefill checkpoint differs from the flushed decode state"
+    sl = [0, batch - 1]
+    S_ref, y_ref = oracle.recurrent(S0[sl], x[:, sl], Bm[:, sl], Cm[:, sl], dt[:, sl], A, D, w.groups)
+    for t in range(Tp):
+        assert_close(yp[sl, t].cpu(), y_ref[t], f"prefill y token {t}")
+    assert_close(lp.ckpt[sl].cpu(), S_ref, "prefill state")
+
+
+def test_prefill_from_zero_and_state_only(rs):
+    """from_zero ignores the stored checkpoint; without outputs the state is
+    the same bit for bit."""
+    w = synth.WORKLOADS["tiny"]
+    batch, Tp = 4, 45
+    A, D, S0, x, Bm, Cm, dt = _case(rs, w, batch, Tp, layer=1, stream=22)
+    ins = (_bt(x).cuda(), _bt(Bm).cuda(), _bt(Cm).cuda(), _bt(dt).cuda())
+    la = _layer(rs, w, batch, A, D, S0, x.dtype)       # S0 stored, then ignored
+    ya = rs.prefill(la, *ins, from_zero=True)
+    lb = _layer(rs, w, batch, A, D, S0, x.dtype)
+    assert rs.prefill(lb, ins[0], ins[1], None, ins[3], from_zero=True, outputs=False) is None
+    assert torch.equal(la.ckpt, lb.ckpt)
+    S_ref, y_ref = oracle.recurrent(torch.zeros_like(S0), x, Bm, Cm, dt, A, D, w.groups)
+    for t in range(Tp):
+        assert_close(ya[:, t].cpu(), y_ref[t], f"y token {t} from zero")
+    assert_close(la.ckpt.cpu(), S_ref, "state from zero")
+
+
+def test_decode_continues_after_prefill(rs):
+    """A prompt prefilled into the checkpoint, then 20 decode steps: the
+    outputs follow the recurrence over prompt + generated tokens."""
+    w = synth.WORKLOADS["4b"]
+    batch, Tp, G = 3, 33, 20
+    A, D, S0, x, Bm, Cm, dt = _case(rs, w, batch, Tp + G, layer=2, stream=23)
+    ls = _layer(rs, w, batch, A, D, S0, x.dtype)
+    rs.prefill(ls, _bt(x[:Tp]).cuda(), _bt(Bm[:Tp]).cuda(), _bt(Cm[:Tp]).cuda(), _bt(dt[:Tp]).cuda(),
+               outputs=False)
+    ys = [rs.step(ls, x[t].cuda(), Bm[t].cuda(), Cm[t].cuda(), dt[t].cuda()).cpu() for t in range(Tp, Tp + G)]
+    _, y_ref = oracle.recurrent(S0, x, Bm, Cm, dt, A, D, w.groups)
+    for i, t in enumerate(range(Tp, Tp + G)):
+        assert_close(ys[i], y_ref[t], f"decode token {t} after prefill")
+
+
+def test_prefill_edge_cases(rs):
+    """Tp = 0 is a no-op; a prefill onto a slot with buffered tokens is
+    flagged (those tokens would be dropped)."""
+    w = synth.WORKLOADS["tiny"]
+    A, D, S0, x, Bm, Cm, dt = _case(rs, w, 2, 3, stream=24)
+    ls = _layer(rs, w, 2, A, D, S0, x.dtype)
+    before = ls.ckpt.clone()
+    e = lambda *shape: torch.empty(*shape, dtype=x.dtype, device="cuda")
+    rs.prefill(ls, e(2, 0, w.heads, 64), e(2, 0, w.groups, 128), e(2, 0, w.groups, 128), e(2, 0, w.heads))
+    torch.cuda.synchronize()
+    assert torch.equal(before, ls.ckpt) and ls.intv.cpu().tolist() == [0, 0]
+    rs.step(ls, x[0].cuda(), Bm[0].cuda(), Cm[0].cuda(), dt[0].cuda())
+    rs.prefill(ls, _bt(x).cuda(), _bt(Bm).cuda(), _bt(Cm).cuda(), _bt(dt).cuda())
+    with pytest.raises(rs.ReplaySSMError, match="device"):
+        rs.check_device_errors(ls)
