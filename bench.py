@@ -265,6 +265,43 @@ def main():
         torch.cuda.empty_cache()
         return out
 
+    def run_stagger(w, batch, steps=128):
+        """Lock-step phases (every slot commits on the same step) against
+        staggered phases (slots admitted one interval position apart, so
+        1/L of them commit on each step): tokens/s and the spread of the
+        per-step time over the stacked layers."""
+        out = {}
+        for mode in ("lockstep", "staggered"):
+            layers = make_layers(w, batch, steps + w.interval)
+            y = [torch.empty(batch, w.heads, 64, device=dev) for _ in layers]
+            if mode == "staggered":   # slot b joins at step b % L: pos ends at (L - b % L) % L
+                for i in range(w.interval):
+                    idx = torch.tensor([b for b in range(batch) if b % w.interval <= i], dtype=torch.int32,
+                                       device=dev)
+                    n = idx.numel()
+                    for li, lay in enumerate(layers):
+                        x, Bm, Cm, dt = lay["in"]
+                        rs.step(lay["ls"], x[i, :n], Bm[i, :n], Cm[i, :n], dt[i, :n], y=y[li][:n], slots=idx)
+            else:
+                replay_loop(layers, 0, w.interval, y)
+            ev = []
+            replay_loop(layers, w.interval, steps, y, ev)
+            torch.cuda.synchronize()
+            per_launch = [a.elapsed_time(b) * 1e3 for a, b in ev]
+            per_step = [sum(per_launch[i:i + w.layers]) for i in range(0, len(per_launch), w.layers)]
+            per_step.sort()
+            sec = timed(replay_loop, layers, w.interval, steps, y)
+            out[mode] = {"tokens_per_s": batch * steps / sec, "step_us_min": per_step[0],
+                         "step_us_median": per_step[len(per_step) // 2], "step_us_max": per_step[-1],
+                         "pos_distinct": int(layers[0]["ls"].pos.unique().numel())}
+            del layers
+            torch.cuda.empty_cache()
+        log(f"[bench] phases (4b, batch {batch}): lock-step {out['lockstep']['tokens_per_s']:.0f} tok/s, step "
+            f"{out['lockstep']['step_us_median']:.0f}/{out['lockstep']['step_us_max']:.0f} us median/max; "
+            f"staggered {out['staggered']['tokens_per_s']:.0f} tok/s, step "
+            f"{out['staggered']['step_us_median']:.0f}/{out['staggered']['step_us_max']:.0f} us")
+        return out
+
     if args.probe:
         layers = make_layers(w, args.batch, 32)
         y = [torch.empty(args.batch, w.heads, 64, device=dev) for _ in layers]
@@ -348,6 +385,7 @@ def main():
             sweep[str(Li)] = {k: r[k] for k in ("replay_tokens_per_s", "replay_ms_per_step",
                                                 "replay_bytes_per_token_layer", "replay_GBps_stack")}
         extras["interval_sweep_4b_batch256"] = sweep
+        extras["phases_4b_batch256"] = run_stagger(w, args.batch)
         log("[bench] interval sweep (4b, batch 256): " + ", ".join(
             f"L={k}: {v['replay_tokens_per_s']:.0f} tok/s ({v['replay_bytes_per_token_layer'] / 1e6:.3f} MB/token/layer)"
             for k, v in sweep.items()))

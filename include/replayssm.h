@@ -38,8 +38,9 @@
  *    detected on the host before anything is launched.  A failed launch
  *    returns RSSM_E_HIP.  The message of the last error of the calling thread
  *    is available from replayssm_last_error().
- *  - Device-side range errors (a position count out of range, n_keep > T)
- *    are clamped and recorded in a sticky flag read by
+ *  - Device-side range errors (a position count out of range, n_keep > T, a
+ *    row mapped to a slot outside 0..S-1) are clamped or skipped and
+ *    recorded in a sticky flag read by
  *    replayssm_check_device_errors().
  *
  * Shapes (B = batch, H = n_heads, P = head_dim, N = d_state, G = n_groups,
@@ -51,6 +52,8 @@
  *   ckpt [B, H, P, N] (ckpt_dtype)
  *   xbuf [B, Lcap, H, P]   bbuf [B, Lcap, G, N]   dtbuf [B, Lcap, H]   (in_dtype)
  *   pos, intv [B] int32;  work [B + 1] int32 (all zero before first use)
+ *   (B here is the slot count S = n_slots; call inputs and outputs have
+ *   `batch` rows, one per entry of slot_idx)
  *   out_q [B, H, P, N/2] uint8 (two FP4 codes per byte, even element in the
  *   low nibble);  out_scale [B, H, P, N/32] uint8 (E4M3 scale per 32 elements)
  *
@@ -124,6 +127,8 @@ typedef struct rssm_desc {
     uint64_t seed;        /* stochastic-rounding stream: key */
     int32_t deferred_commit; /* 1: replayssm_accept_deferred may be used on this layer (F32 checkpoint,
                                 max_draft >= 2, L + Tmax <= 32); verify then also runs the fold pass */
+    int32_t n_slots;      /* state slots S held by the rssm_state buffers; 0 means S = batch.  A call
+                             covers `batch` rows, mapped to slots by rssm_state.slot_idx */
 } rssm_desc;
 
 /* Device buffers of one layer (host struct of device pointers). */
@@ -141,6 +146,9 @@ typedef struct rssm_state {
     const float *A;       /* [H] decay rate, A < 0 */
     const float *D;       /* [H] skip weight */
     float *debug_prequant;/* optional [B,H,P,N] fp32: commit values before rounding (split path tests); NULL */
+    const int32_t *slot_idx; /* [batch] device: state slot of each call row, -1 = padding row (nothing
+                                read or written for it); NULL = row b uses slot b.  Slots of one call
+                                must be distinct.  Rows mapped outside 0..S-1 are skipped and flagged */
 } rssm_state;
 
 /*
@@ -274,10 +282,10 @@ const char *replayssm_status_string(int status);
 /* Message of the calling thread's last error ("" if none). */
 const char *replayssm_last_error(void);
 
-/* Synchronise `stream`, read and clear the sticky device error word of st:
- * RSSM_OK, RSSM_E_DEVICE (with the recorded condition in last_error) or
- * RSSM_E_HIP. */
-int replayssm_check_device_errors(const rssm_state *st, int32_t batch, hipStream_t stream);
+/* Synchronise `stream`, read and clear the sticky device error word of st
+ * (work[n_slots]; n_slots = the state's slot count S): RSSM_OK,
+ * RSSM_E_DEVICE (with the recorded condition in last_error) or RSSM_E_HIP. */
+int replayssm_check_device_errors(const rssm_state *st, int32_t n_slots, hipStream_t stream);
 
 /*
  * Diagnostic: stream `bytes` (a multiple of 16) through HBM with the same

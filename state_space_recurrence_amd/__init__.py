@@ -40,7 +40,7 @@ class RssmDesc(ctypes.Structure):
         ("d_state", ctypes.c_int32), ("n_groups", ctypes.c_int32), ("interval", ctypes.c_int32),
         ("max_draft", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("ckpt_dtype", ctypes.c_int32),
         ("out_dtype", ctypes.c_int32), ("shared_lowp", ctypes.c_int32), ("layer_id", ctypes.c_int32),
-        ("seed", ctypes.c_uint64), ("deferred_commit", ctypes.c_int32),
+        ("seed", ctypes.c_uint64), ("deferred_commit", ctypes.c_int32), ("n_slots", ctypes.c_int32),
     ]
 
 
@@ -50,6 +50,7 @@ class RssmState(ctypes.Structure):
         ("xbuf", ctypes.c_void_p), ("bbuf", ctypes.c_void_p), ("dtbuf", ctypes.c_void_p),
         ("pos", ctypes.c_void_p), ("intv", ctypes.c_void_p), ("work", ctypes.c_void_p),
         ("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("debug_prequant", ctypes.c_void_p),
+        ("slot_idx", ctypes.c_void_p),
     ]
 
 
@@ -217,94 +218,110 @@ def _need(t: torch.Tensor, shape, dtype, name):
                              f"device={t.device}")
 
 
-def _check_inputs(ls, x, B, C, dt, T=None):
-    lead = (ls.batch,) if T is None else (ls.batch, T)
+def _ctx(ls, slots):
+    """Descriptor, state struct and row count of one call: every slot of the
+    layer in order, or the rows of ``slots`` (int32 device tensor of slot
+    indices, -1 = padding row)."""
+    if slots is None:
+        return ls._desc, ls.cstate(), ls.batch
+    _need(slots, (slots.numel(),), torch.int32, "slots")
+    d = RssmDesc.from_buffer_copy(ls._desc)
+    d.batch = slots.numel()
+    d.n_slots = ls.batch
+    st = ls.cstate()
+    st.slot_idx = slots.data_ptr()
+    return d, st, d.batch
+
+
+def _check_inputs(ls, x, B, C, dt, T=None, rows=None):
+    rows = ls.batch if rows is None else rows
+    lead = (rows,) if T is None else (rows, T)
     _need(x, lead + (ls.heads, ls.head_dim), ls.in_dtype, "x")
     _need(B, lead + (ls.groups, ls.d_state), ls.in_dtype, "B")
     _need(C, lead + (ls.groups, ls.d_state), ls.in_dtype, "C")
     _need(dt, lead + (ls.heads,), ls.in_dtype, "dt")
 
 
-def step(ls: LayerState, x, B, C, dt, y=None, stream=None) -> torch.Tensor:
-    """One decode token per slot (replayssm_step): returns y [B,H,P] fp32."""
-    _check_inputs(ls, x, B, C, dt)
+def step(ls: LayerState, x, B, C, dt, y=None, stream=None, slots=None) -> torch.Tensor:
+    """One decode token per slot (replayssm_step): returns y [rows,H,P] fp32.
+    ``slots``: optional int32 device tensor mapping call rows to state slots."""
+    d, st, rows = _ctx(ls, slots)
+    _check_inputs(ls, x, B, C, dt, rows=rows)
     if y is None:
-        y = torch.empty(ls.batch, ls.heads, ls.head_dim, dtype=torch.float32, device=x.device)
-    st = ls.cstate()
-    _check(lib().replayssm_step(ctypes.byref(ls._desc), ctypes.byref(st), _ptr(x), _ptr(B), _ptr(C),
+        y = torch.empty(rows, ls.heads, ls.head_dim, dtype=torch.float32, device=x.device)
+    _check(lib().replayssm_step(ctypes.byref(d), ctypes.byref(st), _ptr(x), _ptr(B), _ptr(C),
                                 _ptr(dt), _ptr(y), _stream(stream)))
     return y
 
 
-def verify(ls: LayerState, x, B, C, dt, y=None, stream=None) -> torch.Tensor:
-    """Speculative verify of T positions (replayssm_verify): x [B,T,H,P] etc.;
-    returns y [B,T,H,P] fp32.  No state is written; pos is unchanged."""
+def verify(ls: LayerState, x, B, C, dt, y=None, stream=None, slots=None) -> torch.Tensor:
+    """Speculative verify of T positions (replayssm_verify): x [rows,T,H,P] etc.;
+    returns y [rows,T,H,P] fp32.  No state is written; pos is unchanged."""
+    d, st, rows = _ctx(ls, slots)
     T = x.shape[1]
-    _check_inputs(ls, x, B, C, dt, T)
+    _check_inputs(ls, x, B, C, dt, T, rows=rows)
     if y is None:
-        y = torch.empty(ls.batch, T, ls.heads, ls.head_dim, dtype=torch.float32, device=x.device)
-    st = ls.cstate()
-    _check(lib().replayssm_verify(ctypes.byref(ls._desc), ctypes.byref(st), T, _ptr(x), _ptr(B),
+        y = torch.empty(rows, T, ls.heads, ls.head_dim, dtype=torch.float32, device=x.device)
+    _check(lib().replayssm_verify(ctypes.byref(d), ctypes.byref(st), T, _ptr(x), _ptr(B),
                                   _ptr(C), _ptr(dt), _ptr(y), _stream(stream)))
     return y
 
 
-def accept(ls: LayerState, n_keep: torch.Tensor, T: int, stream=None) -> None:
-    """Keep the first n_keep[b] verified positions (replayssm_accept)."""
-    _need(n_keep, (ls.batch,), torch.int32, "n_keep")
-    st = ls.cstate()
-    _check(lib().replayssm_accept(ctypes.byref(ls._desc), ctypes.byref(st), _ptr(n_keep), T,
-                                  _stream(stream)))
+def accept(ls: LayerState, n_keep: torch.Tensor, T: int, stream=None, slots=None) -> None:
+    """Keep the first n_keep[row] verified positions (replayssm_accept)."""
+    d, st, rows = _ctx(ls, slots)
+    _need(n_keep, (rows,), torch.int32, "n_keep")
+    _check(lib().replayssm_accept(ctypes.byref(d), ctypes.byref(st), _ptr(n_keep), T, _stream(stream)))
 
 
-def accept_deferred(ls: LayerState, n_keep: torch.Tensor, T: int, stream=None) -> None:
-    """Keep the first n_keep[b] verified positions without committing: slots
+def accept_deferred(ls: LayerState, n_keep: torch.Tensor, T: int, stream=None, slots=None) -> None:
+    """Keep the first n_keep[row] verified positions without committing: slots
     reaching the interval length are folded by their next step / verify /
     commit (replayssm_accept_deferred; fp32 checkpoints)."""
-    _need(n_keep, (ls.batch,), torch.int32, "n_keep")
-    st = ls.cstate()
-    _check(lib().replayssm_accept_deferred(ctypes.byref(ls._desc), ctypes.byref(st), _ptr(n_keep), T,
+    d, st, rows = _ctx(ls, slots)
+    _need(n_keep, (rows,), torch.int32, "n_keep")
+    _check(lib().replayssm_accept_deferred(ctypes.byref(d), ctypes.byref(st), _ptr(n_keep), T,
                                            _stream(stream)))
 
 
-def commit(ls: LayerState, stream=None) -> None:
-    """Flush every slot's buffered tokens into its checkpoint (replayssm_commit)."""
-    st = ls.cstate()
-    _check(lib().replayssm_commit(ctypes.byref(ls._desc), ctypes.byref(st), _stream(stream)))
+def commit(ls: LayerState, stream=None, slots=None) -> None:
+    """Flush buffered tokens into the checkpoint (replayssm_commit): every
+    slot, or the slots listed in ``slots`` (eviction = flush + copy out)."""
+    d, st, _ = _ctx(ls, slots)
+    _check(lib().replayssm_commit(ctypes.byref(d), ctypes.byref(st), _stream(stream)))
 
 
 def prefill(ls: LayerState, x: torch.Tensor, B: torch.Tensor, C: torch.Tensor | None, dt: torch.Tensor, *,
             from_zero: bool = False, outputs: bool = True, y: torch.Tensor | None = None,
-            stream=None) -> torch.Tensor | None:
-    """Run a prompt of Tp tokens per slot into the checkpoint (replayssm_prefill):
-    x [B,Tp,H,P], B/C [B,Tp,G,N], dt [B,Tp,H]; returns y [B,Tp,H,P] fp32 when
-    ``outputs`` (else None)."""
+            stream=None, slots=None) -> torch.Tensor | None:
+    """Run a prompt of Tp tokens per row into the checkpoint (replayssm_prefill):
+    x [rows,Tp,H,P], B/C [rows,Tp,G,N], dt [rows,Tp,H]; returns y [rows,Tp,H,P]
+    fp32 when ``outputs`` (else None)."""
+    d, st, rows = _ctx(ls, slots)
     Tp = x.shape[1] if x.dim() == 4 else 0
-    _need(x, (ls.batch, Tp, ls.heads, ls.head_dim), ls.in_dtype, "x")
-    _need(B, (ls.batch, Tp, ls.groups, ls.d_state), ls.in_dtype, "B")
-    _need(dt, (ls.batch, Tp, ls.heads), ls.in_dtype, "dt")
+    _need(x, (rows, Tp, ls.heads, ls.head_dim), ls.in_dtype, "x")
+    _need(B, (rows, Tp, ls.groups, ls.d_state), ls.in_dtype, "B")
+    _need(dt, (rows, Tp, ls.heads), ls.in_dtype, "dt")
     if outputs:
-        _need(C, (ls.batch, Tp, ls.groups, ls.d_state), ls.in_dtype, "C")
+        _need(C, (rows, Tp, ls.groups, ls.d_state), ls.in_dtype, "C")
         if y is None:
-            y = torch.empty(ls.batch, Tp, ls.heads, ls.head_dim, dtype=torch.float32, device=x.device)
-        _need(y, (ls.batch, Tp, ls.heads, ls.head_dim), torch.float32, "y")
+            y = torch.empty(rows, Tp, ls.heads, ls.head_dim, dtype=torch.float32, device=x.device)
+        _need(y, (rows, Tp, ls.heads, ls.head_dim), torch.float32, "y")
     else:
         y = None
-    st = ls.cstate()
-    _check(lib().replayssm_prefill(ctypes.byref(ls._desc), ctypes.byref(st), Tp, int(from_zero), _ptr(x),
-                                   _ptr(B), _ptr(C) if C is not None else None, _ptr(dt), _ptr(y),
-                                   _stream(stream)))
+    _check(lib().replayssm_prefill(ctypes.byref(d), ctypes.byref(st), Tp, int(from_zero), _ptr(x),
+                                   _ptr(B), _ptr(C), _ptr(dt), _ptr(y), _stream(stream)))
     return y
 
 
-def load_checkpoint(ls: LayerState, src: torch.Tensor, stream=None) -> None:
-    """Set the checkpoint from an fp32 state [B,H,P,N] and reset positions
+def load_checkpoint(ls: LayerState, src: torch.Tensor, stream=None, slots=None) -> None:
+    """Set checkpoints from an fp32 state [rows,H,P,N] and reset their positions
     (quantising into the layer's state format; the rounding stream index is
-    the slot's current intv)."""
-    _need(src, (ls.batch, ls.heads, ls.head_dim, ls.d_state), torch.float32, "src")
-    st = ls.cstate()
-    _check(lib().replayssm_load_checkpoint(ctypes.byref(ls._desc), ctypes.byref(st), _ptr(src),
-                                           _stream(stream)))
+    the slot's current intv).  With ``slots``, row r goes to slot slots[r]
+    (admission into a slot pool)."""
+    d, st, rows = _ctx(ls, slots)
+    _need(src, (rows, ls.heads, ls.head_dim, ls.d_state), torch.float32, "src")
+    _check(lib().replayssm_load_checkpoint(ctypes.byref(d), ctypes.byref(st), _ptr(src), _stream(stream)))
 
 
 def hbm_probe(mode: int, src: torch.Tensor, dst: torch.Tensor, grid: int, stream=None) -> None:

@@ -33,6 +33,9 @@ constexpr int kMaxDraft = 8;
 
 int lcap_of(const rssm_desc *d) { return d->interval + d->max_draft - 1; }
 
+// State slots held by the buffers (rssm_desc.n_slots, 0 = batch).
+int nslots_of(const rssm_desc *d) { return d->n_slots > 0 ? d->n_slots : d->batch; }
+
 int heads_per_wg(const rssm_desc *d) {
     const int hpg = d->n_heads / d->n_groups;
     return hpg % 4 == 0 ? 4 : (hpg % 2 == 0 ? 2 : 1);
@@ -54,6 +57,7 @@ bool deferred_ok(const rssm_desc *d) { return d->deferred_commit == 1; }
 int check_desc(const rssm_desc *d) {
     if (!d) return fail(RSSM_E_ARG, "desc is NULL");
     if (d->batch < 0) return fail(RSSM_E_ARG, "batch %d < 0", d->batch);
+    if (d->n_slots < 0) return fail(RSSM_E_ARG, "n_slots %d < 0", d->n_slots);
     if (d->n_heads <= 0 || d->n_groups <= 0)
         return fail(RSSM_E_ARG, "n_heads %d / n_groups %d must be positive", d->n_heads, d->n_groups);
     if (d->n_heads % d->n_groups != 0)
@@ -93,12 +97,12 @@ int check_desc(const rssm_desc *d) {
             return fail(RSSM_E_CAPACITY, "deferred_commit: interval + max_draft = %d exceeds %d",
                         d->interval + d->max_draft, kMaxLcapVerify);
     }
-    if ((int64_t)d->batch * d->n_heads > (int64_t)1 << 24)
-        return fail(RSSM_E_ARG, "batch * n_heads too large");
+    if ((int64_t)d->batch * d->n_heads > (int64_t)1 << 24 || (int64_t)nslots_of(d) * d->n_heads > (int64_t)1 << 24)
+        return fail(RSSM_E_ARG, "batch * n_heads or n_slots * n_heads too large");
     if (split_mode(d) >= 0 && lcap_of(d) > kMaxLcapVerify)
         return fail(RSSM_E_CAPACITY, "low-precision state: interval + max_draft - 1 = %d exceeds %d",
                     lcap_of(d), kMaxLcapVerify);
-    if (split_mode(d) >= 0 && (int64_t)d->batch * d->n_heads * d->head_dim * d->d_state > 0xFFFFFFFFll)
+    if (split_mode(d) >= 0 && (int64_t)nslots_of(d) * d->n_heads * d->head_dim * d->d_state > 0xFFFFFFFFll)
         return fail(RSSM_E_ARG, "low-precision state: B*H*P*N must fit the 32-bit element index of the "
                                 "rounding stream");
     return RSSM_OK;
@@ -113,6 +117,8 @@ int check_state(const rssm_desc *d, const rssm_state *s) {
     if (!s->xbuf || !s->bbuf || !s->dtbuf) return fail(RSSM_E_ARG, "state buffers are NULL");
     if (!s->pos || !s->intv || !s->work) return fail(RSSM_E_ARG, "state pos/intv/work is NULL");
     if (!s->A || !s->D) return fail(RSSM_E_ARG, "state A/D is NULL");
+    if (!s->slot_idx && d->batch > nslots_of(d))
+        return fail(RSSM_E_ARG, "batch %d exceeds n_slots %d without a slot map", d->batch, nslots_of(d));
     return RSSM_OK;
 }
 
@@ -128,6 +134,8 @@ rssm::ReplayParams replay_params(const rssm_desc *d, const rssm_state *s) {
     p.A = s->A;
     p.D = s->D;
     p.batch = d->batch;
+    p.slot_idx = s->slot_idx;
+    p.nslots = nslots_of(d);
     p.H = d->n_heads;
     p.G = d->n_groups;
     p.L = d->interval;
@@ -286,12 +294,18 @@ int replayssm_load_checkpoint(const rssm_desc *desc, const rssm_state *st, const
         p.src = src;
         p.dbg = nullptr;
         RSSM_TRY(hip_status(rssm::launch_split_load(p, mode, stream), "load_checkpoint quantise"));
-        return hip_status(rssm::launch_zero_pos(st->pos, desc->batch, stream), "load_checkpoint pos reset");
+        return hip_status(rssm::launch_zero_pos(p, stream), "load_checkpoint pos reset");
     }
-    const size_t bytes = (size_t)desc->batch * desc->n_heads * desc->head_dim * desc->d_state * sizeof(float);
-    RSSM_TRY(hip_status(hipMemcpyAsync(st->ckpt, src, bytes, hipMemcpyDeviceToDevice, stream),
-                        "load_checkpoint copy"));
-    return hip_status(rssm::launch_zero_pos(st->pos, desc->batch, stream), "load_checkpoint pos reset");
+    rssm::ReplayParams p = replay_params(desc, st);
+    p.src = src;
+    if (st->slot_idx) {
+        RSSM_TRY(hip_status(rssm::launch_load_f32(p, stream), "load_checkpoint copy"));
+    } else {
+        const size_t bytes = (size_t)desc->batch * desc->n_heads * desc->head_dim * desc->d_state * sizeof(float);
+        RSSM_TRY(hip_status(hipMemcpyAsync(st->ckpt, src, bytes, hipMemcpyDeviceToDevice, stream),
+                            "load_checkpoint copy"));
+    }
+    return hip_status(rssm::launch_zero_pos(p, stream), "load_checkpoint pos reset");
 }
 
 int replayssm_recurrent_step(const rssm_desc *desc, float *state, const void *x, const void *B,
@@ -376,9 +390,10 @@ const char *replayssm_status_string(int status) {
 
 const char *replayssm_last_error(void) { return g_last_error; }
 
-int replayssm_check_device_errors(const rssm_state *st, int32_t batch, hipStream_t stream) {
+int replayssm_check_device_errors(const rssm_state *st, int32_t n_slots, hipStream_t stream) {
     if (!st || !st->work) return fail(RSSM_E_ARG, "check_device_errors: state/work is NULL");
-    if (batch < 0) return fail(RSSM_E_ARG, "check_device_errors: batch < 0");
+    const int32_t batch = n_slots;
+    if (batch < 0) return fail(RSSM_E_ARG, "check_device_errors: n_slots < 0");
     RSSM_TRY(hip_status(hipStreamSynchronize(stream), "check_device_errors sync"));
     int32_t word = 0;
     RSSM_TRY(hip_status(hipMemcpy(&word, st->work + batch, sizeof(word), hipMemcpyDeviceToHost),
@@ -387,7 +402,9 @@ int replayssm_check_device_errors(const rssm_state *st, int32_t batch, hipStream
     const int32_t zero = 0;
     RSSM_TRY(hip_status(hipMemcpy(st->work + batch, &zero, sizeof(zero), hipMemcpyHostToDevice),
                         "check_device_errors clear"));
-    return fail(RSSM_E_DEVICE, "device range error flags 0x%x (1: position out of range, 2: n_keep out of range)",
+    return fail(RSSM_E_DEVICE,
+                "device range error flags 0x%x (1: position out of range, 2: n_keep out of range, "
+                "4: row mapped to a slot out of range)",
                 word);
 }
 

@@ -19,12 +19,14 @@ struct ReplayParams {
     void *dtbuf;            // [B,Lcap,H]
     int32_t *pos;           // [B]
     int32_t *intv;          // [B]
-    int32_t *work;          // [B+1]
+    int32_t *work;          // [nslots+1]
     const float *A;         // [H]
     const float *D;         // [H]
     const int32_t *n_keep;  // [B] (accept)
     int batch, H, G, L, Lcap, T;
     int kmax;               // largest pos a step / verify accepts: L-1, or Lcap with deferred accepts
+    const int32_t *slot_idx;  // [batch] state slot of each call row, -1 = padding row; NULL = identity
+    int nslots;             // state slots (ckpt / buffers / pos / intv; work has nslots + 1)
     int from_zero;          // prefill: start from a zero state instead of the checkpoint
     int hpw;                // heads (waves) per workgroup
     int wg_per_slot;        // H / hpw
@@ -62,7 +64,8 @@ struct RecurrentParams {
 hipError_t launch_replay_step(const ReplayParams &p, bool in_bf16, hipStream_t s);
 hipError_t launch_replay_verify(const ReplayParams &p, bool in_bf16, hipStream_t s);
 hipError_t launch_replay_commit(const ReplayParams &p, bool in_bf16, bool accept, hipStream_t s);
-hipError_t launch_zero_pos(int32_t *pos, int batch, hipStream_t s);
+hipError_t launch_zero_pos(const ReplayParams &p, hipStream_t s);
+hipError_t launch_load_f32(const ReplayParams &p, hipStream_t s);   // ckpt[slot] <- src[row]
 hipError_t launch_defer_accept(const ReplayParams &p, hipStream_t s);
 hipError_t launch_prefill(const ReplayParams &p, bool in_bf16, bool outputs, hipStream_t s);   // p.T = prompt length
 hipError_t launch_split_step(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);

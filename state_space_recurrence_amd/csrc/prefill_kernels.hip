@@ -67,6 +67,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(ReplayParams a) {
     __shared__ PrefillSmem sm;
 
     const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
     const int Tp = a.T;
     float *sp = state_ptr(a.ckpt, s, a.H);
     float4 st[kChunks][kPerChunk];
@@ -78,14 +79,14 @@ __global__ void __launch_bounds__(256) prefill_kernel(ReplayParams a) {
     } else {
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) load_chunk(st[c], sp, c);
-        if (threadIdx.x == 0 && a.pos[s.b] != 0) atomicOr(&a.work[a.batch], kErrPos);   // buffer not empty
+        if (threadIdx.x == 0 && a.pos[s.b] != 0) atomicOr(&a.work[a.nslots], kErrPos);   // buffer not empty
     }
     const size_t HP = (size_t)a.H * kP, GN = (size_t)a.G * kN;
-    const TIn *xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.b * Tp * HP + (size_t)s.h * kP;
-    const TIn *Bin = reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.b * Tp * GN + (size_t)s.g * kN;
-    const TIn *Cin = reinterpret_cast<const TIn *>(a.Cm) + (size_t)s.b * Tp * GN + (size_t)s.g * kN;
-    const TIn *dtin = reinterpret_cast<const TIn *>(a.dt) + (size_t)s.b * Tp * a.H + s.h;
-    float *yout = a.y + (size_t)s.b * Tp * HP + (size_t)s.h * kP + s.prow;
+    const TIn *xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.row * Tp * HP + (size_t)s.h * kP;
+    const TIn *Bin = reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.row * Tp * GN + (size_t)s.g * kN;
+    const TIn *Cin = reinterpret_cast<const TIn *>(a.Cm) + (size_t)s.row * Tp * GN + (size_t)s.g * kN;
+    const TIn *dtin = reinterpret_cast<const TIn *>(a.dt) + (size_t)s.row * Tp * a.H + s.h;
+    float *yout = a.y + (size_t)s.row * Tp * HP + (size_t)s.h * kP + s.prow;
     const float Ah = a.A[s.h], Dh = a.D[s.h];
     const int i_row = s.prow >> 1;   // the lane's row 2 i + hf in cs_index terms
 

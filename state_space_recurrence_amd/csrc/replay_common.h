@@ -13,14 +13,29 @@ constexpr int kMaxHpw = 4;
 constexpr int kNB = 2;   // checkpoint chunks in flight per wave
 
 struct Slot {
-    int b, tile, wave, lane, h, g, c, hf, prow, hpg;
+    int b;     // state slot (checkpoint, buffers, pos, intv); < 0: padding row, nothing to do
+    int row;   // call row (inputs x, B, C, dt, n_keep and outputs y)
+    int tile, wave, lane, h, g, c, hf, prow, hpg;
 };
+
+// State slot of call row `row`: slot_idx[row], or `row` without a map.  Rows
+// mapped outside 0..nslots-1 are flagged and treated as padding.
+__device__ __forceinline__ int slot_of_row(const ReplayParams &a, int row) {
+    if (!a.slot_idx) return row;
+    const int b = a.slot_idx[row];
+    if (b >= a.nslots || b < -1) {
+        if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrSlot);
+        return -1;
+    }
+    return b;
+}
 
 // Slot, head tile and lane roles of logical workgroup `wg`.
 __device__ __forceinline__ Slot slot_at(const ReplayParams &a, int wg) {
     Slot s;
-    s.b = wg / a.wg_per_slot;
-    s.tile = wg - s.b * a.wg_per_slot;
+    s.row = wg / a.wg_per_slot;
+    s.tile = wg - s.row * a.wg_per_slot;
+    s.b = slot_of_row(a, s.row);
     s.wave = threadIdx.x >> 6;
     s.lane = threadIdx.x & 63;
     s.h = s.tile * a.hpw + s.wave;
@@ -133,7 +148,7 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
     StepIn in;
     int k = a.pos[s.b];
     if (k < 0 || k > kmax) {
-        if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrPos);
+        if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrPos);
         k = k < 0 ? 0 : kmax;
     }
     in.k = k;
@@ -141,10 +156,10 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
     in.commit = (in.K >= a.L);   // > L only after a deferred accept
     in.HP = (size_t)a.H * kP;
     in.GN = (size_t)a.G * kN;
-    in.xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.b * in.HP + (size_t)s.h * kP;
-    in.Bin = reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.b * in.GN + (size_t)s.g * kN;
-    in.Cin = reinterpret_cast<const TIn *>(a.Cm) + (size_t)s.b * in.GN + (size_t)s.g * kN;
-    in.dtin = reinterpret_cast<const TIn *>(a.dt) + (size_t)s.b * a.H + s.h;
+    in.xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.row * in.HP + (size_t)s.h * kP;
+    in.Bin = reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.row * in.GN + (size_t)s.g * kN;
+    in.Cin = reinterpret_cast<const TIn *>(a.Cm) + (size_t)s.row * in.GN + (size_t)s.g * kN;
+    in.dtin = reinterpret_cast<const TIn *>(a.dt) + (size_t)s.row * a.H + s.h;
     in.xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)s.b * a.Lcap * in.HP + (size_t)s.h * kP;
     in.bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * in.GN + (size_t)s.g * kN;
     in.db = reinterpret_cast<const TIn *>(a.dtbuf) + (size_t)s.b * a.Lcap * a.H + s.h;
@@ -292,7 +307,7 @@ __device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const S
     VerifyIn in;
     int k = a.pos[s.b];
     if (k < 0 || k > kmax) {
-        if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrPos);
+        if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrPos);
         k = k < 0 ? 0 : kmax;
     }
     in.k = k;
@@ -300,10 +315,10 @@ __device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const S
     in.HP = (size_t)a.H * kP;
     in.GN = (size_t)a.G * kN;
     // token-axis inputs [B,T,...]
-    in.xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.b * T * in.HP + (size_t)s.h * kP;
-    in.Bin = reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.b * T * in.GN + (size_t)s.g * kN;
-    in.Cin = reinterpret_cast<const TIn *>(a.Cm) + (size_t)s.b * T * in.GN + (size_t)s.g * kN;
-    in.dtin = reinterpret_cast<const TIn *>(a.dt) + (size_t)s.b * T * a.H + s.h;
+    in.xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.row * T * in.HP + (size_t)s.h * kP;
+    in.Bin = reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.row * T * in.GN + (size_t)s.g * kN;
+    in.Cin = reinterpret_cast<const TIn *>(a.Cm) + (size_t)s.row * T * in.GN + (size_t)s.g * kN;
+    in.dtin = reinterpret_cast<const TIn *>(a.dt) + (size_t)s.row * T * a.H + s.h;
     in.xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)s.b * a.Lcap * in.HP + (size_t)s.h * kP;
     in.bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * in.GN + (size_t)s.g * kN;
     in.db = reinterpret_cast<const TIn *>(a.dtbuf) + (size_t)s.b * a.Lcap * a.H + s.h;
@@ -569,14 +584,14 @@ __device__ __forceinline__ int commit_count(const ReplayParams &a, const Slot &s
     const int kmax = ACCEPT ? a.L - 1 : a.Lcap;
     int k = a.pos[s.b];
     if (k < 0 || k > kmax) {
-        if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrPos);
+        if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrPos);
         k = k < 0 ? 0 : kmax;
     }
     int nk = 0;
     if (ACCEPT) {
-        nk = a.n_keep[s.b];
+        nk = a.n_keep[s.row];
         if (nk < 0 || nk > a.T) {
-            if (threadIdx.x == 0) atomicOr(&a.work[a.batch], kErrKeep);
+            if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrKeep);
             nk = nk < 0 ? 0 : a.T;
         }
     }

@@ -42,6 +42,7 @@ __global__ void __launch_bounds__(256) replay_step_kernel(ReplayParams a) {
     __shared__ float sB[kBInLds<KMAX> ? KMAX : 1][kN];
 
     const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
     float *sp = state_ptr(a.ckpt, s, a.H);
 
     float4 buf[kNB][kPerChunk];
@@ -74,7 +75,7 @@ __global__ void __launch_bounds__(256) replay_step_kernel(ReplayParams a) {
         if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
     }
     const float y0 = chunk_combine4(r, s.lane);
-    a.y[(size_t)s.b * in.HP + (size_t)s.h * kP + s.prow] = lam * y0 + ybuf;
+    a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + s.prow] = lam * y0 + ybuf;
 
     if (!in.commit) step_append<TIn>(a, s, in);
     publish_position(a, s.b, in.commit ? 0 : in.K, in.commit);
@@ -95,8 +96,9 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
     Slot s;
     {
         const int wg = xcd_remap(blockIdx.x, gridDim.x);
-        s.b = wg / a.H;
-        s.tile = wg - s.b * a.H;
+        s.row = wg / a.H;
+        s.tile = wg - s.row * a.H;
+        s.b = slot_of_row(a, s.row);
         s.h = s.tile;
         s.wave = threadIdx.x >> 6;     // = the chunk this wave streams
         s.lane = threadIdx.x & 63;
@@ -106,6 +108,7 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
         s.hf = s.lane >> 5;
         s.prow = 2 * s.c + s.hf;
     }
+    if (s.b < 0) return;   // padding row
     const int q = s.wave;
     float *sp = state_ptr(a.ckpt, s, a.H);
     float4 cur[kPerChunk];
@@ -136,7 +139,7 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) r[c] = s_r[c][s.lane];
         const float y0 = chunk_combine4(r, s.lane);
-        a.y[(size_t)s.b * in.HP + (size_t)s.h * kP + s.prow] = lam * y0 + ybuf;
+        a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + s.prow] = lam * y0 + ybuf;
         if (!in.commit) step_append<TIn>(a, s, in);
     }
     publish_position(a, s.b, in.commit ? 0 : in.K, in.commit);
@@ -150,6 +153,7 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
     __shared__ VerifySmemF<KMAX, T> sm;
 
     const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
     const VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
     if (in.k >= a.L) return;   // deferred fold: replay_fold_verify_kernel, launched next
     float *sp = state_ptr(a.ckpt, s, a.H);
@@ -180,7 +184,7 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const float y0 = chunk_combine4(r[t], s.lane);
-        a.y[((size_t)s.b * T + t) * in.HP + (size_t)s.h * kP + s.prow] = lam[t] * y0 + ybuf[t];
+        a.y[((size_t)s.row * T + t) * in.HP + (size_t)s.h * kP + s.prow] = lam[t] * y0 + ybuf[t];
     }
     verify_append<TIn, T>(a, s, in);
 }
@@ -195,6 +199,7 @@ __global__ void __launch_bounds__(256) replay_fold_verify_kernel(ReplayParams a)
     __shared__ FoldSmem<KMAX, T> sm;
 
     const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
     VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
     if (in.k < a.L) return;
     float *sp = state_ptr(a.ckpt, s, a.H);
@@ -220,11 +225,11 @@ __global__ void __launch_bounds__(256) replay_fold_verify_kernel(ReplayParams a)
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const float y0 = chunk_combine4(r[t], s.lane);
-        a.y[((size_t)s.b * T + t) * in.HP + (size_t)s.h * kP + s.prow] = sm.u.v.lam[s.wave][t] * y0 + ybuf[t];
+        a.y[((size_t)s.row * T + t) * in.HP + (size_t)s.h * kP + s.prow] = sm.u.v.lam[s.wave][t] * y0 + ybuf[t];
     }
     in.k = 0;
     verify_append<TIn, T, false>(a, s, in);
-    publish_fold<TIn>(a, s.b, 0, reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.b * T * in.GN, T);
+    publish_fold<TIn>(a, s.b, 0, reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.row * T * in.GN, T);
 }
 
 // ------------------------------------------------------------------------
@@ -237,6 +242,7 @@ __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
     __shared__ float sB[KMAX][kN];
 
     const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
     bool commit;
     const int K = commit_count<ACCEPT>(a, s, &commit);
     if (commit) {
@@ -262,26 +268,51 @@ __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
 
 // Deferred accept: pos += n_keep only; a slot reaching L keeps its entries
 // until the next step, verify or flush on it folds them.
-__global__ void defer_accept_kernel(int32_t *pos, const int32_t *n_keep, int32_t *work, int batch, int L,
-                                    int T) {
-    const int b = blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= batch) return;
-    int k = pos[b];
-    if (k < 0 || k > L - 1) {
-        atomicOr(&work[batch], kErrPos);
-        k = k < 0 ? 0 : L - 1;
+__global__ void defer_accept_kernel(ReplayParams a) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.batch) return;
+    int b = row;
+    if (a.slot_idx) {
+        b = a.slot_idx[row];
+        if (b >= a.nslots || b < -1) atomicOr(&a.work[a.nslots], kErrSlot);
+        if (b < 0 || b >= a.nslots) return;
     }
-    int nk = n_keep[b];
-    if (nk < 0 || nk > T) {
-        atomicOr(&work[batch], kErrKeep);
-        nk = nk < 0 ? 0 : T;
+    int k = a.pos[b];
+    if (k < 0 || k > a.L - 1) {
+        atomicOr(&a.work[a.nslots], kErrPos);
+        k = k < 0 ? 0 : a.L - 1;
     }
-    pos[b] = k + nk;
+    int nk = a.n_keep[row];
+    if (nk < 0 || nk > a.T) {
+        atomicOr(&a.work[a.nslots], kErrKeep);
+        nk = nk < 0 ? 0 : a.T;
+    }
+    a.pos[b] = k + nk;
 }
 
-__global__ void zero_pos_kernel(int32_t *pos, int n) {
-    int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i < n) pos[i] = 0;
+__global__ void zero_pos_kernel(ReplayParams a) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.batch) return;
+    const int b = a.slot_idx ? a.slot_idx[row] : row;
+    if (b >= 0 && b < a.nslots) a.pos[b] = 0;
+}
+
+// ckpt[slot_idx[row]] <- src[row] for every mapped row (fp32 checkpoint); one
+// workgroup per (row, head), 16-byte non-temporal copies.
+__global__ void __launch_bounds__(256) load_f32_kernel(ReplayParams a) {
+    const int row = blockIdx.x / a.H, h = blockIdx.x - row * a.H;
+    const int b = a.slot_idx ? a.slot_idx[row] : row;
+    if (b < 0 || b >= a.nslots) {
+        if (threadIdx.x == 0 && (b < -1 || b >= a.nslots)) atomicOr(&a.work[a.nslots], kErrSlot);
+        return;
+    }
+    const float *src = a.src + ((size_t)row * a.H + h) * kP * kN;
+    float *dst = a.ckpt + ((size_t)b * a.H + h) * kP * kN;
+#pragma unroll
+    for (int i = 0; i < kP * kN / 4 / 256; ++i) {
+        const int e = 4 * (threadIdx.x + 256 * i);
+        stream_store4(dst + e, stream_load4(src + e));
+    }
 }
 
 }  // namespace
@@ -375,14 +406,19 @@ hipError_t launch_replay_commit(const ReplayParams &p, bool in_bf16, bool accept
 
 hipError_t launch_defer_accept(const ReplayParams &p, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
-    hipLaunchKernelGGL(defer_accept_kernel, dim3((p.batch + 255) / 256), dim3(256), 0, stream, p.pos, p.n_keep,
-                       p.work, p.batch, p.L, p.T);
+    hipLaunchKernelGGL(defer_accept_kernel, dim3((p.batch + 255) / 256), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
-hipError_t launch_zero_pos(int32_t *pos, int batch, hipStream_t stream) {
-    if (batch == 0) return hipSuccess;
-    hipLaunchKernelGGL(zero_pos_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, pos, batch);
+hipError_t launch_zero_pos(const ReplayParams &p, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    hipLaunchKernelGGL(zero_pos_kernel, dim3((p.batch + 255) / 256), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_load_f32(const ReplayParams &p, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    hipLaunchKernelGGL(load_f32_kernel, dim3(p.batch * p.H), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 

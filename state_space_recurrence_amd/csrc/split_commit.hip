@@ -11,6 +11,7 @@ __global__ void __launch_bounds__(256) split_commit_kernel(ReplayParams a) {
     __shared__ CommitSmem<KMAX> sm;
     __shared__ float sB[KMAX][kN];
     const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
     bool commit;
     const int K = commit_count<ACCEPT>(a, s, &commit);
     const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;
@@ -29,14 +30,16 @@ __global__ void __launch_bounds__(256) split_commit_kernel(ReplayParams a) {
 template <int MODE>
 __global__ void __launch_bounds__(256) split_load_kernel(ReplayParams a) {
     const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
     const uint32_t interval = (uint32_t)a.intv[s.b];
-    const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
+    const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;     // destination (state slot)
+    const size_t srow = ((size_t)s.row * a.H + s.h) * kP + s.hf;   // source (call row)
 #pragma unroll
     for (int q = 0; q < kChunks; ++q) {
         float4 st[kPerChunk];
 #pragma unroll
         for (int m = 0; m < kPerChunk; ++m)
-            st[m] = stream_load4(a.src + (hrow + 2 * chunk_index(q, m)) * kN + 4 * s.c);
+            st[m] = stream_load4(a.src + (srow + 2 * chunk_index(q, m)) * kN + 4 * s.c);
 #pragma unroll
         for (int m = 0; m < kPerChunk; ++m)
             quantize_store_row<MODE>(a, hrow + 2 * chunk_index(q, m), s.c, s.lane, st[m], interval);

@@ -14,6 +14,7 @@ __global__ void __launch_bounds__(256) split_step_kernel(ReplayParams a) {
     __shared__ float sB[KMAX][kN];   // the group's B entries, staged on commit steps
 
     const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
     const int prow = MT::fp4_out ? fp4_prow(s.lane) : s.prow;
     const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
 
@@ -42,7 +43,7 @@ __global__ void __launch_bounds__(256) split_step_kernel(ReplayParams a) {
         float c8[1][8], y0[1];
         load_c8<TIn>(static_cast<const TIn *>(in.Cin), s.lane & 15, c8[0]);
         fp4_rows_dot<1>(o, c8, s.lane, y0);
-        a.y[(size_t)s.b * in.HP + (size_t)s.h * kP + prow] = lam * y0[0] + ybuf;
+        a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + prow] = lam * y0[0] + ybuf;
         if (in.commit) commit_head<KMAX, MODE>(a, s, lam, sm.cs[s.wave], sB, interval);
     } else {
         const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
@@ -64,7 +65,7 @@ __global__ void __launch_bounds__(256) split_step_kernel(ReplayParams a) {
             if (in.commit) commit_chunk_q<KMAX, MODE>(a, s, st, q, lam, sm.cs[s.wave], sB, interval);
         }
         const float y0 = chunk_combine4(r, s.lane);
-        a.y[(size_t)s.b * in.HP + (size_t)s.h * kP + prow] = lam * y0 + ybuf;
+        a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + prow] = lam * y0 + ybuf;
     }
 
     if (!in.commit) step_append<TIn>(a, s, in);

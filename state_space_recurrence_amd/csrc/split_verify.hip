@@ -14,6 +14,7 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
     __shared__ VerifySmem<KMAX, T> sm;
 
     const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
     const int prow = MT::fp4_out ? fp4_prow(s.lane) : s.prow;
     const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
 
@@ -45,7 +46,7 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
     }
 #pragma unroll
     for (int t = 0; t < T; ++t)
-        a.y[((size_t)s.b * T + t) * in.HP + (size_t)s.h * kP + prow] = sm.lam[s.wave][t] * y0[t] + ybuf[t];
+        a.y[((size_t)s.row * T + t) * in.HP + (size_t)s.h * kP + prow] = sm.lam[s.wave][t] * y0[t] + ybuf[t];
     verify_append<TIn, T>(a, s, in);
 }
 

@@ -131,6 +131,19 @@ def test_prefill_arguments_checked(rs):
     assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), 4, 0, None, None, None, None, None, None) == 0
 
 
+def test_slot_map_arguments_checked(rs):
+    """Without a slot map the call's rows are slots 0..batch-1, so batch may
+    not exceed n_slots; with one, any row count is allowed."""
+    L = rs.lib()
+    st = rs.RssmState(*([1] * 11))          # non-NULL placeholders, no launch happens on error
+    d = _desc(rs, batch=6)
+    d.n_slots = 4
+    assert L.replayssm_step(ctypes.byref(d), ctypes.byref(st), None, None, None, None, None, None) == -1
+    assert "n_slots" in L.replayssm_last_error().decode()
+    d.n_slots = -2
+    assert L.replayssm_check_desc(ctypes.byref(d)) == -1
+
+
 def test_empty_batch_is_a_noop_without_device(rs):
     L = rs.lib()
     d = _desc(rs, batch=0)
