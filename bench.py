@@ -108,11 +108,14 @@ def main():
                                     "python -u bench.py --steps 64 --no-cpu-baseline",
                             title="Kernel trace: every benchmarked path",
                             workload="4B-class layers at batch 256 (64 timed steps), 1 and 512; 120B-class "
-                                     "(batch 256, 8 layers, 128 heads); speculative verify + accept "
-                                     "(batch 512, 4 drafts) and its per-draft-copy baseline; the precision "
-                                     "split formats (batch 256, 4 layers) and their drift runs.  Kernel names "
-                                     "carry <input type, max buffer entries, ...> template arguments; "
-                                     "split modes 0..4 = split-bf16, split-e4m3, shared-fp4, low-bf16, low-e4m3.")
+                                     "(batch 256, 8 layers, 128 heads); lock-step and staggered interval "
+                                     "phases; the interval sweep L = 4..64; speculative verify + accept "
+                                     "(batch 512, 4 drafts; eager and deferred commits) and its per-draft-copy "
+                                     "baseline; prompt prefill (one 4B-class layer, batch 256, 256 tokens) "
+                                     "against token-by-token decode; the precision split formats (batch 256, "
+                                     "4 layers) and their drift runs.  Kernel names carry <input type, max "
+                                     "buffer entries, ...> template arguments; split modes 0..4 = split-bf16, "
+                                     "split-e4m3, shared-fp4, low-bf16, low-e4m3.")
         return
     if args.summarize_counters:
         cmd = ("rocprofv3 --pmc COUNTER -f csv -d gpurun_out/pmc_COUNTER -o pmc -- "
@@ -699,7 +702,7 @@ def cpu_baseline(w, steps, log, slots=None):
 
 
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "replay_step_4b_b256_counters.md")
-KERNEL_SOURCES = ("replay_kernels.hip", "device_common.h")
+KERNEL_SOURCES = ("replay_kernels.hip", "replay_common.h", "device_common.h", "kernels.h")
 
 
 def _kernel_source_hash() -> str:
