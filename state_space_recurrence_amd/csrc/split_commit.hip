@@ -41,8 +41,11 @@ __global__ void __launch_bounds__(256) split_load_kernel(ReplayParams a) {
         for (int m = 0; m < kPerChunk; ++m)
             st[m] = stream_load4(a.src + (srow + 2 * chunk_index(q, m)) * kN + 4 * s.c);
 #pragma unroll
-        for (int m = 0; m < kPerChunk; ++m)
-            quantize_store_row<MODE>(a, hrow + 2 * chunk_index(q, m), s.c, s.lane, st[m], interval);
+        for (int m = 0; m < kPerChunk; m += 2) {
+            quantize_store_rows<MODE>(a, hrow + 2 * chunk_index(q, m), hrow + 2 * chunk_index(q, m + 1), s.c,
+                                      s.lane, st[m], st[m + 1], interval);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 }
 

@@ -97,18 +97,40 @@ __device__ __forceinline__ float4 decode_row4(typename Raw4<UB>::T r) {
     }
 }
 
+// The 16-bit draws of columns 4c..4c+3 of two rows (elements e0 and e1,
+// multiples of 4).  Lanes 2j and 2j+1 share each Philox counter (8 draws =
+// 8 columns); instead of both computing it, the even lane computes row 0's
+// counter and the odd lane row 1's, and they swap the halves the other needs
+// (one quad_perm [1,0,3,2] exchange).  The draws are those of sr_draws4.
+__device__ __forceinline__ uint32_t swap_pair_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadSwap1, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ void sr_draws4_pair(uint64_t seed, uint32_t layer, uint32_t interval, uint32_t e0,
+                                               uint32_t e1, int lane, uint32_t (&r0)[4], uint32_t (&r1)[4]) {
+    const bool odd = lane & 1;
+    const Philox4 o = philox4x32_10((odd ? e1 : e0) >> 3, interval, layer, 0, (uint32_t)seed,
+                                    (uint32_t)(seed >> 32));
+    // an even lane's columns use words x, y of a counter, an odd lane's z, w
+    const uint32_t own_a = odd ? o.z : o.x, own_b = odd ? o.w : o.y;
+    const uint32_t got_a = swap_pair_u32(odd ? o.x : o.z), got_b = swap_pair_u32(odd ? o.y : o.w);
+    const uint32_t wa0 = odd ? got_a : own_a, wb0 = odd ? got_b : own_b;
+    const uint32_t wa1 = odd ? own_a : got_a, wb1 = odd ? own_b : got_b;
+    r0[0] = wa0 & 0xFFFFu; r0[1] = wa0 >> 16; r0[2] = wb0 & 0xFFFFu; r0[3] = wb0 >> 16;
+    r1[0] = wa1 & 0xFFFFu; r1[1] = wa1 >> 16; r1[2] = wb1 & 0xFFFFu; r1[3] = wb1 >> 16;
+}
+
 // Rounds and stores one row slice (columns 4c..4c+3 of row `row`) of a new
-// state: the update checkpoint by stochastic rounding with stream index
-// `interval`, the output copy by FP4 quantisation (scale over the 8 lanes
-// sharing a 32-element block).  Must be called by all 64 lanes together.
+// state: the update checkpoint by stochastic rounding with the draws `r`
+// (stream index of the interval being started), the output copy by FP4
+// quantisation (scale over the 8 lanes sharing a 32-element block).  Must be
+// called by all 64 lanes together.
 template <int MODE>
 __device__ __forceinline__ void quantize_store_row(const ReplayParams &a, size_t row, int c, int lane,
-                                                   float4 v, uint32_t interval) {
+                                                   float4 v, const uint32_t (&r)[4]) {
     using MT = ModeTraits<MODE>;
     if (a.dbg) stream_store4(a.dbg + row * kN + 4 * c, v);
     if constexpr (MT::has_u) {
-        uint32_t r[4];
-        sr_draws4(a.seed, (uint32_t)a.layer, interval, (uint32_t)(row * kN + 4 * c), r);
         if constexpr (MT::ubits == 16) {
             uint2 q;
             q.x = bf16_sr(v.x, r[0]) | (bf16_sr(v.y, r[1]) << 16);
@@ -134,6 +156,19 @@ __device__ __forceinline__ void quantize_store_row(const ReplayParams &a, size_t
         *reinterpret_cast<uint16_t *>(a.oq + row * (kN / 2) + 2 * c) = (uint16_t)code16;
         if ((c & 7) == 0) a.os[row * (kN / 32) + (c >> 3)] = (uint8_t)sc;
     }
+}
+
+// Two row slices (see quantize_store_row), their draws generated together.
+template <int MODE>
+__device__ __forceinline__ void quantize_store_rows(const ReplayParams &a, size_t row0, size_t row1, int c, int lane,
+                                                    float4 v0, float4 v1, uint32_t interval) {
+    uint32_t r0[4] = {0, 0, 0, 0}, r1[4] = {0, 0, 0, 0};
+    if constexpr (ModeTraits<MODE>::has_u)
+        sr_draws4_pair(a.seed, (uint32_t)a.layer, interval, (uint32_t)(row0 * kN + 4 * c),
+                       (uint32_t)(row1 * kN + 4 * c), lane, r0, r1);
+    quantize_store_row<MODE>(a, row0, c, lane, v0, r0);
+    __builtin_amdgcn_sched_barrier(0);   // the rows' quantisers one after the other
+    quantize_store_row<MODE>(a, row1, c, lane, v1, r1);
 }
 
 // New state rows of chunk q (rows 2(q + 4m) + hf) from the decoded source
@@ -171,11 +206,22 @@ __device__ __forceinline__ void commit_chunk_q(const ReplayParams &a, const Slot
     // rounding streams from being interleaved with, and stretching, the FMAs)
 #pragma unroll
     for (int m = 0; m < kPerChunk; ++m) asm volatile("" : "+v"(st[m].x), "+v"(st[m].y), "+v"(st[m].z), "+v"(st[m].w));
+    if constexpr (ModeTraits<MODE>::has_u) {
 #pragma unroll
-    for (int m = 0; m < kPerChunk; ++m) {
-        const size_t row = ((size_t)s.b * a.H + s.h) * kP + 2 * chunk_index(q, m) + s.hf;
-        quantize_store_row<MODE>(a, row, s.c, s.lane, st[m], interval);
-        __builtin_amdgcn_sched_barrier(0);   // one row's rounding stream at a time
+        for (int m = 0; m < kPerChunk; m += 2) {
+            const size_t row0 = ((size_t)s.b * a.H + s.h) * kP + 2 * chunk_index(q, m) + s.hf;
+            const size_t row1 = ((size_t)s.b * a.H + s.h) * kP + 2 * chunk_index(q, m + 1) + s.hf;
+            quantize_store_rows<MODE>(a, row0, row1, s.c, s.lane, st[m], st[m + 1], interval);
+            __builtin_amdgcn_sched_barrier(0);   // one row pair's rounding streams at a time
+        }
+    } else {   // no stochastic rounding (shared FP4): one row at a time
+        const uint32_t none[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int m = 0; m < kPerChunk; ++m) {
+            const size_t row = ((size_t)s.b * a.H + s.h) * kP + 2 * chunk_index(q, m) + s.hf;
+            quantize_store_row<MODE>(a, row, s.c, s.lane, st[m], none);
+            __builtin_amdgcn_sched_barrier(0);
+        }
     }
 }
 
