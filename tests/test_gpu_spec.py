@@ -174,3 +174,55 @@ def test_n_keep_out_of_range_is_flagged(rs):
     with pytest.raises(rs.ReplaySSMError, match="device"):
         rs.check_device_errors(ls)
     assert ls.pos.cpu().tolist() == [T, 0]
+
+
+@pytest.mark.parametrize("deferred", [False, True])
+def test_spec_rounds_inside_hip_graph(rs, deferred):
+    """Four speculative rounds (verify + accept, eager or deferred) captured
+    in one HIP graph and replayed three times, with eager work and syncs
+    between replays: every replay reproduces eager execution bit for bit
+    (outputs, checkpoint, positions).  The path records no memset nodes."""
+    w = dataclasses.replace(synth.WORKLOADS["spec"], heads=16, groups=2)
+    T, R, batch = w.drafts + 1, 4, 5
+    A, D = synth.layer_params(w, 1)
+    S0 = synth.init_state(w, 1, batch=batch).cuda()
+    x, Bm, Cm, dt = synth.token_inputs(w, 1, R, batch=batch, tokens=T, stream=41)
+    nk = synth.n_keep(w, R, batch=batch, stream=41).cuda()
+    ins = [tuple(_bt(t[r]).cuda() for t in (x, Bm, Cm, dt)) for r in range(R)]
+    acc = rs.accept_deferred if deferred else rs.accept
+    kw = dict(interval=w.interval, max_draft=T, in_dtype=x.dtype, deferred_commit=deferred)
+
+    def rounds(ls, ys):
+        for r in range(R):
+            rs.verify(ls, *ins[r], y=ys[r])
+            acc(ls, nk[r].contiguous(), T)
+
+    ref = rs.LayerState(batch, w.heads, w.groups, A, D, **kw)
+    rs.load_checkpoint(ref, S0)
+    eager = []
+    for _ in range(3):
+        ys = [torch.empty(batch, T, w.heads, 64, device="cuda") for _ in range(R)]
+        rounds(ref, ys)
+        eager.append(([y.clone() for y in ys], ref.ckpt.clone(), ref.pos.clone()))
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, **kw)
+    rs.load_checkpoint(ls, S0)
+    ys = [torch.empty(batch, T, w.heads, 64, device="cuda") for _ in range(R)]
+    snap = ls.snapshot()
+    g = torch.cuda.CUDAGraph()
+    s2 = torch.cuda.Stream()
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s2):
+        with torch.cuda.graph(g, stream=s2):
+            rounds(ls, ys)
+    torch.cuda.current_stream().wait_stream(s2)
+    torch.cuda.synchronize()
+    ls.restore(snap)
+    ls.work.zero_()
+    for i in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        for r in range(R):
+            assert torch.equal(ys[r], eager[i][0][r]), (i, r)
+        assert torch.equal(ls.ckpt, eager[i][1]) and torch.equal(ls.pos, eager[i][2]), i
+        _ = (ls.ckpt * 2.0).sum().item()   # unrelated eager work between replays
+    rs.check_device_errors(ls)
