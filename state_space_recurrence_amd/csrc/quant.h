@@ -57,18 +57,6 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
     return {c0, c1, c2, c3};
 }
 
-// The four 16-bit draws for elements e0..e0+3 (e0 a multiple of 4).
-__device__ __forceinline__ void sr_draws4(uint64_t seed, uint32_t layer, uint32_t interval, uint32_t e0,
-                                          uint32_t (&r)[4]) {
-    const Philox4 o = philox4x32_10(e0 >> 3, interval, layer, 0, (uint32_t)seed, (uint32_t)(seed >> 32));
-    const uint32_t wa = (e0 & 4) ? o.z : o.x;
-    const uint32_t wb = (e0 & 4) ? o.w : o.y;
-    r[0] = wa & 0xFFFFu;
-    r[1] = wa >> 16;
-    r[2] = wb & 0xFFFFu;
-    r[3] = wb >> 16;
-}
-
 // ------------------------------------------------------------------- bf16 --
 __device__ __forceinline__ float bf16_decode(uint32_t code16) { return __uint_as_float(code16 << 16); }
 

@@ -98,10 +98,12 @@ __device__ __forceinline__ float4 decode_row4(typename Raw4<UB>::T r) {
 }
 
 // The 16-bit draws of columns 4c..4c+3 of two rows (elements e0 and e1,
-// multiples of 4).  Lanes 2j and 2j+1 share each Philox counter (8 draws =
-// 8 columns); instead of both computing it, the even lane computes row 0's
-// counter and the odd lane row 1's, and they swap the halves the other needs
-// (one quad_perm [1,0,3,2] exchange).  The draws are those of sr_draws4.
+// multiples of 4).  Element e draws halfword (e mod 8) of Philox4x32-10 at
+// counter (e / 8, interval, layer, 0), key = seed, low halfword of each word
+// first -- so lanes 2j and 2j+1 share a counter (8 draws = 8 columns).
+// Instead of both computing it, the even lane computes row 0's counter and
+// the odd lane row 1's, and they swap the halves the other needs (one
+// quad_perm [1,0,3,2] exchange).
 __device__ __forceinline__ uint32_t swap_pair_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadSwap1, 0xF, 0xF, false);
 }
