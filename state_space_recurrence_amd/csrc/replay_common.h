@@ -601,12 +601,17 @@ __device__ __forceinline__ int commit_count(const ReplayParams &a, const Slot &s
 }
 
 // Lambda_K, commit coefficients (LDS) and this lane's B_j slices for folding
-// all K buffered entries (K >= 1).
+// all K buffered entries (K >= 1).  l_i = A dt_i lives in lane i; the prefix
+// sum (Lambda_K) and each lane's suffix sum sum_{lane < i < K} l_i grow in
+// ascending i through lane broadcasts (no LDS round trips).  sl / sw are
+// unused (kept for the callers' shared-memory layouts).
 template <typename TIn, int KMAX, bool LOAD_BJ = true>
 __device__ __forceinline__ float commit_prologue(const ReplayParams &a, const Slot &s, int K,
                                                  float (*sl)[KMAX], float (*sw)[KMAX],
                                                  float (*scs)[kP * KMAX],
                                                  typename io<TIn>::raw4 (&Bj)[KMAX]) {
+    (void)sl;
+    (void)sw;
     const size_t HP = (size_t)a.H * kP, GN = (size_t)a.G * kN;
     const TIn *xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)s.b * a.Lcap * HP + (size_t)s.h * kP;
     const TIn *bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * GN + (size_t)s.g * kN;
@@ -620,33 +625,24 @@ __device__ __forceinline__ float commit_prologue(const ReplayParams &a, const Sl
         xv[j] = io<TIn>::load1(xb + (size_t)jj * HP + s.prow);
         if (LOAD_BJ) Bj[j] = io<TIn>::load_raw4(bb + (size_t)jj * GN + 4 * s.c);
     }
-    float dl = 0.f;
-    if (s.lane < K) {
-        dl = io<TIn>::load1(db + (size_t)s.lane * a.H);
-        sl[s.wave][s.lane] = Ah * dl;
+    const float dl = s.lane < K ? io<TIn>::load1(db + (size_t)s.lane * a.H) : 0.f;
+    const float l = Ah * dl;
+    float tot = 0.f, suf = 0.f;
+    for (int i = 0; i < K; ++i) {
+        const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
+        tot += li;
+        if (i > s.lane) suf += li;
     }
-    __syncthreads();
-    float tot = 0.f;
-    for (int i = 0; i < K; ++i) tot += sl[s.wave][i];
-    if (s.lane < KMAX) {
-        float wj = 0.f;
-        if (s.lane < K) {
-            float suf = 0.f;
-            for (int i = s.lane + 1; i < K; ++i) suf += sl[s.wave][i];
-            wj = dl * expf(suf);
-        }
-        sw[s.wave][s.lane] = wj;
-    }
-    __syncthreads();
+    const float wj = s.lane < K ? dl * expf(suf) : 0.f;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-        const float cf = sw[s.wave][j] * xv[j];
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
+        const float cf = w * xv[j];
         scs[s.wave][cs_index<KMAX>(s.hf, s.c & 3, j, s.c >> 2)] = (j < K) ? cf : 0.f;
     }
     __syncthreads();
     return expf(tot);
 }
-
 
 // As commit_chunk, with the group's B entries staged in LDS (sB, zero past
 // K) and the entry loop cut at Kr = K rounded up to 4, so a short fold does
@@ -711,29 +707,25 @@ template <int KMAX, int T>
 struct FoldSmem {
     float cs[kMaxHpw][kP * KMAX];   // commit coefficients (cs_index layout)
     float B[KMAX][kN];              // the group's B entries, zero past K
-    union {
-        struct {
-            float l[kMaxHpw][KMAX];
-            float w[kMaxHpw][KMAX];
-        } c;                        // commit prologue scratch, dead once cs is built
-        VerifySmem<KMAX, T> v;      // replay coefficients of the T new tokens
-    } u;
+    VerifySmemF<KMAX, T> v;         // the drafts' Gram operands and rows
 };
 
 // Commit coefficients of the K buffered entries, then the replay
-// coefficients and buffer part of the outputs of T tokens at positions
-// 0..T-1 (token inputs as laid out for verify).  Returns Lambda_K.
+// coefficients, Lambda_t (lam) and buffer part of the outputs of T tokens at
+// positions 0..T-1 (token inputs as laid out for verify).  Returns Lambda_K.
 template <typename TIn, int KMAX, int T>
 __device__ __forceinline__ float fold_prologue(const ReplayParams &a, const Slot &s, int K, const VerifyIn &in,
-                                               FoldSmem<KMAX, T> &sm, float (&ybuf)[T]) {
-    stage_B<TIn, KMAX>(sm.B, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.bb), in.GN, K, K);
-    typename io<TIn>::raw4 unused[KMAX];
-    const float lam = commit_prologue<TIn, KMAX, false>(a, s, K, sm.u.c.l, sm.u.c.w, sm.cs, unused);
+                                               FoldSmem<KMAX, T> &sm, float (&ybuf)[T], float (&lam)[T]) {
     VerifyIn v = in;
     v.k = 0;
     v.KL = T;
-    verify_prologue<TIn, KMAX, T>(a, s, v, s.prow, sm.u.v, ybuf);
-    return lam;
+    VerifyPre<TIn, KMAX, T> pre;
+    verify_preload<TIn, KMAX, T>(a, s, v, s.prow, pre);
+    stage_B<TIn, KMAX>(sm.B, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.bb), in.GN, K, K);
+    typename io<TIn>::raw4 unused[KMAX];
+    const float lamK = commit_prologue<TIn, KMAX, false>(a, s, K, nullptr, nullptr, sm.cs, unused);
+    verify_finish<TIn, KMAX, T>(a, s, v, pre, sm.v, ybuf, lam);
+    return lamK;
 }
 
 // End of a fold: the last-arriving workgroup of slot b publishes the commit

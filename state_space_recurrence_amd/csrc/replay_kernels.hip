@@ -215,8 +215,8 @@ __global__ void __launch_bounds__(256) replay_fold_verify_kernel(ReplayParams a)
 #pragma unroll
     for (int t = 0; t < T; ++t)
         C4[t] = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN + 4 * s.c);
-    float ybuf[T];
-    const float lam = fold_prologue<TIn, KMAX, T>(a, s, in.k, in, sm, ybuf);
+    float ybuf[T], lamt[T];
+    const float lam = fold_prologue<TIn, KMAX, T>(a, s, in.k, in, sm, ybuf, lamt);
     const int Kr = (in.k + 3) & ~3;
     float r[T][kChunks];
 #pragma unroll
@@ -229,7 +229,7 @@ __global__ void __launch_bounds__(256) replay_fold_verify_kernel(ReplayParams a)
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const float y0 = chunk_combine4(r[t], s.lane);
-        a.y[((size_t)s.row * T + t) * in.HP + (size_t)s.h * kP + s.prow] = sm.u.v.lam[s.wave][t] * y0 + ybuf[t];
+        a.y[((size_t)s.row * T + t) * in.HP + (size_t)s.h * kP + s.prow] = lamt[t] * y0 + ybuf[t];
     }
     in.k = 0;
     verify_append<TIn, T, false>(a, s, in);
