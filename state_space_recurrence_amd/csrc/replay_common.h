@@ -125,11 +125,7 @@ __device__ __forceinline__ void commit_chunk(float4 (&st)[kPerChunk], int c, flo
 // ------------------------------------------------------------------------
 template <int KMAX>
 struct StepSmem {
-    float l[kMaxHpw][KMAX];        // A dt_j
-    float dt[kMaxHpw][KMAX];       // dt_j
     float gram[KMAX];              // B_j . C  (one group per workgroup)
-    float w[kMaxHpw][KMAX];        // w_j = dt_j exp(sum_{j<i<K} l_i), zero for j >= K
-    float cy[kMaxHpw][KMAX];       // w_j gram_j, zero for j >= K
     float cs[kMaxHpw][kP * KMAX];  // commit coefficients w_j x_j[r] (cs_index layout)
 };
 
@@ -191,12 +187,9 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
     const float xcur = io<TIn>::load1(xin + prow);
     const float Ah = a.A[s.h], Dh = a.D[s.h];
 
-    if (s.lane < K) {
-        const TIn *pd = (s.lane < k) ? db + (size_t)s.lane * a.H : static_cast<const TIn *>(in.dtin);
-        const float d = io<TIn>::load1(pd);
-        sm.dt[s.wave][s.lane] = d;
-        sm.l[s.wave][s.lane] = Ah * d;
-    }
+    const float d = s.lane < K ? io<TIn>::load1((s.lane < k) ? db + (size_t)s.lane * a.H
+                                                            : static_cast<const TIn *>(in.dtin))
+                               : 0.f;
     {   // Gram row g_j = B_j . C, 16 lanes x 8 elements per dot
         const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4, ngrp = blockDim.x >> 4;
         const float4 c0 = io<TIn>::load4(Cin + 8 * t16), c1 = io<TIn>::load4(Cin + 8 * t16 + 4);
@@ -209,26 +202,25 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
     }
     __syncthreads();
 
-    float tot = 0.f;
-    for (int i = 0; i < K; ++i) tot += sm.l[s.wave][i];
-    *lam = expf(tot);
-    if (s.lane < KMAX) {
-        float wj = 0.f, cy = 0.f;
-        if (s.lane < K) {
-            float suf = 0.f;
-            for (int i = s.lane + 1; i < K; ++i) suf += sm.l[s.wave][i];
-            wj = sm.dt[s.wave][s.lane] * expf(suf);
-            cy = wj * sm.gram[s.lane];
-        }
-        sm.w[s.wave][s.lane] = wj;
-        sm.cy[s.wave][s.lane] = cy;
+    // l_i = A dt_i lives in lane i.  Lambda_K = exp(sum_{i<K} l_i) and each
+    // lane's suffix sum_{lane < i < K} l_i grow in ascending i through lane
+    // broadcasts (no LDS round trips).
+    const float l = Ah * d;
+    float tot = 0.f, suf = 0.f;
+    for (int i = 0; i < K; ++i) {
+        const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
+        tot += li;
+        if (i > s.lane) suf += li;
     }
-    __syncthreads();
+    *lam = expf(tot);
+    const float wj = s.lane < K ? d * expf(suf) : 0.f;               // w_j in lane j, zero for j >= K
+    const float cyj = s.lane < K ? wj * sm.gram[s.lane < KMAX ? s.lane : 0] : 0.f;   // w_j g_j
 
     float yb = Dh * xcur;
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-        const float term = sm.cy[s.wave][j] * xv[j];
+        const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cyj), j));
+        const float term = cj * xv[j];
         yb += (j < K) ? term : 0.f;   // select: entries beyond K never leak (even NaN)
     }
     *ybuf = yb;
@@ -237,7 +229,8 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
         const int i = prow >> 1, hf = prow & 1;
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
-            const float cf = sm.w[s.wave][j] * xv[j];
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
+            const float cf = w * xv[j];
             sm.cs[s.wave][cs_index<KMAX>(hf, i & 3, j, i >> 2)] = (j < K) ? cf : 0.f;
             if (LOAD_BJ) {
                 const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin;
