@@ -112,7 +112,7 @@ typedef enum rssm_dtype {
 
 /* Layer descriptor (host struct). */
 typedef struct rssm_desc {
-    int32_t batch;        /* B: sequence slots */
+    int32_t batch;        /* rows of a call (one sequence each); without a slot map, row b is slot b */
     int32_t n_heads;      /* H */
     int32_t head_dim;     /* P */
     int32_t d_state;      /* N */
