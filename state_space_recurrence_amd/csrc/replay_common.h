@@ -401,28 +401,45 @@ __device__ __forceinline__ void verify_prologue(const ReplayParams &a, const Slo
 // ---- Split form of the verify prologue for the verify kernel.  Loads
 // retire in issue order, so a wave waiting for a load issued after the
 // checkpoint chunks also waits for those chunks: verify_preload issues every
-// prologue load (x rows, dt, and the Gram operands B_j / C_t as raw pieces)
-// before the kernel starts the checkpoint stream, and verify_finish consumes
-// them: Gram rows from LDS, then per-wave decay sums and weights in
-// registers.  Arithmetic and summation order are those of verify_prologue,
-// so results are bit-identical to it.
+// prologue load (the head's x rows, dt, and the Gram operands B_j / C_t as
+// raw pieces) before the kernel starts the checkpoint stream, and
+// verify_finish consumes them through LDS: Gram rows, per-wave decay sums
+// (lane broadcasts), then the buffer part of the outputs from the staged x
+// rows and replay coefficients.  The raw pieces occupy few registers while
+// the first chunks are in flight, which keeps the kernel at four waves per
+// SIMD.  Per-output arithmetic and summation order are those of
+// verify_prologue.
 template <int KMAX, int T>
 constexpr int stage_pieces() { return (KMAX + T) * (kN / 4); }
 template <int KMAX, int T>
 constexpr int stage_iters() { return (stage_pieces<KMAX, T>() + 255) / 256; }
 
-template <typename TIn, int KMAX, int T>
+// x rows of one head (64 elements each) are fetched with 16-byte loads:
+// xt_elems elements per lane, xt_rows rows per wave-wide load.
+template <typename TIn>
+constexpr int xt_elems() { return 16 / (int)sizeof(TIn); }
+template <typename TIn>
+constexpr int xt_rows() { return kWave * xt_elems<TIn>() / kP; }
+template <typename TIn, int XR>
+constexpr int xt_loads() { return (XR + xt_rows<TIn>() - 1) / xt_rows<TIn>(); }
+
+__device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void store16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
+
+// XR: rows of the x tile (>= k + T, a multiple of 4).
+template <typename TIn, int KMAX, int XR, int T>
 struct VerifyPre {
-    float xv[KMAX];   // x_j[prow], entry j < KL (clamped past it)
-    float xt[T];      // x_t[prow] of the drafts
-    float d;          // dt of entry `lane` (lane < KL), else 0
+    uint4 xw[xt_loads<TIn, XR>()];   // x rows j < KL: entry j < k from the buffer, else draft j - k
+    float d;                         // dt of entry `lane` (lane < KL), else 0
     typename io<TIn>::raw4 g[stage_iters<KMAX, T>()];   // Gram operand pieces
 };
 
-template <int KMAX, int T>
-struct VerifySmemF {
-    float G[KMAX + T][kN];   // rows 0..KL-1: B_j; rows KL..KL+T-1: C_t (fp32)
+template <typename TIn, int KMAX, int XR, int T>
+struct __align__(16) VerifySmemF {
+    float G[KMAX + T][kN];        // rows 0..KL-1: B_j; rows KL..KL+T-1: C_t (fp32)
     float gram[T][KMAX];
+    float cy[kMaxHpw][T][XR];     // per head: w_tj (B_j . C_t), zero for j > k + t
+    TIn X[kMaxHpw][XR][kP];       // per head: x rows as stored (rows >= KL unset)
 };
 
 // Gram operand piece q (4 elements): row q/32 of the staged rows.
@@ -437,21 +454,24 @@ __device__ __forceinline__ const TIn *stage_src(const VerifyIn &in, int q) {
     return p + col;
 }
 
-template <typename TIn, int KMAX, int T>
-__device__ __forceinline__ void verify_preload(const ReplayParams &a, const Slot &s, const VerifyIn &in, int prow,
-                                               VerifyPre<TIn, KMAX, T> &pre) {
+template <typename TIn, int KMAX, int XR, int T>
+__device__ __forceinline__ void verify_preload(const ReplayParams &a, const Slot &s, const VerifyIn &in,
+                                               VerifyPre<TIn, KMAX, XR, T> &pre) {
+    static_assert(XR % 4 == 0 && XR <= KMAX, "x tile rows");
     const int k = in.k;
     const TIn *xin = static_cast<const TIn *>(in.xin);
     const TIn *xb = static_cast<const TIn *>(in.xb);
+    const int lpr = kP / xt_elems<TIn>();
+    const int r0 = s.lane / lpr, col = xt_elems<TIn>() * (s.lane % lpr);
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        int t = j - k;
-        t = t < 0 ? 0 : (t > T - 1 ? T - 1 : t);
-        const TIn *px = (j < k) ? xb + (size_t)j * in.HP + prow : xin + (size_t)t * in.HP + prow;
-        pre.xv[j] = io<TIn>::load1(px);
+    for (int i = 0; i < xt_loads<TIn, XR>(); ++i) {
+        if (i * xt_rows<TIn>() < in.KL) {   // uniform: loads past the last row are skipped
+            int j = i * xt_rows<TIn>() + r0;
+            j = j < in.KL ? j : in.KL - 1;   // lanes past it repeat the last row
+            const TIn *px = (j < k) ? xb + (size_t)j * in.HP + col : xin + (size_t)(j - k) * in.HP + col;
+            pre.xw[i] = load16(px);
+        }
     }
-#pragma unroll
-    for (int t = 0; t < T; ++t) pre.xt[t] = io<TIn>::load1(xin + (size_t)t * in.HP + prow);
     pre.d = 0.f;
     if (s.lane < in.KL) {
         const TIn *pd = (s.lane < k) ? static_cast<const TIn *>(in.db) + (size_t)s.lane * a.H
@@ -467,11 +487,13 @@ __device__ __forceinline__ void verify_preload(const ReplayParams &a, const Slot
 }
 
 // Returns ybuf[t] = sum_{j < k+t+1} w_tj (B_j . C_t) x_j[prow] + D x_t[prow]
-// and lam[t] = Lambda_t (uniform across the wave).
-template <typename TIn, int KMAX, int T>
+// and lam[t] = Lambda_t (uniform across the wave).  The C_t rows stay in
+// sm.G[KL + t] for the caller.
+template <typename TIn, int KMAX, int XR, int T>
 __device__ __forceinline__ void verify_finish(const ReplayParams &a, const Slot &s, const VerifyIn &in,
-                                              const VerifyPre<TIn, KMAX, T> &pre, VerifySmemF<KMAX, T> &sm,
-                                              float (&ybuf)[T], float (&lam)[T]) {
+                                              const VerifyPre<TIn, KMAX, XR, T> &pre,
+                                              VerifySmemF<TIn, KMAX, XR, T> &sm, int prow, float (&ybuf)[T],
+                                              float (&lam)[T]) {
     const int k = in.k, KL = in.KL;
     const int nq = (KL + T) * (kN / 4);
 #pragma unroll
@@ -482,6 +504,15 @@ __device__ __forceinline__ void verify_finish(const ReplayParams &a, const Slot 
     // workgroups narrower than 256 threads stage the remaining pieces directly
     for (int q = threadIdx.x + stage_iters<KMAX, T>() * blockDim.x; q < nq; q += blockDim.x)
         *reinterpret_cast<float4 *>(&sm.G[q >> 5][4 * (q & 31)]) = io<TIn>::load4(stage_src<TIn>(in, q));
+    {
+        const int lpr = kP / xt_elems<TIn>();
+        const int r0 = s.lane / lpr, col = xt_elems<TIn>() * (s.lane % lpr);
+#pragma unroll
+        for (int i = 0; i < xt_loads<TIn, XR>(); ++i) {
+            const int j = i * xt_rows<TIn>() + r0;
+            if (i * xt_rows<TIn>() < KL && j < KL) store16(&sm.X[s.wave][j][col], pre.xw[i]);
+        }
+    }
     __syncthreads();
     {   // Gram g[t][j] = B_j . C_t, 16 lanes x 8 elements per dot
         const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4, ngrp = blockDim.x >> 4;
@@ -508,7 +539,6 @@ __device__ __forceinline__ void verify_finish(const ReplayParams &a, const Slot 
         tot += li;
         if (i > s.lane) suf += li;
     }
-    float cy[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         if (t > 0) {
@@ -518,20 +548,32 @@ __device__ __forceinline__ void verify_finish(const ReplayParams &a, const Slot 
             if (i > s.lane) suf += li;
         }
         lam[t] = expf(tot);
-        cy[t] = (s.lane < k + t + 1) ? pre.d * expf(suf) * sm.gram[t][s.lane < KMAX ? s.lane : 0] : 0.f;
+        const float cy = (s.lane < k + t + 1) ? pre.d * expf(suf) * sm.gram[t][s.lane < KMAX ? s.lane : 0] : 0.f;
+        if (s.lane < XR) sm.cy[s.wave][t][s.lane] = cy;
     }
+    __syncthreads();
+    // buffer part: x rows (broadcast across rows of the tile) times the
+    // coefficients (LDS broadcasts), entries in ascending order
+    float acc[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int Kt = k + t + 1;
-        float acc = Dh * pre.xt[t];
+    for (int t = 0; t < T; ++t) acc[t] = Dh * io<TIn>::load1(&sm.X[s.wave][k + t][prow]);
+    for (int j0 = 0; j0 < KL; j0 += 4) {
+        float xj[4];
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cy[t]), j));
-            const float term = cj * pre.xv[j];
-            acc += (j < Kt) ? term : 0.f;
+        for (int u = 0; u < 4; ++u) xj[u] = io<TIn>::load1(&sm.X[s.wave][j0 + u][prow]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const float4 c4 = *reinterpret_cast<const float4 *>(&sm.cy[s.wave][t][j0]);
+            const float cf[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float term = cf[u] * xj[u];
+                acc[t] += (j0 + u < k + t + 1) ? term : 0.f;   // later drafts never reach output t
+            }
         }
-        ybuf[t] = acc;
     }
+#pragma unroll
+    for (int t = 0; t < T; ++t) ybuf[t] = acc[t];
 }
 
 // Append the T drafts at entries k .. k+T-1 (the position is not advanced).
@@ -687,6 +729,34 @@ __device__ __forceinline__ void chunk_dots(const float4 (&cur)[kPerChunk], const
     }
 }
 
+// Dots of one chunk's 8 rows with the T vectors C4[t], each reduced over
+// the lane's half-wave down to the chunk value of the lane's row.
+template <int T>
+__device__ __forceinline__ void chunk_dots_1(const float4 (&cur)[kPerChunk], const float4 (&C4)[T], int lane,
+                                             float (&out)[T]) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        float v[kPerChunk];
+#pragma unroll
+        for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4[t]);
+        out[t] = chunk_reduce8(v, lane);
+    }
+}
+
+// The two stages of chunk_combine4 taken one pair at a time: combine_pair
+// closes lane bit 1 for chunks (0, 2) or (1, 3), combine_last closes lane
+// bit 0 on the two pair values.  Same additions as chunk_combine4.
+__device__ __forceinline__ float combine_pair(float ra, float rb, bool up) {
+    const float lo = ra + dpp<kDppQuadRev>(ra);
+    const float hi = rb + dpp<kDppQuadRev>(rb);
+    return up ? hi : lo;
+}
+__device__ __forceinline__ float combine_last(float p0, float p1, bool up) {
+    const float lo = p0 + dpp<kDppQuadSwap1>(p0);
+    const float hi = p1 + dpp<kDppQuadSwap1>(p1);
+    return up ? hi : lo;
+}
+
 // ------------------------------------------------------------------------
 // Deferred fold.  replayssm_accept_deferred only advances pos, so a slot can
 // hold K = pos >= L accepted entries; the next verify on the slot folds them
@@ -696,11 +766,14 @@ __device__ __forceinline__ void chunk_dots(const float4 (&cur)[kPerChunk], const
 // interval.  Same per-element arithmetic as a commit followed by a verify
 // at pos 0, so results are bit-identical to the eager accept.
 // ------------------------------------------------------------------------
-template <int KMAX, int T>
+template <int T>
+constexpr int fold_xrows() { return (T + 3) & ~3; }   // the drafts' x rows, rounded to 4
+
+template <typename TIn, int KMAX, int T>
 struct FoldSmem {
     float cs[kMaxHpw][kP * KMAX];   // commit coefficients (cs_index layout)
     float B[KMAX][kN];              // the group's B entries, zero past K
-    VerifySmemF<KMAX, T> v;         // the drafts' Gram operands and rows
+    VerifySmemF<TIn, KMAX, fold_xrows<T>(), T> v;   // the drafts' Gram operands and rows
 };
 
 // Commit coefficients of the K buffered entries, then the replay
@@ -708,16 +781,16 @@ struct FoldSmem {
 // positions 0..T-1 (token inputs as laid out for verify).  Returns Lambda_K.
 template <typename TIn, int KMAX, int T>
 __device__ __forceinline__ float fold_prologue(const ReplayParams &a, const Slot &s, int K, const VerifyIn &in,
-                                               FoldSmem<KMAX, T> &sm, float (&ybuf)[T], float (&lam)[T]) {
+                                               FoldSmem<TIn, KMAX, T> &sm, float (&ybuf)[T], float (&lam)[T]) {
     VerifyIn v = in;
     v.k = 0;
     v.KL = T;
-    VerifyPre<TIn, KMAX, T> pre;
-    verify_preload<TIn, KMAX, T>(a, s, v, s.prow, pre);
+    VerifyPre<TIn, KMAX, fold_xrows<T>(), T> pre;
+    verify_preload<TIn, KMAX, fold_xrows<T>(), T>(a, s, v, pre);
     stage_B<TIn, KMAX>(sm.B, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.bb), in.GN, K, K);
     typename io<TIn>::raw4 unused[KMAX];
     const float lamK = commit_prologue<TIn, KMAX, false>(a, s, K, nullptr, nullptr, sm.cs, unused);
-    verify_finish<TIn, KMAX, T>(a, s, v, pre, sm.v, ybuf, lam);
+    verify_finish<TIn, KMAX, fold_xrows<T>(), T>(a, s, v, pre, sm.v, s.prow, ybuf, lam);
     return lamK;
 }
 

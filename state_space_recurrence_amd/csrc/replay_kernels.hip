@@ -154,7 +154,7 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
 // ------------------------------------------------------------------------
 template <typename TIn, int KMAX, int T>
 __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
-    __shared__ VerifySmemF<KMAX, T> sm;
+    __shared__ VerifySmemF<TIn, KMAX, KMAX, T> sm;
 
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
@@ -163,31 +163,47 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
     float *sp = state_ptr(a.ckpt, s, a.H);
 
     // prologue loads first (they retire before the checkpoint chunks)
-    VerifyPre<TIn, KMAX, T> pre;
-    verify_preload<TIn, KMAX, T>(a, s, in, s.prow, pre);
-    float4 C4[T];
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-        C4[t] = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN + 4 * s.c);
+    VerifyPre<TIn, KMAX, KMAX, T> pre;
+    verify_preload<TIn, KMAX, KMAX, T>(a, s, in, pre);
     __builtin_amdgcn_sched_barrier(0);
+    // chunks in the order 0, 2, 1, 3: the first butterfly stage of the
+    // combine pairs chunk 0 with 2 and 1 with 3, so each pair closes as soon
+    // as its second chunk is reduced
     float4 buf[kNB][kPerChunk];
-#pragma unroll
-    for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
+    load_chunk(buf[0], sp, 0);
+    load_chunk(buf[1], sp, 2);
     __builtin_amdgcn_sched_barrier(0);
 
     float ybuf[T], lam[T];
-    verify_finish<TIn, KMAX, T>(a, s, in, pre, sm, ybuf, lam);
-
-    float r[T][kChunks];
+    verify_finish<TIn, KMAX, KMAX, T>(a, s, in, pre, sm, s.prow, ybuf, lam);
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-        float4 (&cur)[kPerChunk] = buf[c % kNB];
-        chunk_dots<T>(cur, C4, s.lane, r, c);
-        if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
+    for (int t = 0; t < T; ++t)   // uniform: keep it in a scalar register
+        lam[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, lam[t])));
+    float4 C4[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) C4[t] = *reinterpret_cast<const float4 *>(&sm.G[in.KL + t][4 * s.c]);
+
+    const bool up2 = (s.lane & 2) != 0;
+    float r0[T], p02[T], p13[T];
+    chunk_dots_1<T>(buf[0], C4, s.lane, r0);
+    load_chunk(buf[0], sp, 1);
+    {
+        float r2[T];
+        chunk_dots_1<T>(buf[1], C4, s.lane, r2);
+#pragma unroll
+        for (int t = 0; t < T; ++t) p02[t] = combine_pair(r0[t], r2[t], up2);
+    }
+    load_chunk(buf[1], sp, 3);
+    chunk_dots_1<T>(buf[0], C4, s.lane, r0);   // chunk 1
+    {
+        float r3[T];
+        chunk_dots_1<T>(buf[1], C4, s.lane, r3);
+#pragma unroll
+        for (int t = 0; t < T; ++t) p13[t] = combine_pair(r0[t], r3[t], up2);
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        const float y0 = chunk_combine4(r[t], s.lane);
+        const float y0 = combine_last(p02[t], p13[t], (s.lane & 1) != 0);
         a.y[((size_t)s.row * T + t) * in.HP + (size_t)s.h * kP + s.prow] = lam[t] * y0 + ybuf[t];
     }
     verify_append<TIn, T>(a, s, in);
@@ -200,7 +216,7 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
 // Launched only for layers that declare deferred commits.
 template <typename TIn, int KMAX, int T>
 __global__ void __launch_bounds__(256) replay_fold_verify_kernel(ReplayParams a) {
-    __shared__ FoldSmem<KMAX, T> sm;
+    __shared__ FoldSmem<TIn, KMAX, T> sm;
 
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
