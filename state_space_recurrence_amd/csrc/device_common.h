@@ -83,6 +83,22 @@ __device__ __forceinline__ void stream_store4(float *p, float4 v) {
     __builtin_nontemporal_store(u, reinterpret_cast<f4v *>(p));
 }
 
+// Buffer-resource form of the same accesses (raw buffer, stride 0): word 3
+// of the descriptor selects 32-bit data so the hardware range check applies;
+// cache-policy operand 2 is the non-temporal hint.
+constexpr int kBufferRsrcWord3 = 0x00020000;
+constexpr int kNonTemporal = 2;
+
+__device__ __forceinline__ float4 buffer_stream_load4(__amdgpu_buffer_rsrc_t r, int vo, int off) {
+    const f4v v = __builtin_amdgcn_raw_buffer_load_b128(r, vo, off, kNonTemporal);
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void buffer_stream_store4(__amdgpu_buffer_rsrc_t r, int vo, int off, float4 v) {
+    const f4v u = {v.x, v.y, v.z, v.w};
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, vo, off, kNonTemporal);
+}
+
 __device__ __forceinline__ float dot4(float4 a, float4 b) {
     return a.x * b.x + a.y * b.y + a.z * b.z + a.w * b.w;
 }

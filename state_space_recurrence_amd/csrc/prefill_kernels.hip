@@ -69,7 +69,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(ReplayParams a) {
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
     const int Tp = a.T;
-    float *sp = state_ptr(a.ckpt, s, a.H);
+    const HeadState sp = head_state(a.ckpt, s, a.H);
     float4 st[kChunks][kPerChunk];
     if (a.from_zero) {
 #pragma unroll
@@ -183,9 +183,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(ReplayParams a) {
         for (int c = 0; c < kChunks; ++c) advance_chunk(st[c], c, lamq, sm.cs[s.wave], sm.B, s.hf, Kr);
     }
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c)
-#pragma unroll
-        for (int m = 0; m < kPerChunk; ++m) stream_store4(sp + (size_t)chunk_index(c, m) * 2 * kN, st[c][m]);
+    for (int c = 0; c < kChunks; ++c) store_chunk(sp, c, st[c]);
     publish_position(a, s.b, 0, true);
 }
 

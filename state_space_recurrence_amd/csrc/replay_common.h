@@ -36,7 +36,7 @@ __device__ __forceinline__ Slot slot_at(const ReplayParams &a, int wg) {
     s.row = wg / a.wg_per_slot;
     s.tile = wg - s.row * a.wg_per_slot;
     s.b = slot_of_row(a, s.row);
-    s.wave = threadIdx.x >> 6;
+    s.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform: head math in scalar registers
     s.lane = threadIdx.x & 63;
     s.h = s.tile * a.hpw + s.wave;
     s.hpg = a.H / a.G;
@@ -51,16 +51,38 @@ __device__ __forceinline__ Slot slot_of(const ReplayParams &a) {
     return slot_at(a, xcd_remap(blockIdx.x, gridDim.x));
 }
 
-// Lane base pointer into head (b,h) of an fp32 state: row hf, columns 4c..;
-// value index i adds i * 2 rows.
-__device__ __forceinline__ float *state_ptr(float *base, const Slot &s, int H) {
-    return base + ((size_t)(s.b * H + s.h) * kP + s.hf) * kN + 4 * s.c;
+// Head (b,h) of an fp32 state (64 x 128, 32 KB) as a buffer resource: the
+// head's base address is wave-uniform and sits in scalar registers, the lane
+// adds one 32-bit byte offset (row hf, columns 4c..4c+3) and each row access
+// a constant offset (value index i adds i * 2 rows), so the 32 row accesses
+// of a lane share a single address register.  The hardware range check
+// confines every access to the head's 32 KB.
+struct HeadState {
+    __amdgpu_buffer_rsrc_t r;
+    int vo;
+};
+
+__device__ __forceinline__ HeadState head_state(float *base, const Slot &s, int H) {
+    float *hb = base + (size_t)(s.b * H + s.h) * kP * kN;
+    const uint64_t u = reinterpret_cast<uint64_t>(hb);   // uniform; pinned to scalar registers
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    HeadState hs;
+    hs.r = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0, kP * kN * 4,
+                                             kBufferRsrcWord3);
+    hs.vo = (s.hf * kN + 4 * s.c) * 4;
+    return hs;
 }
 
-__device__ __forceinline__ void load_chunk(float4 (&buf)[kPerChunk], const float *p, int c) {
+__device__ __forceinline__ int row_offset(int c, int m) { return chunk_index(c, m) * 2 * kN * 4; }
+
+__device__ __forceinline__ void load_chunk(float4 (&buf)[kPerChunk], const HeadState &hs, int c) {
 #pragma unroll
-    for (int m = 0; m < kPerChunk; ++m)
-        buf[m] = stream_load4(p + (size_t)chunk_index(c, m) * 2 * kN);
+    for (int m = 0; m < kPerChunk; ++m) buf[m] = buffer_stream_load4(hs.r, hs.vo, row_offset(c, m));
+}
+
+__device__ __forceinline__ void store_chunk(const HeadState &hs, int c, const float4 (&st)[kPerChunk]) {
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m) buffer_stream_store4(hs.r, hs.vo, row_offset(c, m), st[m]);
 }
 
 // Last-arriving workgroup of slot b publishes the slot's new position (and
@@ -86,47 +108,45 @@ __device__ __forceinline__ int cs_index(int hf, int c, int j, int m) {
     return ((hf * kChunks + c) * KMAX + j) * kPerChunk + m;
 }
 
-// Rewrite the 8 rows of chunk c in place:
-//   S_new[r] = lam * S0[r] + sum_j cs[r][j] * B_j[4c..4c+3]
-// (cs zero for j >= K).  Entry-outer order keeps one widened B_j slice and
-// 8 coefficients live at a time.
+// Stage the group's B entries 0..KMAX-1 of a commit into LDS as fp32 (the
+// workgroup's heads share one group): entries j < nbuf from the buffer, entry
+// nbuf (when < K) from the current input, entries >= K zero.  Visible after
+// the next __syncthreads.
 template <typename TIn, int KMAX>
-__device__ __forceinline__ void commit_chunk(float4 (&st)[kPerChunk], int c, float lam,
-                                             const float *cs, const typename io<TIn>::raw4 (&Bj)[KMAX],
-                                             int hf, float *dst) {
-#pragma unroll
-    for (int m = 0; m < kPerChunk; ++m) {
-        st[m].x *= lam; st[m].y *= lam; st[m].z *= lam; st[m].w *= lam;
+__device__ __forceinline__ void stage_B(float (*sB)[kN], const TIn *bb, const TIn *Bin, size_t GN, int nbuf,
+                                        int K) {
+#pragma unroll 4
+    for (int q = threadIdx.x; q < KMAX * kN / 4; q += blockDim.x) {
+        const int j = q / (kN / 4), n = 4 * (q - j * (kN / 4));
+        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (j < K) v = io<TIn>::load4((j < nbuf ? bb + (size_t)j * GN : Bin) + n);
+        *reinterpret_cast<float4 *>(&sB[j][n]) = v;
     }
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        const float4 b = io<TIn>::widen_here(Bj[j]);
-        const float *cp = cs + cs_index<KMAX>(hf, c, j, 0);
-        const float4 c0 = *reinterpret_cast<const float4 *>(cp);
-        const float4 c1 = *reinterpret_cast<const float4 *>(cp + 4);
-        const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-        for (int m = 0; m < kPerChunk; ++m) {
-            st[m].x += cf[m] * b.x;
-            st[m].y += cf[m] * b.y;
-            st[m].z += cf[m] * b.z;
-            st[m].w += cf[m] * b.w;
-        }
-        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound hoisted LDS reads
-    }
-#pragma unroll
-    for (int m = 0; m < kPerChunk; ++m)
-        stream_store4(dst + (size_t)chunk_index(c, m) * 2 * kN, st[m]);
 }
 
+// x rows of one head (64 elements each) are fetched with 16-byte loads:
+// xt_elems elements per lane, xt_rows rows per wave-wide load.
+template <typename TIn>
+constexpr int xt_elems() { return 16 / (int)sizeof(TIn); }
+template <typename TIn>
+constexpr int xt_rows() { return kWave * xt_elems<TIn>() / kP; }
+template <typename TIn, int XR>
+constexpr int xt_loads() { return (XR + xt_rows<TIn>() - 1) / xt_rows<TIn>(); }
+
+__device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
+__device__ __forceinline__ void store16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
 // ------------------------------------------------------------------------
 // Standard-step prologue: everything that does not read the checkpoint.
 // ------------------------------------------------------------------------
-template <int KMAX>
-struct StepSmem {
+template <typename TIn, int KMAX>
+struct __align__(16) StepSmem {
     float gram[KMAX];              // B_j . C  (one group per workgroup)
     float cs[kMaxHpw][kP * KMAX];  // commit coefficients w_j x_j[r] (cs_index layout)
+    union {
+        TIn X[kMaxHpw][KMAX][kP];  // prologue, per head: x rows of the K entries as stored (rows >= K unset)
+        float B[KMAX][kN];         // commit steps, after the prologue: the group's B entries, zero past K
+    } u;
 };
 
 struct StepIn {
@@ -163,13 +183,14 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
 }
 
 // Decay prep, Gram row, replay weights and the buffer part of the output for
-// row `prow` of this lane; on commit steps also the commit coefficients (LDS)
-// and this lane's B_j slices (columns 4c..4c+3, raw).  Returns Lambda_K in
-// *lam and sum_j w_j g_j x_j[prow] + D x[prow] in *ybuf.
-template <typename TIn, int KMAX, bool LOAD_BJ = true>
+// row `prow` of this lane; on commit steps also the commit coefficients
+// (sm.cs) and the group's B entries (sm.u.B, fp32).  Returns Lambda_K in
+// *lam and sum_j w_j g_j x_j[prow] + D x[prow] in *ybuf.  The head's x rows
+// arrive with a few 16-byte loads and are read back per row from LDS, so the
+// prologue holds few registers next to the checkpoint chunks in flight.
+template <typename TIn, int KMAX>
 __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot &s, const StepIn &in,
-                                              int prow, StepSmem<KMAX> &sm, float *lam, float *ybuf,
-                                              typename io<TIn>::raw4 (&Bj)[KMAX]) {
+                                              int prow, StepSmem<TIn, KMAX> &sm, float *lam, float *ybuf) {
     const int k = in.k, K = in.K;
     const TIn *xin = static_cast<const TIn *>(in.xin);
     const TIn *Bin = static_cast<const TIn *>(in.Bin);
@@ -178,13 +199,18 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
     const TIn *bb = static_cast<const TIn *>(in.bb);
     const TIn *db = static_cast<const TIn *>(in.db);
 
-    float xv[KMAX];   // x_j[prow] of every entry (entry k is the current token)
+    // x rows of entries 0..K-1 (entry k is the current token)
+    const int lpr = kP / xt_elems<TIn>();
+    const int r0 = s.lane / lpr, col = xt_elems<TIn>() * (s.lane % lpr);
+    uint4 xw[xt_loads<TIn, KMAX>()];
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        const TIn *px = (j < k) ? xb + (size_t)j * in.HP + prow : xin + prow;
-        xv[j] = io<TIn>::load1(px);
+    for (int i = 0; i < xt_loads<TIn, KMAX>(); ++i) {
+        if (i * xt_rows<TIn>() < K) {   // uniform: loads past the last row are skipped
+            int j = i * xt_rows<TIn>() + r0;
+            j = j < K ? j : K - 1;      // lanes past it repeat the last row
+            xw[i] = load16(j < k ? xb + (size_t)j * in.HP + col : xin + col);
+        }
     }
-    const float xcur = io<TIn>::load1(xin + prow);
     const float Ah = a.A[s.h], Dh = a.D[s.h];
 
     const float d = s.lane < K ? io<TIn>::load1((s.lane < k) ? db + (size_t)s.lane * a.H
@@ -199,6 +225,11 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
             const float acc = row16_sum(dot4(b0, c0) + dot4(b1, c1));
             if (t16 == 0) sm.gram[j] = acc;
         }
+    }
+#pragma unroll
+    for (int i = 0; i < xt_loads<TIn, KMAX>(); ++i) {
+        const int j = i * xt_rows<TIn>() + r0;
+        if (i * xt_rows<TIn>() < K && j < K) store16(&sm.u.X[s.wave][j][col], xw[i]);
     }
     __syncthreads();
 
@@ -216,12 +247,16 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
     const float wj = s.lane < K ? d * expf(suf) : 0.f;               // w_j in lane j, zero for j >= K
     const float cyj = s.lane < K ? wj * sm.gram[s.lane < KMAX ? s.lane : 0] : 0.f;   // w_j g_j
 
-    float yb = Dh * xcur;
+    const TIn *xrow = &sm.u.X[s.wave][0][prow];   // x_j[prow] at xrow[j * kP]
+    float yb = Dh * io<TIn>::load1(xrow + k * kP);
+    for (int j0 = 0; j0 < K; j0 += 4) {
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cyj), j));
-        const float term = cj * xv[j];
-        yb += (j < K) ? term : 0.f;   // select: entries beyond K never leak (even NaN)
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u;
+            const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cyj), j));
+            const float term = cj * io<TIn>::load1(xrow + j * kP);
+            yb += (j < K) ? term : 0.f;   // select: entries beyond K never leak (even NaN)
+        }
     }
     *ybuf = yb;
     if (in.commit) {
@@ -230,13 +265,11 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
 #pragma unroll
         for (int j = 0; j < KMAX; ++j) {
             const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
-            const float cf = w * xv[j];
+            const float cf = w * io<TIn>::load1(xrow + j * kP);
             sm.cs[s.wave][cs_index<KMAX>(hf, i & 3, j, i >> 2)] = (j < K) ? cf : 0.f;
-            if (LOAD_BJ) {
-                const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin;
-                Bj[j] = io<TIn>::load_raw4(pb + 4 * s.c);
-            }
         }
+        __syncthreads();   // every head is done with its x rows; B takes their place
+        stage_B<TIn, KMAX>(sm.u.B, bb, Bin, in.GN, k, K);
     }
     __syncthreads();
 }
@@ -260,22 +293,6 @@ __device__ __forceinline__ void step_append(const ReplayParams &a, const Slot &s
     }
 }
 
-
-// Stage the group's B entries 0..KMAX-1 of a commit into LDS as fp32 (the
-// workgroup's heads share one group): entries j < nbuf from the buffer, entry
-// nbuf (when < K) from the current input, entries >= K zero.  Visible after
-// the next __syncthreads.
-template <typename TIn, int KMAX>
-__device__ __forceinline__ void stage_B(float (*sB)[kN], const TIn *bb, const TIn *Bin, size_t GN, int nbuf,
-                                        int K) {
-#pragma unroll 4
-    for (int q = threadIdx.x; q < KMAX * kN / 4; q += blockDim.x) {
-        const int j = q / (kN / 4), n = 4 * (q - j * (kN / 4));
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j < K) v = io<TIn>::load4((j < nbuf ? bb + (size_t)j * GN : Bin) + n);
-        *reinterpret_cast<float4 *>(&sB[j][n]) = v;
-    }
-}
 
 // ------------------------------------------------------------------------
 // Speculative-verify prologue.
@@ -413,18 +430,6 @@ template <int KMAX, int T>
 constexpr int stage_pieces() { return (KMAX + T) * (kN / 4); }
 template <int KMAX, int T>
 constexpr int stage_iters() { return (stage_pieces<KMAX, T>() + 255) / 256; }
-
-// x rows of one head (64 elements each) are fetched with 16-byte loads:
-// xt_elems elements per lane, xt_rows rows per wave-wide load.
-template <typename TIn>
-constexpr int xt_elems() { return 16 / (int)sizeof(TIn); }
-template <typename TIn>
-constexpr int xt_rows() { return kWave * xt_elems<TIn>() / kP; }
-template <typename TIn, int XR>
-constexpr int xt_loads() { return (XR + xt_rows<TIn>() - 1) / xt_rows<TIn>(); }
-
-__device__ __forceinline__ uint4 load16(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
-__device__ __forceinline__ void store16(void *p, uint4 v) { *reinterpret_cast<uint4 *>(p) = v; }
 
 // XR: rows of the x tile (>= k + T, a multiple of 4).
 template <typename TIn, int KMAX, int XR, int T>
@@ -679,13 +684,14 @@ __device__ __forceinline__ float commit_prologue(const ReplayParams &a, const Sl
     return expf(tot);
 }
 
-// As commit_chunk, with the group's B entries staged in LDS (sB, zero past
+// Rewrite the 8 rows of chunk c in place, S_new[r] = lam S0[r] + sum_j
+// cs[r][j] B_j[4c..4c+3], with the group's B entries staged in LDS (sB, zero past
 // K) and the entry loop cut at Kr = K rounded up to 4, so a short fold does
 // not pay for KMAX entries.  `col` = 4c, laundered per chunk by the caller's
 // asm so the B_j reads are redone per chunk instead of held in registers.
 template <int KMAX>
 __device__ __forceinline__ void commit_chunk_lds(float4 (&st)[kPerChunk], int c, float lam, const float *cs,
-                                                 const float (*sB)[kN], int hf, int Kr, float *dst) {
+                                                 const float (*sB)[kN], int hf, int Kr, const HeadState &dst) {
 #pragma unroll
     for (int m = 0; m < kPerChunk; ++m) {
         st[m].x *= lam; st[m].y *= lam; st[m].z *= lam; st[m].w *= lam;
@@ -710,9 +716,7 @@ __device__ __forceinline__ void commit_chunk_lds(float4 (&st)[kPerChunk], int c,
             }
         }
     }
-#pragma unroll
-    for (int m = 0; m < kPerChunk; ++m)
-        stream_store4(dst + (size_t)chunk_index(c, m) * 2 * kN, st[m]);
+    store_chunk(dst, c, st);
 }
 
 // Partial sums of row pairs of one chunk against T vectors, reduce-scattered

@@ -34,20 +34,16 @@ namespace {
 // Commit steps stage the group's B entries in LDS instead of holding KMAX raw
 // slices per lane in registers (a commit happens once per interval; the
 // registers are held on every step).  With them out of the register budget
-// the 16-entry kernel fits 168 VGPRs, i.e. three waves per SIMD (measured
-// +5% over two waves with B in registers).
-template <int KMAX>
-constexpr bool kBInLds = true;
-
+// the 16-entry kernel runs three waves per SIMD (measured +5% over two waves
+// with B in registers).
 template <typename TIn, int KMAX>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KMAX == 16 ? 3 : 1)))
 replay_step_kernel(ReplayParams a) {
-    __shared__ StepSmem<KMAX> sm;
-    __shared__ float sB[kBInLds<KMAX> ? KMAX : 1][kN];
+    __shared__ StepSmem<TIn, KMAX> sm;
 
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
-    float *sp = state_ptr(a.ckpt, s, a.H);
+    const HeadState sp = head_state(a.ckpt, s, a.H);
 
     float4 buf[kNB][kPerChunk];
 #pragma unroll
@@ -56,11 +52,7 @@ replay_step_kernel(ReplayParams a) {
     const StepIn in = step_inputs<TIn>(a, s, a.kmax);
     const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
     float lam, ybuf;
-    typename io<TIn>::raw4 Bj[KMAX];
-    if (kBInLds<KMAX> && in.commit)   // visible after the prologue's barriers
-        stage_B<TIn, KMAX>(sB, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.Bin), in.GN, in.k,
-                           in.K);
-    step_prologue<TIn, KMAX, !kBInLds<KMAX>>(a, s, in, s.prow, sm, &lam, &ybuf, Bj);
+    step_prologue<TIn, KMAX>(a, s, in, s.prow, sm, &lam, &ybuf);
 
     float r[kChunks];
 #pragma unroll
@@ -70,12 +62,7 @@ replay_step_kernel(ReplayParams a) {
 #pragma unroll
         for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4);
         r[c] = chunk_reduce8(v, s.lane);
-        if (in.commit) {
-            if constexpr (kBInLds<KMAX>)
-                commit_chunk_lds<KMAX>(cur, c, lam, sm.cs[s.wave], sB, s.hf, (in.K + 3) & ~3, sp);
-            else
-                commit_chunk<TIn, KMAX>(cur, c, lam, sm.cs[s.wave], Bj, s.hf, sp);
-        }
+        if (in.commit) commit_chunk_lds<KMAX>(cur, c, lam, sm.cs[s.wave], sm.u.B, s.hf, (in.K + 3) & ~3, sp);
         if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
     }
     const float y0 = chunk_combine4(r, s.lane);
@@ -93,9 +80,8 @@ replay_step_kernel(ReplayParams a) {
 // ------------------------------------------------------------------------
 template <typename TIn, int KMAX>
 __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
-    __shared__ StepSmem<KMAX> sm;
+    __shared__ StepSmem<TIn, KMAX> sm;
     __shared__ float s_r[kChunks][kWave];
-    __shared__ float sB[kBInLds<KMAX> ? KMAX : 1][kN];
 
     Slot s;
     {
@@ -114,29 +100,20 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
     }
     if (s.b < 0) return;   // padding row
     const int q = s.wave;
-    float *sp = state_ptr(a.ckpt, s, a.H);
+    const HeadState sp = head_state(a.ckpt, s, a.H);
     float4 cur[kPerChunk];
     load_chunk(cur, sp, q);
 
     const StepIn in = step_inputs<TIn>(a, s, a.kmax);
     const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
     float lam, ybuf;
-    typename io<TIn>::raw4 Bj[KMAX];
-    if (kBInLds<KMAX> && in.commit)
-        stage_B<TIn, KMAX>(sB, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.Bin), in.GN, in.k,
-                           in.K);
-    step_prologue<TIn, KMAX, !kBInLds<KMAX>>(a, s, in, s.prow, sm, &lam, &ybuf, Bj);
+    step_prologue<TIn, KMAX>(a, s, in, s.prow, sm, &lam, &ybuf);
 
     float v[kPerChunk];
 #pragma unroll
     for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4);
     s_r[q][s.lane] = chunk_reduce8(v, s.lane);
-    if (in.commit) {
-        if constexpr (kBInLds<KMAX>)
-            commit_chunk_lds<KMAX>(cur, q, lam, sm.cs[s.wave], sB, s.hf, (in.K + 3) & ~3, sp);
-        else
-            commit_chunk<TIn, KMAX>(cur, q, lam, sm.cs[s.wave], Bj, s.hf, sp);
-    }
+    if (in.commit) commit_chunk_lds<KMAX>(cur, q, lam, sm.cs[s.wave], sm.u.B, s.hf, (in.K + 3) & ~3, sp);
     __syncthreads();
     if (q == 0) {
         float r[kChunks];
@@ -160,7 +137,7 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
     if (s.b < 0) return;   // padding row
     const VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
     if (in.k >= a.L) return;   // deferred fold: replay_fold_verify_kernel, launched next
-    float *sp = state_ptr(a.ckpt, s, a.H);
+    const HeadState sp = head_state(a.ckpt, s, a.H);
 
     // prologue loads first (they retire before the checkpoint chunks)
     VerifyPre<TIn, KMAX, KMAX, T> pre;
@@ -222,7 +199,7 @@ __global__ void __launch_bounds__(256) replay_fold_verify_kernel(ReplayParams a)
     if (s.b < 0) return;   // padding row
     VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
     if (in.k < a.L) return;
-    float *sp = state_ptr(a.ckpt, s, a.H);
+    const HeadState sp = head_state(a.ckpt, s, a.H);
     float4 buf[kNB][kPerChunk];
 #pragma unroll
     for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
@@ -266,7 +243,7 @@ __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
     bool commit;
     const int K = commit_count<ACCEPT>(a, s, &commit);
     if (commit) {
-        float *sp = state_ptr(a.ckpt, s, a.H);
+        const HeadState sp = head_state(a.ckpt, s, a.H);
         float4 buf[kNB][kPerChunk];
 #pragma unroll
         for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);

@@ -10,8 +10,7 @@ template <typename TIn, int KMAX, int MODE>
 __global__ void __launch_bounds__(256) split_step_kernel(ReplayParams a) {
     using MT = ModeTraits<MODE>;
     constexpr int UB = MT::ubits;
-    __shared__ StepSmem<KMAX> sm;
-    __shared__ float sB[KMAX][kN];   // the group's B entries, staged on commit steps
+    __shared__ StepSmem<TIn, KMAX> sm;
 
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
@@ -32,19 +31,15 @@ __global__ void __launch_bounds__(256) split_step_kernel(ReplayParams a) {
 
     const StepIn in = step_inputs<TIn>(a, s, a.L - 1);
     const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;
-    if (in.commit)
-        stage_B<TIn, KMAX>(sB, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.Bin), in.GN, in.k,
-                           in.K);
     float lam, ybuf;
-    typename io<TIn>::raw4 unused[KMAX];
-    step_prologue<TIn, KMAX, false>(a, s, in, prow, sm, &lam, &ybuf, unused);
+    step_prologue<TIn, KMAX>(a, s, in, prow, sm, &lam, &ybuf);
 
     if constexpr (MT::fp4_out) {
         float c8[1][8], y0[1];
         load_c8<TIn>(static_cast<const TIn *>(in.Cin), s.lane & 15, c8[0]);
         fp4_rows_dot<1>(o, c8, s.lane, y0);
         a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + prow] = lam * y0[0] + ybuf;
-        if (in.commit) commit_head<KMAX, MODE>(a, s, lam, sm.cs[s.wave], sB, interval);
+        if (in.commit) commit_head<KMAX, MODE>(a, s, lam, sm.cs[s.wave], sm.u.B, interval);
     } else {
         const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
         float r[kChunks];
@@ -62,7 +57,7 @@ __global__ void __launch_bounds__(256) split_step_kernel(ReplayParams a) {
 #pragma unroll
             for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(st[m], C4);
             r[q] = chunk_reduce8(v, s.lane);
-            if (in.commit) commit_chunk_q<KMAX, MODE>(a, s, st, q, lam, sm.cs[s.wave], sB, interval);
+            if (in.commit) commit_chunk_q<KMAX, MODE>(a, s, st, q, lam, sm.cs[s.wave], sm.u.B, interval);
         }
         const float y0 = chunk_combine4(r, s.lane);
         a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + prow] = lam * y0 + ybuf;
