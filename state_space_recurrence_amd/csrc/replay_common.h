@@ -777,7 +777,7 @@ template <typename TIn, int KMAX, int T>
 struct FoldSmem {
     float cs[kMaxHpw][kP * KMAX];   // commit coefficients (cs_index layout)
     float B[KMAX][kN];              // the group's B entries, zero past K
-    VerifySmemF<TIn, KMAX, fold_xrows<T>(), T> v;   // the drafts' Gram operands and rows
+    VerifySmemF<TIn, fold_xrows<T>(), fold_xrows<T>(), T> v;   // the drafts (entries 0..T-1): Gram operands, x rows
 };
 
 // Commit coefficients of the K buffered entries, then the replay
@@ -789,12 +789,13 @@ __device__ __forceinline__ float fold_prologue(const ReplayParams &a, const Slot
     VerifyIn v = in;
     v.k = 0;
     v.KL = T;
-    VerifyPre<TIn, KMAX, fold_xrows<T>(), T> pre;
-    verify_preload<TIn, KMAX, fold_xrows<T>(), T>(a, s, v, pre);
+    constexpr int FX = fold_xrows<T>();
+    VerifyPre<TIn, FX, FX, T> pre;
+    verify_preload<TIn, FX, FX, T>(a, s, v, pre);
     stage_B<TIn, KMAX>(sm.B, static_cast<const TIn *>(in.bb), static_cast<const TIn *>(in.bb), in.GN, K, K);
     typename io<TIn>::raw4 unused[KMAX];
     const float lamK = commit_prologue<TIn, KMAX, false>(a, s, K, nullptr, nullptr, sm.cs, unused);
-    verify_finish<TIn, KMAX, fold_xrows<T>(), T>(a, s, v, pre, sm.v, s.prow, ybuf, lam);
+    verify_finish<TIn, FX, FX, T>(a, s, v, pre, sm.v, s.prow, ybuf, lam);
     return lamK;
 }
 

@@ -200,28 +200,45 @@ __global__ void __launch_bounds__(256) replay_fold_verify_kernel(ReplayParams a)
     VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
     if (in.k < a.L) return;
     const HeadState sp = head_state(a.ckpt, s, a.H);
-    float4 buf[kNB][kPerChunk];
-#pragma unroll
-    for (int c = 0; c < kNB; ++c) load_chunk(buf[c], sp, c);
+    float4 buf[kNB][kPerChunk];   // chunks in the order 0, 2, 1, 3 (as in the verify kernel)
+    load_chunk(buf[0], sp, 0);
+    load_chunk(buf[1], sp, 2);
 
-    float4 C4[T];
+    float ybuf[T], lamt[T];
+    float lam = fold_prologue<TIn, KMAX, T>(a, s, in.k, in, sm, ybuf, lamt);
+    lam = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, lam)));
 #pragma unroll
     for (int t = 0; t < T; ++t)
-        C4[t] = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN + 4 * s.c);
-    float ybuf[T], lamt[T];
-    const float lam = fold_prologue<TIn, KMAX, T>(a, s, in.k, in, sm, ybuf, lamt);
-    const int Kr = (in.k + 3) & ~3;
-    float r[T][kChunks];
+        lamt[t] = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, lamt[t])));
+    float4 C4[T];   // the drafts' C rows, staged by the prologue (rows KL.. with KL = T)
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) {
-        float4 (&cur)[kPerChunk] = buf[c % kNB];
-        commit_chunk_lds<KMAX>(cur, c, lam, sm.cs[s.wave], sm.B, s.hf, Kr, sp);
-        chunk_dots<T>(cur, C4, s.lane, r, c);
-        if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
+    for (int t = 0; t < T; ++t) C4[t] = *reinterpret_cast<const float4 *>(&sm.v.G[T + t][4 * s.c]);
+    const int Kr = (in.k + 3) & ~3;
+    const bool up2 = (s.lane & 2) != 0;
+    float r0[T], p02[T], p13[T];
+    commit_chunk_lds<KMAX>(buf[0], 0, lam, sm.cs[s.wave], sm.B, s.hf, Kr, sp);
+    chunk_dots_1<T>(buf[0], C4, s.lane, r0);
+    load_chunk(buf[0], sp, 1);
+    {
+        float r2[T];
+        commit_chunk_lds<KMAX>(buf[1], 2, lam, sm.cs[s.wave], sm.B, s.hf, Kr, sp);
+        chunk_dots_1<T>(buf[1], C4, s.lane, r2);
+#pragma unroll
+        for (int t = 0; t < T; ++t) p02[t] = combine_pair(r0[t], r2[t], up2);
+    }
+    load_chunk(buf[1], sp, 3);
+    commit_chunk_lds<KMAX>(buf[0], 1, lam, sm.cs[s.wave], sm.B, s.hf, Kr, sp);
+    chunk_dots_1<T>(buf[0], C4, s.lane, r0);
+    {
+        float r3[T];
+        commit_chunk_lds<KMAX>(buf[1], 3, lam, sm.cs[s.wave], sm.B, s.hf, Kr, sp);
+        chunk_dots_1<T>(buf[1], C4, s.lane, r3);
+#pragma unroll
+        for (int t = 0; t < T; ++t) p13[t] = combine_pair(r0[t], r3[t], up2);
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-        const float y0 = chunk_combine4(r[t], s.lane);
+        const float y0 = combine_last(p02[t], p13[t], (s.lane & 1) != 0);
         a.y[((size_t)s.row * T + t) * in.HP + (size_t)s.h * kP + s.prow] = lamt[t] * y0 + ybuf[t];
     }
     in.k = 0;

@@ -239,17 +239,24 @@ __device__ __forceinline__ void commit_head(const ReplayParams &a, const Slot &s
     for (int q = 0; q < kNB; ++q)
 #pragma unroll
         for (int m = 0; m < kPerChunk; ++m) raw[q][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q, m), s.c);
+    // The commit body is too large for the chunk loop to be unrolled whole;
+    // the inner loop over the kNB buffers is, so every buffer index stays
+    // static (a dynamic index would move the buffers to scratch memory).
+#pragma nounroll
+    for (int q0 = 0; q0 < kChunks; q0 += kNB) {
 #pragma unroll
-    for (int q = 0; q < kChunks; ++q) {
-        float4 st[kPerChunk];
+        for (int qq = 0; qq < kNB; ++qq) {
+            const int q = q0 + qq;
+            float4 st[kPerChunk];
 #pragma unroll
-        for (int m = 0; m < kPerChunk; ++m) st[m] = decode_row4<UB>(raw[q % kNB][m]);
-        if (q + kNB < kChunks) {
+            for (int m = 0; m < kPerChunk; ++m) st[m] = decode_row4<UB>(raw[qq][m]);
+            if (q + kNB < kChunks) {
 #pragma unroll
-            for (int m = 0; m < kPerChunk; ++m)
-                raw[q % kNB][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q + kNB, m), s.c);
+                for (int m = 0; m < kPerChunk; ++m)
+                    raw[qq][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q + kNB, m), s.c);
+            }
+            commit_chunk_q<KMAX, MODE>(a, s, st, q, lam, cs, sB, interval);
         }
-        commit_chunk_q<KMAX, MODE>(a, s, st, q, lam, cs, sB, interval);
     }
 }
 
