@@ -418,7 +418,7 @@ __device__ __forceinline__ void verify_prologue(const ReplayParams &a, const Slo
 // ---- Split form of the verify prologue for the verify kernel.  Loads
 // retire in issue order, so a wave waiting for a load issued after the
 // checkpoint chunks also waits for those chunks: verify_preload issues every
-// prologue load (the head's x rows, dt, and the Gram operands B_j / C_t as
+// prologue load (the head's x rows, dt, A, D and the Gram operands B_j / C_t as
 // raw pieces) before the kernel starts the checkpoint stream, and
 // verify_finish consumes them through LDS: Gram rows, per-wave decay sums
 // (lane broadcasts), then the buffer part of the outputs from the staged x
@@ -435,7 +435,8 @@ constexpr int stage_iters() { return (stage_pieces<KMAX, T>() + 255) / 256; }
 template <typename TIn, int KMAX, int XR, int T>
 struct VerifyPre {
     uint4 xw[xt_loads<TIn, XR>()];   // x rows j < KL: entry j < k from the buffer, else draft j - k
-    float d;                         // dt of entry `lane` (lane < KL), else 0
+    TIn draw;                        // dt of entry min(lane, KL - 1) as stored (widened in verify_finish)
+    float Ah, Dh;                    // the head's A and D
     typename io<TIn>::raw4 g[stage_iters<KMAX, T>()];   // Gram operand pieces
 };
 
@@ -477,11 +478,13 @@ __device__ __forceinline__ void verify_preload(const ReplayParams &a, const Slot
             pre.xw[i] = load16(px);
         }
     }
-    pre.d = 0.f;
-    if (s.lane < in.KL) {
-        const TIn *pd = (s.lane < k) ? static_cast<const TIn *>(in.db) + (size_t)s.lane * a.H
-                                     : static_cast<const TIn *>(in.dtin) + (size_t)(s.lane - k) * a.H;
-        pre.d = io<TIn>::load1(pd);
+    pre.Ah = a.A[s.h];
+    pre.Dh = a.D[s.h];
+    {   // every lane loads (no branch around the load): lanes past the last entry repeat it
+        const int j = s.lane < in.KL ? s.lane : in.KL - 1;
+        const TIn *pd = (j < k) ? static_cast<const TIn *>(in.db) + (size_t)j * a.H
+                                : static_cast<const TIn *>(in.dtin) + (size_t)(j - k) * a.H;
+        pre.draw = *pd;
     }
     const int nq = (in.KL + T) * (kN / 4);
 #pragma unroll
@@ -536,8 +539,9 @@ __device__ __forceinline__ void verify_finish(const ReplayParams &a, const Slot 
     // Per wave (head): l_i = A dt_i lives in lane i.  Suffix sums
     // sum_{lane < i <= k+t} l_i and prefix sums sum_{i <= k+t} l_i grow in
     // ascending i, one entry per step, as the sequential loops add them.
-    const float Dh = a.D[s.h];
-    const float l = a.A[s.h] * pre.d;
+    const float Dh = pre.Dh;
+    const float d = s.lane < KL ? io<TIn>::load1(&pre.draw) : 0.f;   // dt of entry `lane`, 0 past the last
+    const float l = pre.Ah * d;
     float suf = 0.f, tot = 0.f;
     for (int i = 0; i <= k; ++i) {
         const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
@@ -553,7 +557,7 @@ __device__ __forceinline__ void verify_finish(const ReplayParams &a, const Slot 
             if (i > s.lane) suf += li;
         }
         lam[t] = expf(tot);
-        const float cy = (s.lane < k + t + 1) ? pre.d * expf(suf) * sm.gram[t][s.lane < KMAX ? s.lane : 0] : 0.f;
+        const float cy = (s.lane < k + t + 1) ? d * expf(suf) * sm.gram[t][s.lane < KMAX ? s.lane : 0] : 0.f;
         if (s.lane < XR) sm.cy[s.wave][t][s.lane] = cy;
     }
     __syncthreads();
