@@ -68,6 +68,16 @@ def split_bytes_per_token(fmt, H, G, P=64, N=128, L=16, in_bytes=2):
             + entry * (L - 1) / 2 + H * P * 4)
 
 
+def verify_bytes_per_slot(H, G, T, k, P=64, N=128, in_bytes=2, state_bytes=4):
+    """One verify of T draft positions for one slot in one layer at buffer
+    position k: checkpoint read once; the T drafts' x, B, C, dt read; their
+    x, B, dt appended at entries k..k+T-1; the k buffered entries read; T
+    outputs written (fp32).  No state is written."""
+    entry = (H * P + G * N + H) * in_bytes
+    cur = (H * P + 2 * G * N + H) * in_bytes
+    return H * P * N * state_bytes + T * (cur + entry + H * P * 4) + k * entry
+
+
 def recurrent_bytes_per_token(H, G, P=64, N=128, in_bytes=2, state_bytes=4):
     """Conventional step: state read + written every token, inputs read, y written."""
     return 2 * H * P * N * state_bytes + (H * P + 2 * G * N + H) * in_bytes + H * P * 4
@@ -483,6 +493,34 @@ def run_spec(rs, L, torch, synth, dev, stream, sh, log, rounds=64, warm=8):
            "replay_kept_tokens_per_s": kept / sec,
            "deferred_ms_per_round": dsec / rounds * 1e3,
            "deferred_kept_tokens_per_s": kept / dsec}
+    # verify kernel alone, in the state the rounds left (positions 0..L-1 after
+    # eager accepts): repeated verifies of one round's drafts change nothing
+    # but re-append the same entries.  Algorithmic bytes from the positions.
+    lay0 = layers[0]
+    for lay in layers:
+        rs.commit(lay["ls"])   # flush what the deferred rounds left; eager rounds from here
+    replay_rounds(0, 3)
+    ksum = int(lay0["ls"].pos.sum())
+    x, Bm, Cm, dt = lay0["in"]
+
+    def verifies(n):
+        for _ in range(n):
+            rc = L.replayssm_verify(ctypes.byref(lay0["desc"]), ctypes.byref(lay0["st"]), T, x[0].data_ptr(),
+                                    Bm[0].data_ptr(), Cm[0].data_ptr(), dt[0].data_ptr(), y.data_ptr(), sh)
+            if rc:
+                raise RuntimeError(L.replayssm_last_error().decode())
+
+    verifies(8)
+    vsec = min(t(verifies, 32) for _ in range(3)) / 32
+    vbytes = (w.batch * verify_bytes_per_slot(w.heads, w.groups, T, 0)
+              + ksum * (64 * w.heads + 128 * w.groups + w.heads) * 2)
+    out["verify_kernel"] = {"us_per_launch": vsec * 1e6, "bytes_per_launch": vbytes,
+                            "mean_pos": ksum / w.batch, "GBps": vbytes / vsec / 1e9,
+                            "frac_of_peak": vbytes / vsec / 1e9 / HBM_PEAK_GBS,
+                            "checkpoint_GBps": w.batch * w.heads * 64 * 128 * 4 / vsec / 1e9}
+    log(f"[bench] verify kernel (T={T}, batch {w.batch}, mean pos {ksum / w.batch:.1f}): "
+        f"{vsec * 1e6:.1f} us, {vbytes / 1e9:.3f} GB algorithmic = {vbytes / vsec / 1e9:.0f} GB/s "
+        f"({vbytes / vsec / 1e9 / HBM_PEAK_GBS:.3f} of peak)")
     # conventional: a pool of T+1 states per slot, one copy written per draft
     pools, sels = [], []
     for lay in layers:

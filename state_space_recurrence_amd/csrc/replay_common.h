@@ -212,20 +212,32 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
         }
     }
     const float Ah = a.A[s.h], Dh = a.D[s.h];
-
-    const float d = s.lane < K ? io<TIn>::load1((s.lane < k) ? db + (size_t)s.lane * a.H
-                                                            : static_cast<const TIn *>(in.dtin))
-                               : 0.f;
-    {   // Gram row g_j = B_j . C, 16 lanes x 8 elements per dot
+    // dt of entry `lane`: every lane loads (lanes past the last entry repeat
+    // it) and the value is widened and masked at its use, so no branch around
+    // the load makes the wave wait for it on the spot.
+    const int jd = s.lane < K ? s.lane : K - 1;
+    const TIn draw = *((jd < k) ? db + (size_t)jd * a.H : static_cast<const TIn *>(in.dtin));
+    {   // Gram row g_j = B_j . C, 16 lanes x 8 elements per dot; the first
+        // pass's operands are requested unconditionally with the other
+        // prologue loads (a group past the last entry re-reads it)
         const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4, ngrp = blockDim.x >> 4;
-        const float4 c0 = io<TIn>::load4(Cin + 8 * t16), c1 = io<TIn>::load4(Cin + 8 * t16 + 4);
-        for (int j = grp; j < K; j += ngrp) {
+        const typename io<TIn>::raw4 rc0 = io<TIn>::load_raw4(Cin + 8 * t16), rc1 = io<TIn>::load_raw4(Cin + 8 * t16 + 4);
+        const int j0 = grp < K ? grp : K - 1;
+        const TIn *pb0 = (j0 < k) ? bb + (size_t)j0 * in.GN : Bin;
+        const typename io<TIn>::raw4 rb0 = io<TIn>::load_raw4(pb0 + 8 * t16), rb1 = io<TIn>::load_raw4(pb0 + 8 * t16 + 4);
+        const float4 c0 = io<TIn>::widen(rc0), c1 = io<TIn>::widen(rc1);
+        {   // computed by every group (keeps the loads ahead), stored where grp < K
+            const float acc = row16_sum(dot4(io<TIn>::widen(rb0), c0) + dot4(io<TIn>::widen(rb1), c1));
+            if (grp < K && t16 == 0) sm.gram[grp] = acc;
+        }
+        for (int j = grp + ngrp; j < K; j += ngrp) {
             const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin;
             const float4 b0 = io<TIn>::load4(pb + 8 * t16), b1 = io<TIn>::load4(pb + 8 * t16 + 4);
             const float acc = row16_sum(dot4(b0, c0) + dot4(b1, c1));
             if (t16 == 0) sm.gram[j] = acc;
         }
     }
+    const float d = s.lane < K ? io<TIn>::load1(&draw) : 0.f;
 #pragma unroll
     for (int i = 0; i < xt_loads<TIn, KMAX>(); ++i) {
         const int j = i * xt_rows<TIn>() + r0;
