@@ -192,7 +192,8 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
 // interval (their outputs from the folded rows).  A commit: pos = 0, intv+1.
 // Launched only for layers that declare deferred commits.
 template <typename TIn, int KMAX, int T>
-__global__ void __launch_bounds__(256) replay_fold_verify_kernel(ReplayParams a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KMAX <= 24 ? 3 : 1)))
+replay_fold_verify_kernel(ReplayParams a) {
     __shared__ FoldSmem<TIn, KMAX, T> sm;
 
     const Slot s = slot_of(a);
@@ -368,14 +369,17 @@ hipError_t launch_replay_step(const ReplayParams &p0, bool in_bf16, hipStream_t 
     return hipGetLastError();
 }
 
-template <typename TIn, int KMAX>
+// The fold pass folds up to Lcap entries; its LDS (commit coefficients and B
+// per entry) is sized by FK = Lcap rounded up to 16, 24 or 32, which decides
+// how many of its workgroups fit on a CU (three at 24: a 20-entry buffer).
+template <typename TIn, int KMAX, int FK>
 static void launch_verify_t(const ReplayParams &p, dim3 grid, dim3 block, hipStream_t stream) {
     switch (p.T) {
 #define RSSM_VERIFY_CASE(TT)                                                                            \
     case TT:                                                                                            \
         hipLaunchKernelGGL((replay_verify_kernel<TIn, KMAX, TT>), grid, block, 0, stream, p);           \
         if (p.kmax >= p.L)                                                                              \
-            hipLaunchKernelGGL((replay_fold_verify_kernel<TIn, KMAX, TT>), grid, block, 0, stream, p);      \
+            hipLaunchKernelGGL((replay_fold_verify_kernel<TIn, FK, TT>), grid, block, 0, stream, p);        \
         break;
         RSSM_VERIFY_CASE(1)
         RSSM_VERIFY_CASE(2)
@@ -394,11 +398,14 @@ hipError_t launch_replay_verify(const ReplayParams &p, bool in_bf16, hipStream_t
     if (p.batch == 0) return hipSuccess;
     dim3 grid(p.batch * p.wg_per_slot), block(64 * p.hpw);
     if (p.Lcap <= 16) {
-        if (in_bf16) launch_verify_t<uint16_t, 16>(p, grid, block, stream);
-        else launch_verify_t<float, 16>(p, grid, block, stream);
+        if (in_bf16) launch_verify_t<uint16_t, 16, 16>(p, grid, block, stream);
+        else launch_verify_t<float, 16, 16>(p, grid, block, stream);
+    } else if (p.Lcap <= 24) {
+        if (in_bf16) launch_verify_t<uint16_t, 32, 24>(p, grid, block, stream);
+        else launch_verify_t<float, 32, 24>(p, grid, block, stream);
     } else {
-        if (in_bf16) launch_verify_t<uint16_t, 32>(p, grid, block, stream);
-        else launch_verify_t<float, 32>(p, grid, block, stream);
+        if (in_bf16) launch_verify_t<uint16_t, 32, 32>(p, grid, block, stream);
+        else launch_verify_t<float, 32, 32>(p, grid, block, stream);
     }
     return hipGetLastError();
 }
