@@ -410,10 +410,20 @@ hipError_t launch_replay_verify(const ReplayParams &p, bool in_bf16, hipStream_t
     return hipGetLastError();
 }
 
+// Entries a commit can fold: 16, 24, 32 or 64 (24 covers a 20-entry buffer:
+// its coefficients and B take 37 KB of LDS, four workgroups per CU).
+#define RSSM_COMMIT_KMAX_DISPATCH(N, CALL)             \
+    do {                                               \
+        if ((N) <= 16) { constexpr int KM_ = 16; CALL; } \
+        else if ((N) <= 24) { constexpr int KM_ = 24; CALL; } \
+        else if ((N) <= 32) { constexpr int KM_ = 32; CALL; } \
+        else { constexpr int KM_ = 64; CALL; }         \
+    } while (0)
+
 hipError_t launch_replay_commit(const ReplayParams &p, bool in_bf16, bool accept, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
     dim3 grid(p.batch * p.wg_per_slot), block(64 * p.hpw);
-    RSSM_KMAX_DISPATCH(p.Lcap, {
+    RSSM_COMMIT_KMAX_DISPATCH(p.Lcap, {
         if (in_bf16) {
             if (accept) hipLaunchKernelGGL((replay_commit_kernel<uint16_t, KM_, true>), grid, block, 0, stream, p);
             else hipLaunchKernelGGL((replay_commit_kernel<uint16_t, KM_, false>), grid, block, 0, stream, p);
