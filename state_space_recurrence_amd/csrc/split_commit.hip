@@ -14,8 +14,8 @@ __global__ void __launch_bounds__(256) split_commit_kernel(ReplayParams a) {
     if (s.b < 0) return;   // padding row
     bool commit;
     const int K = commit_count<ACCEPT>(a, s, &commit);
-    const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;
     if (commit) {
+        const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;   // read only where a commit needs it
         const size_t GN = (size_t)a.G * kN;
         const TIn *bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * GN + (size_t)s.g * kN;
         stage_B<TIn, KMAX>(sB, bb, bb, GN, K, K);

@@ -33,7 +33,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) s
     }
 
     const StepIn in = step_inputs<TIn>(a, s, a.L - 1);
-    const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;
+    // stream index of this step's commit, read on commit steps only: the
+    // value is uniform, and loaded unconditionally the wave waited for it
+    // right here, one memory latency ahead of the prologue's loads
+    const uint32_t interval = in.commit ? (uint32_t)a.intv[s.b] + 1u : 0u;
     float lam, ybuf;
     step_prologue<TIn, KMAX>(a, s, in, prow, sm, &lam, &ybuf);
 
