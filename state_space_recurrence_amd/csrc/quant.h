@@ -73,14 +73,27 @@ __device__ __forceinline__ uint32_t bf16_sr(float v, uint32_t r16) {
 }
 
 // ------------------------------------------------------------------- E4M3 --
+// Decoding uses gfx950's packed FP8 (OCP E4M3) -> f32 conversion with unit
+// scale: exact for every finite code (subnormals m * 2^-9 included, sign
+// kept).  The two NaN codes (S.1111.111) are mapped to the canonical quiet
+// NaN 0x7FC00000, whatever payload the conversion gives them.
+typedef float f2v_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float e4m3_nan_fix(uint32_t code8, float v) {
+    return ((code8 & 0x7Fu) == 0x7Fu) ? __uint_as_float(0x7FC00000u) : v;
+}
+
 __device__ __forceinline__ float e4m3_decode(uint32_t code8) {
-    const uint32_t s = (code8 & 0x80u) << 24;
-    const uint32_t e = (code8 >> 3) & 0xFu, m = code8 & 7u;
-    if (e == 0xFu && m == 7u) return __uint_as_float(0x7FC00000u);
-    float v;
-    if (e == 0) v = (float)m * 0.001953125f;                      // m * 2^-9
-    else v = __uint_as_float(((e + 120u) << 23) | (m << 20));     // 2^(e-7) * (1 + m/8)
-    return __uint_as_float(__float_as_uint(v) | s);
+    const f2v_t v = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(code8 & 0xFFu, 1.0f, false);
+    return e4m3_nan_fix(code8 & 0xFFu, v.x);
+}
+
+// The four codes of a dword (byte n -> component n).
+__device__ __forceinline__ float4 e4m3_decode4(uint32_t w) {
+    const f2v_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+    const f2v_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+    return make_float4(e4m3_nan_fix(w & 0xFFu, lo.x), e4m3_nan_fix((w >> 8) & 0xFFu, lo.y),
+                       e4m3_nan_fix((w >> 16) & 0xFFu, hi.x), e4m3_nan_fix(w >> 24, hi.y));
 }
 
 // Magnitude (fp32 bits, finite, < 448) -> (grid multiple k, quantum exponent

@@ -88,8 +88,7 @@ __device__ __forceinline__ float4 decode_row4(typename Raw4<UB>::T r) {
         return make_float4(bf16_decode(r.x & 0xFFFFu), bf16_decode(r.x >> 16), bf16_decode(r.y & 0xFFFFu),
                            bf16_decode(r.y >> 16));
     } else if constexpr (UB == 8) {
-        return make_float4(e4m3_decode(r & 0xFFu), e4m3_decode((r >> 8) & 0xFFu),
-                           e4m3_decode((r >> 16) & 0xFFu), e4m3_decode(r >> 24));
+        return e4m3_decode4(r);
     } else {
         const float s = e4m3_decode(r >> 16);
         return make_float4(e2m1_decode(r & 0xFu) * s, e2m1_decode((r >> 4) & 0xFu) * s,

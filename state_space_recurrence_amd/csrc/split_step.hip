@@ -6,11 +6,12 @@ namespace rssm {
 
 namespace {
 
-// Four waves per SIMD: the non-commit steps (all but one per interval) are
-// latency-bound and gain more from the occupancy than the commit path, which
-// holds the most registers, loses to the few values the limit moves out.
+// Four waves per SIMD (six for split E4M3): the non-commit steps (all but one
+// per interval) are latency-bound and gain more from the occupancy than the
+// commit path, which holds the most registers, loses to the values the limit
+// moves out (split E4M3 at six waves: +6% although its commit path spills).
 template <typename TIn, int KMAX, int MODE>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) split_step_kernel(ReplayParams a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE == kSplitE4M3 ? 6 : 4))) split_step_kernel(ReplayParams a) {
     using MT = ModeTraits<MODE>;
     constexpr int UB = MT::ubits;
     __shared__ StepSmem<TIn, KMAX> sm;
