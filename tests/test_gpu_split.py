@@ -266,3 +266,40 @@ def test_split_drift_ordering(rs):
     drift = {f: float((ys[f] - ref)[-w.interval:].norm() / ref[-w.interval:].norm()) for f in ys if f != "f32"}
     print("drift over the last interval:", drift)
     assert drift["split-bf16"] < drift["shared-fp4"]
+
+
+@pytest.mark.parametrize("fmt", ["low-e4m3", "split-e4m3", "shared-fp4"])
+def test_e4m3_decode_of_every_code(rs, fmt):
+    """Every E4M3 code (OCP E4M3FN: subnormals, signed zeros, 448, NaN) is
+    decoded exactly, compared with the oracle's decode table.  One step at
+    position 0 with x = 0, dt = 0 and C = e_0 outputs exactly the decoded
+    column 0 of each row of the output source (Lambda = exp(0) = 1, no
+    buffer term): for the single E4M3 checkpoint that is the stored code; for
+    the FP4 copy, element 0 holds E2M1 1.0 and the row's first block scale is
+    the code under test, so the output is the decoded scale."""
+    w = dataclasses.replace(synth.WORKLOADS["tiny"])
+    Bsz, H, G, P, N = w.batch, w.heads, w.groups, 64, 128
+    A, D = synth.layer_params(w, 0)
+    ls = rs.LayerState(Bsz, H, G, A, D, interval=w.interval, in_dtype=torch.float32, state_format=fmt,
+                       layer_id=LAYER, seed=SEED)
+    codes = (torch.arange(Bsz * H * P, dtype=torch.int64) % 256).to(torch.uint8).reshape(Bsz, H, P)
+    if fmt == "low-e4m3":
+        ls.ckpt.copy_(codes[..., None].expand(Bsz, H, P, N).contiguous().cuda())
+    else:
+        q = torch.zeros(Bsz, H, P, N // 2, dtype=torch.uint8)
+        q[..., 0] = 0x02                               # element 0: E2M1 code 2 = 1.0; the rest 0
+        sc = torch.full((Bsz, H, P, N // 32), 0x38, dtype=torch.uint8)   # 1.0 for the zero blocks
+        sc[..., 0] = codes
+        ls.out_q.copy_(q.cuda())
+        ls.out_scale.copy_(sc.cuda())
+    x = torch.zeros(Bsz, H, P, device="cuda")
+    Bm = torch.zeros(Bsz, G, N, device="cuda")
+    Cm = torch.zeros(Bsz, G, N, device="cuda")
+    Cm[..., 0] = 1.0
+    dt = torch.zeros(Bsz, H, device="cuda")
+    y = rs.step(ls, x, Bm, Cm, dt).cpu().double().numpy()
+    rs.check_device_errors(ls)
+    ref = oracle.e4m3_decode_array(codes.numpy())
+    assert np.array_equal(y, ref, equal_nan=True), (
+        f"{fmt}: codes decoded differently: {sorted(set(codes.numpy()[~np.isclose(y, ref, rtol=0, atol=0, equal_nan=True)].tolist()))[:16]}")
+    assert np.isnan(y).sum() == np.isnan(ref).sum() > 0
