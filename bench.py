@@ -679,7 +679,27 @@ def run_split(rs, L, torch, synth, dev, stream, sh, log, steps=256, warm=16, dri
         out[fmt] = {"tokens_per_s": w.batch * steps / sec, "ms_per_step": sec / steps * 1e3,
                     "bytes_per_token_layer": bpt,
                     "GBps_stack": bpt * w.batch * w.layers * steps / sec / 1e9}
-        log(f"[bench] {fmt}: {out[fmt]['tokens_per_s']:.0f} tok/s ({out[fmt]['GBps_stack']:.0f} GB/s)")
+        del layers
+        # staggered phases: slot b joins at step b % L (through the slot map),
+        # so 1/L of the slots commit on every step instead of all on one
+        layers = make(fmt)
+        for i in range(w.interval):
+            idx = torch.tensor([b for b in range(w.batch) if b % w.interval <= i], dtype=torch.int32, device=dev)
+            n = idx.numel()
+            for li, (ls, d, st) in enumerate(layers):
+                x, Bm, Cm, dt = ins[li]
+                rs.step(ls, x[i, :n], Bm[i, :n], Cm[i, :n], dt[i, :n], y=ys[li][:n], slots=idx)
+        loop(layers, w.interval, warm, ys)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        loop(layers, w.interval + warm, steps, ys)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ssec = e0.elapsed_time(e1) / 1e3
+        out[fmt]["staggered_tokens_per_s"] = w.batch * steps / ssec
+        out[fmt]["staggered_pos_distinct"] = int(layers[0][0].pos.unique().numel())
+        log(f"[bench] {fmt}: {out[fmt]['tokens_per_s']:.0f} tok/s ({out[fmt]['GBps_stack']:.0f} GB/s); "
+            f"staggered phases {out[fmt]['staggered_tokens_per_s']:.0f} tok/s")
         del layers
     # drift vs the fp32 trajectory, all formats stepped together on the same inputs
     def drift(tag):
