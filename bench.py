@@ -123,7 +123,7 @@ def main():
                                      "(batch 512, 4 drafts; eager and deferred commits) and its per-draft-copy "
                                      "baseline; prompt prefill (one 4B-class layer, batch 256, 256 tokens) "
                                      "against token-by-token decode; the precision split formats (batch 256, "
-                                     "4 layers) and their drift runs.  Kernel names carry <input type, max "
+                                     "4 layers; lock-step and staggered phases) and their drift runs.  Kernel names carry <input type, max "
                                      "buffer entries, ...> template arguments; split modes 0..4 = split-bf16, "
                                      "split-e4m3, shared-fp4, low-bf16, low-e4m3.")
         return
