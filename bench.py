@@ -97,6 +97,12 @@ def main():
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "RUN"),
                     help="write the kernel-trace summary of a rocprofv3 --kernel-trace --stats run "
                          "(RUN: 'headline' or 'all')")
+    ap.add_argument("--probe-verify", action="store_true",
+                    help="short fixed run for profiler counters of the verify kernel: the speculative "
+                         "layer (batch 512, 128 heads, 5 positions) after 3 eager rounds, 16 verify "
+                         "launches, then 3 plain 1 GiB device copies (calibration)")
+    ap.add_argument("--summarize-verify-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="write the verify kernel's counter summary from two --probe-verify runs")
     ap.add_argument("--probe", action="store_true",
                     help="short fixed run for profiler counters: 16 warm-up + 16 replay steps, "
                          "16 recurrent steps, then 3 plain 1 GiB device copies (calibration)")
@@ -126,6 +132,11 @@ def main():
                                      "4 layers; lock-step and staggered phases) and their drift runs.  Kernel names carry <input type, max "
                                      "buffer entries, ...> template arguments; split modes 0..4 = split-bf16, "
                                      "split-e4m3, shared-fp4, low-bf16, low-e4m3.")
+        return
+    if args.summarize_verify_counters:
+        cmd = ("rocprofv3 --pmc COUNTER -f csv -d gpurun_out/pmc_verify_COUNTER -o pmc -- "
+               "python -u bench.py --probe-verify")
+        summarize_verify_counters(*args.summarize_verify_counters, command=cmd)
         return
     if args.summarize_counters:
         cmd = ("rocprofv3 --pmc COUNTER -f csv -d gpurun_out/pmc_COUNTER -o pmc -- "
@@ -315,6 +326,9 @@ def main():
             f"{out['staggered']['step_us_median']:.0f}/{out['staggered']['step_us_max']:.0f} us")
         return out
 
+    if args.probe_verify:
+        probe_verify(rs, L, torch, synth, dev, stream, sh, log)
+        return
     if args.probe:
         layers = make_layers(w, args.batch, 32)
         y = [torch.empty(args.batch, w.heads, 64, device=dev) for _ in layers]
@@ -805,6 +819,115 @@ def summarize_trace(stats_csv: str, out_md: str, command: str, title: str, workl
         lines.append(f"| {short} | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | "
                      f"{float(r['MinNs'])/1e3:.1f} | {float(r['MaxNs'])/1e3:.1f} | {float(r['Percentage']):.1f}% |")
     lines.append("")
+    open(out_md, "w").write("\n".join(lines))
+    print("\n".join(lines))
+
+
+PROBE_VERIFY_ROUNDS = 3
+
+
+def probe_verify_positions(synth, w):
+    """Positions the probe's eager rounds leave (every slot starts at 0; an
+    accept that brings the count to L or more commits and resets it)."""
+    nk = synth.n_keep(w, PROBE_VERIFY_ROUNDS)
+    pos = [0] * w.batch
+    for r in range(PROBE_VERIFY_ROUNDS):
+        for b in range(w.batch):
+            k = pos[b] + int(nk[r, b])
+            pos[b] = 0 if k >= w.interval else k
+    return pos
+
+
+def probe_verify(rs, L, torch, synth, dev, stream, sh, log, launches=16):
+    """Counter probe of the verify kernel: layer 0 of the speculative
+    workload, PROBE_VERIFY_ROUNDS eager rounds (verify + accept), then
+    `launches` verifies of one round's drafts on that state (verify writes no
+    state, so every launch sees the same positions), then the calibration
+    copies."""
+    w = synth.WORKLOADS["spec"]
+    T = w.drafts + 1
+    A, D = synth.layer_params(w, 0, device=dev)
+    S0 = synth.init_state(w, 0, device=dev)
+    x, Bm, Cm, dt = synth.token_inputs(w, 0, PROBE_VERIFY_ROUNDS, device=dev, tokens=T)
+    bt = lambda t: t.transpose(1, 2).contiguous()
+    x, Bm, Cm, dt = bt(x), bt(Bm), bt(Cm), bt(dt)
+    # drawn on the host (the summary recomputes the positions from the same draws)
+    nk = synth.n_keep(w, PROBE_VERIFY_ROUNDS).to(dev)
+    ls = rs.LayerState(w.batch, w.heads, w.groups, A, D, interval=w.interval, max_draft=T,
+                       in_dtype=x.dtype, device=dev)
+    rs.load_checkpoint(ls, S0)
+    y = torch.empty(w.batch, T, w.heads, 64, device=dev)
+    for r in range(PROBE_VERIFY_ROUNDS):
+        rs.verify(ls, x[r], Bm[r], Cm[r], dt[r], y=y)
+        rs.accept(ls, nk[r], T)
+    torch.cuda.synchronize()
+    assert ls.pos.cpu().tolist() == probe_verify_positions(synth, w)
+    for _ in range(launches):
+        rs.verify(ls, x[0], Bm[0], Cm[0], dt[0], y=y)
+    rs.check_device_errors(ls)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] verify probe done: {PROBE_VERIFY_ROUNDS} eager rounds, {launches} verifies, 3 x 1 GiB copies")
+
+
+def summarize_verify_counters(fetch_csv: str, write_csv: str, out_md: str, command: str,
+                              launches: int = 16) -> None:
+    """Counter summary of the verify kernel from two `bench.py --probe-verify`
+    runs (FETCH_SIZE, then WRITE_SIZE): the last `launches` verify dispatches,
+    calibrated by the probe's 1 GiB copies, against the algorithmic bytes of
+    those launches (positions recomputed from the seeded accepted lengths)."""
+    import csv
+    import synth
+    copy_bytes = float(1 << 30)
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        cp = [r for r in rows if "copyBuffer" in r["Kernel_Name"]]
+        big = max(int(r["Grid_Size"]) for r in cp)      # the 1 GiB calibration copies (not small runtime copies)
+        copies = [float(r["Counter_Value"]) for r in cp if int(r["Grid_Size"]) == big]
+        ver = [float(r["Counter_Value"]) for r in rows if "replay_verify_kernel" in r["Kernel_Name"]]
+        return copies, ver[-launches:]
+
+    fc, fv = per_kernel(fetch_csv, "FETCH_SIZE")
+    wc, wv = per_kernel(write_csv, "WRITE_SIZE")
+    avg = lambda v: sum(v) / len(v)
+    fcal = copy_bytes / (avg(fc[-3:]) * 1024)
+    wcal = copy_bytes / (avg(wc[-3:]) * 1024)
+    f_v, w_v = avg(fv) * 1024 * fcal, avg(wv) * 1024 * wcal
+    w = synth.WORKLOADS["spec"]
+    T = w.drafts + 1
+    pos = probe_verify_positions(synth, w)
+    entry = (64 * w.heads + 128 * w.groups + w.heads) * 2
+    algo = w.batch * verify_bytes_per_slot(w.heads, w.groups, T, 0) + sum(pos) * entry
+    algo_w = w.batch * T * ((64 * w.heads + 128 * w.groups + w.heads) * 2 + w.heads * 64 * 4)
+    lines = [
+        "# HBM traffic counters: speculative verify kernel, 120B-class heads, batch 512, 5 positions",
+        "",
+        "Commands (from the repository root; one counter per run):",
+        "",
+        f"    {command.replace('COUNTER', 'FETCH_SIZE')}",
+        f"    {command.replace('COUNTER', 'WRITE_SIZE')}",
+        "",
+        f"`bench.py --probe-verify` runs {PROBE_VERIFY_ROUNDS} eager speculative rounds (verify + accept) on one",
+        "layer (batch 512, H=128, G=8, P=64, N=128, L=16, T=5, fp32 checkpoint, bf16 inputs), then",
+        f"{launches} verifies of one round's drafts on that state (mean buffer position "
+        f"{sum(pos) / w.batch:.2f}), then three plain 1 GiB device copies used as calibration.",
+        "",
+        "| quantity | FETCH_SIZE | WRITE_SIZE |",
+        "|---|---|---|",
+        f"| 1 GiB copy, counter KiB per dispatch | {avg(fc[-3:]):.0f} | {avg(wc[-3:]):.0f} |",
+        f"| calibration scale (known bytes / counter bytes) | {fcal:.4f} | {wcal:.4f} |",
+        f"| verify, scaled MB per launch (avg of {len(fv)}) | {f_v/1e6:.1f} | {w_v/1e6:.1f} |",
+        f"| verify, algorithmic MB per launch | {(algo - algo_w)/1e6:.1f} | {algo_w/1e6:.1f} |",
+        "",
+        f"Verify: measured {(f_v + w_v)/1e6:.1f} MB per launch vs algorithmic {algo/1e6:.1f} MB "
+        f"(ratio {(f_v + w_v)/algo:.3f}); no checkpoint bytes are written (WRITE = outputs and buffer "
+        "appends).",
+        "",
+    ]
     open(out_md, "w").write("\n".join(lines))
     print("\n".join(lines))
 
