@@ -19,8 +19,9 @@ state buffer", devotd.net; English edition sections 1-4):
                      and every interval checkpoint is the recurrence itself,
                      evaluated token by token.
 * codecs, Philox4x32-10 and stochastic rounding for the precision split
-  (section 4), and ``split_interval`` -- the split path's outputs and commit
-  taken step by step from the decoded checkpoints.
+  (section 4).  The split path's outputs and commits are the recurrence
+  replayed from the exactly decoded output copy / update checkpoint (the
+  tests anchor it on the stored bytes at each commit).
 
 The arithmetic lives in ``oracle.c`` (plain C, fp64); this module only
 marshals numpy arrays.  Inputs arrive as their stored values (fp32 or bf16)
@@ -243,4 +244,4 @@ def e4m3_decode_array(codes) -> np.ndarray:
     return _table("e4m3")[np.asarray(codes, dtype=np.uint8)]
 
 
-from .drivers import decode_run, spec_run, split_interval  # noqa: E402,F401
+from .drivers import decode_run, spec_run  # noqa: E402,F401

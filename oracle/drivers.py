@@ -9,9 +9,7 @@ state buffer", devotd.net) describes the method's life cycle:
   after its once-per-interval rewrite;
 * speculative decoding (section 3): rounds of T draft positions, only the
   accepted prefix of each round becomes part of the sequence; the position
-  count since the last checkpoint decides when the checkpoint is rewritten;
-* precision split (section 4): outputs are replayed from the decoded output
-  copy, the next checkpoint from the decoded update checkpoint.
+  count since the last checkpoint decides when the checkpoint is rewritten.
 """
 from __future__ import annotations
 
@@ -71,18 +69,3 @@ def spec_run(S0, x, Bm, Cm, dt, A, D, n_keep, groups: int, L: int, keep_states: 
             states.append(S.copy())
     return {"y": np.stack(ys), "pos": np.stack(poss), "commit": np.stack(commits),
             "state": states}
-
-
-def split_interval(U_dec, O_dec, x, Bm, Cm, dt, A, D, groups: int):
-    """One interval of the precision split, from decoded checkpoints.
-
-    U_dec: the decoded update checkpoint at the interval start;
-    O_dec: the decoded output copy at the interval start (for the shared
-           variant pass the same array twice).
-    x etc. hold the interval's tokens ([k, batch, ...]).
-
-    Returns (y [k, batch, H, P]: every output replayed from O_dec,
-             S_new: the state after the k tokens replayed from U_dec)."""
-    _, y = recurrent(O_dec, x, Bm, Cm, dt, A, D, groups)
-    S_new, _ = recurrent(U_dec, x, Bm, Cm, dt, A, D, groups)
-    return y, S_new

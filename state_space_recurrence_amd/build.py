@@ -77,6 +77,12 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
             raise RuntimeError(f"build failed: {' '.join(cmd)}\n{out}")
         if verbose and out.strip():
             print(out, flush=True)
+    # refuse device code in which a VALU op overwrites the data of a wide
+    # store before the store has read it (see isa_check)
+    from . import isa_check
+    nst = isa_check.check_objects([o for o in objs if o.endswith(".hip.o")], ARCH)
+    if verbose:
+        print(f"isa check: {nst} wide stores, no data hazards", flush=True)
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"], verbose)
     os.replace(LIB + ".tmp", LIB)
     if verbose:

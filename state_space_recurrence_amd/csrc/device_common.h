@@ -84,19 +84,31 @@ __device__ __forceinline__ void stream_store4(float *p, float4 v) {
 }
 
 // Buffer-resource form of the same accesses (raw buffer, stride 0): word 3
-// of the descriptor selects 32-bit data so the hardware range check applies;
-// cache-policy operand 2 is the non-temporal hint.
+// of the descriptor selects 32-bit data; cache-policy operand 2 is the
+// non-temporal hint.
 constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;
 
-__device__ __forceinline__ float4 buffer_stream_load4(__amdgpu_buffer_rsrc_t r, int vo, int off) {
-    const f4v v = __builtin_amdgcn_raw_buffer_load_b128(r, vo, off, kNonTemporal);
+// Load at byte offset vo + soff: vo in a VGPR (covered by the descriptor's
+// range check), soff a wave-uniform constant carried in the scalar offset
+// operand, which the range check does not cover -- callers keep vo + soff
+// inside the resource by construction.
+__device__ __forceinline__ float4 buffer_stream_load4(__amdgpu_buffer_rsrc_t r, int vo, int soff) {
+    const f4v v = __builtin_amdgcn_raw_buffer_load_b128(r, vo, soff, kNonTemporal);
     return make_float4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ void buffer_stream_store4(__amdgpu_buffer_rsrc_t r, int vo, int off, float4 v) {
+// Store at byte offset vo.  The whole offset is a VGPR operand (the scalar
+// offset is the constant 0), so the range check covers it and, more
+// importantly, the compiler's hazard model applies: a store of more than
+// 64 bits of data must be followed by wait states before any VALU op may
+// overwrite its data VGPRs, and LLVM waives that requirement when the
+// scalar offset operand is a register.  A build that let the next
+// instruction overwrite the data of a 128-bit store with an SGPR offset
+// wrote wrong values for exactly that store's rows.
+__device__ __forceinline__ void buffer_stream_store4(__amdgpu_buffer_rsrc_t r, int vo, float4 v) {
     const f4v u = {v.x, v.y, v.z, v.w};
-    __builtin_amdgcn_raw_buffer_store_b128(u, r, vo, off, kNonTemporal);
+    __builtin_amdgcn_raw_buffer_store_b128(u, r, vo, 0, kNonTemporal);
 }
 
 __device__ __forceinline__ float dot4(float4 a, float4 b) {

@@ -53,10 +53,13 @@ __device__ __forceinline__ Slot slot_of(const ReplayParams &a) {
 
 // Head (b,h) of an fp32 state (64 x 128, 32 KB) as a buffer resource: the
 // head's base address is wave-uniform and sits in scalar registers, the lane
-// adds one 32-bit byte offset (row hf, columns 4c..4c+3) and each row access
-// a constant offset (value index i adds i * 2 rows), so the 32 row accesses
-// of a lane share a single address register.  The hardware range check
-// confines every access to the head's 32 KB.
+// adds one 32-bit byte offset vo (row hf, columns 4c..4c+3) and each row
+// access a constant offset (value index i adds i * 2 rows).  Loads carry the
+// row offset in the scalar offset operand, so the 32 row loads of a lane
+// share a single address register; the hardware range check does not cover
+// that operand, and vo + row offset <= 32 KB - 16 holds by construction
+// (0 <= vo <= 1008, row offsets 0..31744).  Stores (commits only) put the
+// row offset into the vector operand (see buffer_stream_store4).
 struct HeadState {
     __amdgpu_buffer_rsrc_t r;
     int vo;
@@ -82,7 +85,7 @@ __device__ __forceinline__ void load_chunk(float4 (&buf)[kPerChunk], const HeadS
 
 __device__ __forceinline__ void store_chunk(const HeadState &hs, int c, const float4 (&st)[kPerChunk]) {
 #pragma unroll
-    for (int m = 0; m < kPerChunk; ++m) buffer_stream_store4(hs.r, hs.vo, row_offset(c, m), st[m]);
+    for (int m = 0; m < kPerChunk; ++m) buffer_stream_store4(hs.r, hs.vo + row_offset(c, m), st[m]);
 }
 
 // Last-arriving workgroup of slot b publishes the slot's new position (and

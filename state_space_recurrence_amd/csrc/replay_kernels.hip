@@ -90,7 +90,7 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
         s.tile = wg - s.row * a.H;
         s.b = slot_of_row(a, s.row);
         s.h = s.tile;
-        s.wave = threadIdx.x >> 6;     // = the chunk this wave streams
+        s.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // = the chunk this wave streams (uniform)
         s.lane = threadIdx.x & 63;
         s.hpg = a.H / a.G;
         s.g = s.h / s.hpg;

@@ -73,3 +73,34 @@ def test_long_interval_bf16_head_layout(rs):
     rs.commit(ls)   # flush the 5-token tail
     S_end, _ = oracle.recurrent(S0, x, Bm, Cm, dt, A, D, w.groups)
     assert_close(ls.ckpt.cpu(), S_end, "flushed state")
+
+
+@pytest.mark.parametrize("L", [32, 64])
+def test_long_interval_bf16_head_tile(rs, L):
+    """The head-tile step instances the interval sweep times (bf16 inputs,
+    4B-class heads): 24 slots x 24 workgroups of 4 heads = 576 workgroups,
+    above the row-split threshold, so replay_step_kernel<bf16, 32/64> runs.
+    Every output of three slots and their checkpoint after every interval
+    against the oracle."""
+    w = dataclasses.replace(synth.WORKLOADS["4b"], interval=L)
+    batch, steps = 24, 2 * L + 5
+    A, D = synth.layer_params(w, 2)
+    S0 = synth.init_state(w, 2, batch=batch)
+    x, Bm, Cm, dt = synth.token_inputs(w, 2, steps, batch=batch, stream=13)
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=L, in_dtype=x.dtype)
+    rs.load_checkpoint(ls, S0.cuda())
+    sl = [0, 11, batch - 1]
+    xs, Bs, Cs, ds = (t.cuda() for t in (x, Bm, Cm, dt))
+    ys, cks = [], []
+    for t in range(steps):
+        ys.append(rs.step(ls, xs[t], Bs[t], Cs[t], ds[t])[sl].cpu())
+        if (t + 1) % L == 0:
+            cks.append(ls.ckpt[sl].cpu())
+    rs.check_device_errors(ls)
+    y_ref, ck_ref = oracle.decode_run(S0[sl], x[:, sl], Bm[:, sl], Cm[:, sl], dt[:, sl], A, D, w.groups, L)
+    for t in range(steps):
+        assert_close(ys[t], y_ref[t], f"y step {t} (L={L}, head tile)")
+    assert len(cks) == len(ck_ref) == 2
+    for i, (c, r) in enumerate(zip(cks, ck_ref)):
+        assert_close(c, r, f"checkpoint after interval {i} (L={L}, head tile)")
+    assert ls.pos.cpu().tolist() == [5] * batch

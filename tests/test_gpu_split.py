@@ -303,3 +303,80 @@ def test_e4m3_decode_of_every_code(rs, fmt):
     assert np.array_equal(y, ref, equal_nan=True), (
         f"{fmt}: codes decoded differently: {sorted(set(codes.numpy()[~np.isclose(y, ref, rtol=0, atol=0, equal_nan=True)].tolist()))[:16]}")
     assert np.isnan(y).sum() == np.isnan(ref).sum() > 0
+
+
+def _quant_bytes(ls):
+    """Stored bytes of every slot: update checkpoint (if any), FP4 codes, scales."""
+    return [t.cpu().clone() for t in (ls.ckpt, ls.out_q, ls.out_scale) if t is not None]
+
+
+@pytest.mark.parametrize("fmt", SPLIT_FORMATS)
+def test_split_decode_staggered_phases(rs, fmt):
+    """Continuous batching: slot b joins at step b mod L through the slot
+    map (rows in reverse slot order), so after the first interval every step
+    carries committing and non-committing slots in one launch.  Teacher
+    forced per slot: each output from the oracle replaying the slot's tokens
+    since its last commit from the decoded output source; each commit's
+    pre-rounding values from the decoded update source; the committing
+    slots' bytes bit-exact against the oracle's quantisation of those values
+    with the slot's own interval index and element offset; every other
+    slot's bytes unchanged."""
+    w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
+    L, batch = w.interval, 20
+    steps = 2 * L + 6
+    A, D = synth.layer_params(w, 2)
+    S0 = synth.init_state(w, 2, batch=batch)
+    x, Bm, Cm, dt = synth.token_inputs(w, 2, steps, batch=batch, stream=5)
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=L, in_dtype=x.dtype, state_format=fmt,
+                       seed=SEED, layer_id=LAYER, debug_prequant=True)
+    rs.load_checkpoint(ls, S0.cuda())
+    out_src, upd_src = _sources(fmt, ls)
+    hist = [[] for _ in range(batch)]
+    joined = [b % L for b in range(batch)]
+    elems = w.heads * 64 * 128
+    n_commits = 0
+    for t in range(steps):
+        rows = [b for b in range(batch) if joined[b] <= t][::-1]
+        idx = torch.tensor(rows, dtype=torch.int32, device="cuda")
+        before = _quant_bytes(ls)
+        y = rs.step(ls, x[t, rows].cuda(), Bm[t, rows].cuda(), Cm[t, rows].cuda(), dt[t, rows].cuda(),
+                    slots=idx).cpu()
+        committed = [b for b in rows if len(hist[b]) == L - 1]
+        after = _quant_bytes(ls)
+        if committed:
+            dump = ls.debug_prequant.cpu()
+            out_next, upd_next = _sources(fmt, ls)
+            intv = ls.intv.cpu()
+        for r, b in enumerate(rows):
+            hist[b].append(t)
+            tt = hist[b]
+            sel = lambda a: a[tt, b:b + 1]
+            _, yref = oracle.recurrent(out_src[b:b + 1], sel(x), sel(Bm), sel(Cm), sel(dt), A, D, w.groups)
+            assert_close(y[r], yref[-1, 0], f"{fmt} y of slot {b} at step {t}")
+        for b in range(batch):
+            if b not in committed:
+                for k, (u, v) in enumerate(zip(before, after)):
+                    assert torch.equal(u[b], v[b]), f"{fmt}: bytes {k} of non-committing slot {b} changed at step {t}"
+                continue
+            tt = hist[b]
+            sel = lambda a: a[tt, b:b + 1]
+            S_new, _ = oracle.recurrent(upd_src[b:b + 1], sel(x), sel(Bm), sel(Cm), sel(dt), A, D, w.groups)
+            assert_close(dump[b:b + 1], S_new, f"{fmt} commit values of slot {b} at step {t}")
+            v = dump[b].numpy().astype(np.float32)
+            if _ufmt(fmt):
+                ref = oracle.sr_quantize(v.reshape(-1), _ufmt(fmt), SEED, LAYER, int(intv[b]), elem0=b * elems)
+                got = ls.ckpt[b].cpu().numpy().reshape(-1)
+                got = got.view(np.uint16) if _ufmt(fmt) == "bf16" else got
+                assert np.array_equal(got, ref), f"{fmt} update bytes of slot {b} at step {t}"
+            if fmt.startswith("split") or fmt == "shared-fp4":
+                codes, scales = oracle.fp4_quantize(v)
+                assert np.array_equal(ls.out_q[b].cpu().numpy(), codes), f"{fmt} FP4 codes of slot {b}"
+                assert np.array_equal(ls.out_scale[b].cpu().numpy(), scales), f"{fmt} FP4 scales of slot {b}"
+            out_src[b], upd_src[b] = out_next[b], upd_next[b]
+            hist[b] = []
+            n_commits += 1
+        exp_pos = np.array([len(h) for h in hist], dtype=np.int32)
+        assert np.array_equal(ls.pos.cpu().numpy(), exp_pos), f"positions after step {t}"
+    rs.check_device_errors(ls)
+    assert n_commits == sum((steps - j) // L for j in joined)
+    assert ls.intv.cpu().tolist() == [(steps - joined[b]) // L for b in range(batch)]
