@@ -291,9 +291,13 @@ int replayssm_check_device_errors(const rssm_state *st, int32_t n_slots, hipStre
  * Diagnostic: stream `bytes` (a multiple of 16) through HBM with the same
  * 16-byte non-temporal accesses as the state-streaming kernels, so callers
  * can time the practical ceiling next to the kernels' achieved bandwidth.
- * mode 0 = read src (dst receives grid*256 floats of partial sums and must
- * hold that many), mode 1 = copy src -> dst (both `bytes` long).  grid
- * workgroups of 256 threads in a grid-stride loop.  Asynchronous on stream.
+ * mode 0 = read src with 8 independent loads in flight per thread (dst
+ * receives grid*256 floats of partial sums and must hold that many);
+ * mode 1 = copy src -> dst (both `bytes` long), same depth; mode 2 = read
+ * src as 32 KB blocks, one per wave, 16 loads in flight per lane (the step
+ * kernel's shape; `bytes` a multiple of 32768; dst as for mode 0).  grid
+ * workgroups of 256 threads in a grid-stride loop.  Asynchronous on stream;
+ * RSSM_E_ARG for a bad mode, size or grid.
  */
 int replayssm_hbm_probe(int32_t mode, const void *src, void *dst, size_t bytes, int32_t grid,
                         hipStream_t stream);

@@ -87,12 +87,20 @@ def lib():
         L.oracle_sr_quantize.restype = None
         L.oracle_num_threads.argtypes = []
         L.oracle_num_threads.restype = ctypes.c_int
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        L.oracle_set_num_threads.restype = None
         _LIB = L
     return _LIB
 
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """OpenMP threads for later oracle calls (the parallel loops run over
+    independent (slot, head) pairs, so results do not depend on it)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 def _f64(a) -> np.ndarray:

@@ -56,6 +56,16 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads of the following parallel regions (timing on 1 core vs all). */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------------------ */
 /* Conventional per-token recurrence (the definition).                      */
 /* ------------------------------------------------------------------------ */

@@ -410,9 +410,11 @@ int replayssm_check_device_errors(const rssm_state *st, int32_t n_slots, hipStre
 
 int replayssm_hbm_probe(int32_t mode, const void *src, void *dst, size_t bytes, int32_t grid,
                         hipStream_t stream) {
-    if (mode != 0 && mode != 1) return fail(RSSM_E_ARG, "hbm_probe: mode must be 0 (read) or 1 (copy)");
+    if (mode < 0 || mode > 2)
+        return fail(RSSM_E_ARG, "hbm_probe: mode must be 0 (read), 1 (copy) or 2 (read, 32 KB per wave)");
     if (!src || !dst) return fail(RSSM_E_ARG, "hbm_probe: NULL buffer");
     if (bytes % 16 != 0 || bytes == 0) return fail(RSSM_E_ARG, "hbm_probe: bytes must be a positive multiple of 16");
+    if (mode == 2 && bytes % 32768 != 0) return fail(RSSM_E_ARG, "hbm_probe: mode 2 needs a multiple of 32 KB");
     if (grid < 1 || grid > (1 << 20)) return fail(RSSM_E_ARG, "hbm_probe: grid outside 1..2^20");
     return hip_status(rssm::launch_probe(mode, static_cast<const float *>(src), static_cast<float *>(dst), bytes,
                                          grid, stream),
