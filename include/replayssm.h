@@ -168,6 +168,24 @@ int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x,
                    hipStream_t stream);
 
 /*
+ * replayssm_step without the caller's arrival counters, for callers that
+ * cannot allocate device memory at any point (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  Same arguments,
+ * kernels and results as replayssm_step (bit-identical outputs and state),
+ * but the per-slot arrival counters live in library scratch: a device array
+ * of 65536 counters (256 KB) per GPU, set up on the first call on that
+ * device and held until the process ends.  Of st->work only the sticky
+ * error word work[n_slots] is used (read it with
+ * replayssm_check_device_errors as usual).  Calls nothing that allocates.
+ * Every call on one GPU shares that GPU's counters: calls that overlap on
+ * one GPU (different streams, different layers) race and must be ordered by
+ * the caller.  Returns RSSM_E_CAPACITY when the state holds more than 65536
+ * slots, RSSM_E_HIP if the scratch cannot be set up.
+ */
+int replayssm_step_noalloc(const rssm_desc *desc, const rssm_state *st, const void *x,
+                           const void *B, const void *C, const void *dt, float *y, hipStream_t stream);
+
+/*
  * Speculative verification (article section 3): T draft positions per slot
  * are appended at buffer entries pos .. pos+T-1 and the outputs of all T
  * positions are produced from the checkpoint and the buffer; no state is

@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         i32 = ctypes.c_int32
         L.replayssm_step.argtypes = [_DP, _SP, _vp, _vp, _vp, _vp, _vp, _vp]
+        L.replayssm_step_noalloc.argtypes = [_DP, _SP, _vp, _vp, _vp, _vp, _vp, _vp]
         L.replayssm_verify.argtypes = [_DP, _SP, i32, _vp, _vp, _vp, _vp, _vp, _vp]
         L.replayssm_accept.argtypes = [_DP, _SP, _vp, i32, _vp]
         L.replayssm_accept_deferred.argtypes = [_DP, _SP, _vp, i32, _vp]
@@ -91,7 +92,7 @@ def lib() -> ctypes.CDLL:
         L.replayssm_version.restype = ctypes.c_char_p
         L.replayssm_hbm_probe.argtypes = [i32, _vp, _vp, ctypes.c_size_t, i32, _vp]
         L.replayssm_hbm_probe.restype = ctypes.c_int
-        for name in ("replayssm_step", "replayssm_verify", "replayssm_accept", "replayssm_accept_deferred",
+        for name in ("replayssm_step", "replayssm_step_noalloc", "replayssm_verify", "replayssm_accept", "replayssm_accept_deferred",
                      "replayssm_commit", "replayssm_prefill",
                      "replayssm_load_checkpoint", "replayssm_recurrent_step",
                      "replayssm_recurrent_verify", "replayssm_recurrent_accept",
@@ -251,6 +252,19 @@ def step(ls: LayerState, x, B, C, dt, y=None, stream=None, slots=None) -> torch.
         y = torch.empty(rows, ls.heads, ls.head_dim, dtype=torch.float32, device=x.device)
     _check(lib().replayssm_step(ctypes.byref(d), ctypes.byref(st), _ptr(x), _ptr(B), _ptr(C),
                                 _ptr(dt), _ptr(y), _stream(stream)))
+    return y
+
+
+def step_noalloc(ls: LayerState, x, B, C, dt, y=None, stream=None, slots=None) -> torch.Tensor:
+    """replayssm_step_noalloc: the same step with the per-slot arrival
+    counters in library scratch (nothing allocated; `y` must be given by
+    callers that cannot allocate)."""
+    d, st, rows = _ctx(ls, slots)
+    _check_inputs(ls, x, B, C, dt, rows=rows)
+    if y is None:
+        y = torch.empty(rows, ls.heads, ls.head_dim, dtype=torch.float32, device=x.device)
+    _check(lib().replayssm_step_noalloc(ctypes.byref(d), ctypes.byref(st), _ptr(x), _ptr(B), _ptr(C),
+                                        _ptr(dt), _ptr(y), _stream(stream)))
     return y
 
 

@@ -131,6 +131,7 @@ rssm::ReplayParams replay_params(const rssm_desc *d, const rssm_state *s) {
     p.pos = s->pos;
     p.intv = s->intv;
     p.work = s->work;
+    p.err = s->work + nslots_of(d);
     p.A = s->A;
     p.D = s->D;
     p.batch = d->batch;
@@ -180,6 +181,28 @@ int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x, c
     if (desc->batch == 0) return RSSM_OK;
     if (!x || !B || !C || !dt || !y) return fail(RSSM_E_ARG, "step: an input/output pointer is NULL");
     rssm::ReplayParams p = replay_params(desc, st);
+    p.x = x;
+    p.Bm = B;
+    p.Cm = C;
+    p.dt = dt;
+    p.y = y;
+    const bool bf = desc->in_dtype == RSSM_BF16;
+    const int mode = split_mode(desc);
+    if (mode >= 0) return hip_status(rssm::launch_split_step(p, bf, mode, stream), "split step launch");
+    return hip_status(rssm::launch_replay_step(p, bf, stream), "replay step launch");
+}
+
+int replayssm_step_noalloc(const rssm_desc *desc, const rssm_state *st, const void *x, const void *B,
+                           const void *C, const void *dt, float *y, hipStream_t stream) {
+    RSSM_TRY(check_desc(desc));
+    if (nslots_of(desc) > rssm::kNoAllocMaxSlots)
+        return fail(RSSM_E_CAPACITY, "step_noalloc: %d state slots exceed the library scratch (%d slots)",
+                    nslots_of(desc), rssm::kNoAllocMaxSlots);
+    RSSM_TRY(check_state(desc, st));
+    if (desc->batch == 0) return RSSM_OK;
+    if (!x || !B || !C || !dt || !y) return fail(RSSM_E_ARG, "step_noalloc: an input/output pointer is NULL");
+    rssm::ReplayParams p = replay_params(desc, st);
+    RSSM_TRY(hip_status(rssm::noalloc_work(&p.work, stream), "step_noalloc: library scratch"));
     p.x = x;
     p.Bm = B;
     p.Cm = C;

@@ -19,14 +19,15 @@ struct ReplayParams {
     void *dtbuf;            // [B,Lcap,H]
     int32_t *pos;           // [B]
     int32_t *intv;          // [B]
-    int32_t *work;          // [nslots+1]
+    int32_t *work;          // [nslots] per-slot arrival counters (zero between calls)
+    int32_t *err;           // sticky device error word (work[nslots] of the caller's state)
     const float *A;         // [H]
     const float *D;         // [H]
     const int32_t *n_keep;  // [B] (accept)
     int batch, H, G, L, Lcap, T;
     int kmax;               // largest pos a step / verify accepts: L-1, or Lcap with deferred accepts
     const int32_t *slot_idx;  // [batch] state slot of each call row, -1 = padding row; NULL = identity
-    int nslots;             // state slots (ckpt / buffers / pos / intv; work has nslots + 1)
+    int nslots;             // state slots (ckpt / buffers / pos / intv / arrival counters)
     int from_zero;          // prefill: start from a zero state instead of the checkpoint
     int hpw;                // heads (waves) per workgroup
     int wg_per_slot;        // H / hpw
@@ -76,5 +77,11 @@ hipError_t launch_recurrent(const RecurrentParams &p, bool in_bf16, bool pool, h
 hipError_t launch_probe(int mode, const float *src, float *dst, size_t bytes, int grid, hipStream_t s);
 hipError_t launch_recurrent_accept(int32_t *sel, const int32_t *n_keep, int batch, int T,
                                    int Tmax, hipStream_t s);
+
+// Library scratch for callers that cannot allocate: per-slot arrival counters
+// of up to kNoAllocMaxSlots slots, one array per device.  *work receives the
+// current device's copy (set up, and cleared on `s`, on its first use).
+constexpr int kNoAllocMaxSlots = 1 << 16;
+hipError_t noalloc_work(int32_t **work, hipStream_t s);
 
 }  // namespace rssm

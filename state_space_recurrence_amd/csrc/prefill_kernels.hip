@@ -79,7 +79,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(ReplayParams a) {
     } else {
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) load_chunk(st[c], sp, c);
-        if (threadIdx.x == 0 && a.pos[s.b] != 0) atomicOr(&a.work[a.nslots], kErrPos);   // buffer not empty
+        if (threadIdx.x == 0 && a.pos[s.b] != 0) atomicOr(a.err, kErrPos);   // buffer not empty
     }
     const size_t HP = (size_t)a.H * kP, GN = (size_t)a.G * kN;
     const TIn *xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.row * Tp * HP + (size_t)s.h * kP;

@@ -24,7 +24,7 @@ __device__ __forceinline__ int slot_of_row(const ReplayParams &a, int row) {
     if (!a.slot_idx) return row;
     const int b = a.slot_idx[row];
     if (b >= a.nslots || b < -1) {
-        if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrSlot);
+        if (threadIdx.x == 0) atomicOr(a.err, kErrSlot);
         return -1;
     }
     return b;
@@ -167,7 +167,7 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
     StepIn in;
     int k = a.pos[s.b];
     if (k < 0 || k > kmax) {
-        if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrPos);
+        if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
         k = k < 0 ? 0 : kmax;
     }
     in.k = k;
@@ -332,7 +332,7 @@ __device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const S
     VerifyIn in;
     int k = a.pos[s.b];
     if (k < 0 || k > kmax) {
-        if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrPos);
+        if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
         k = k < 0 ? 0 : kmax;
     }
     in.k = k;
@@ -643,14 +643,14 @@ __device__ __forceinline__ int commit_count(const ReplayParams &a, const Slot &s
     const int kmax = ACCEPT ? a.L - 1 : a.Lcap;
     int k = a.pos[s.b];
     if (k < 0 || k > kmax) {
-        if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrPos);
+        if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
         k = k < 0 ? 0 : kmax;
     }
     int nk = 0;
     if (ACCEPT) {
         nk = a.n_keep[s.row];
         if (nk < 0 || nk > a.T) {
-            if (threadIdx.x == 0) atomicOr(&a.work[a.nslots], kErrKeep);
+            if (threadIdx.x == 0) atomicOr(a.err, kErrKeep);
             nk = nk < 0 ? 0 : a.T;
         }
     }

@@ -20,6 +20,8 @@
 //
 // Decays are formed as exp of segment sums of A dt (never as ratios of
 // prefix products, which underflow to 0/0 over an interval).
+#include <mutex>
+
 #include "device_common.h"
 #include "kernels.h"
 #include "replay_common.h"
@@ -289,17 +291,17 @@ __global__ void defer_accept_kernel(ReplayParams a) {
     int b = row;
     if (a.slot_idx) {
         b = a.slot_idx[row];
-        if (b >= a.nslots || b < -1) atomicOr(&a.work[a.nslots], kErrSlot);
+        if (b >= a.nslots || b < -1) atomicOr(a.err, kErrSlot);
         if (b < 0 || b >= a.nslots) return;
     }
     int k = a.pos[b];
     if (k < 0 || k > a.L - 1) {
-        atomicOr(&a.work[a.nslots], kErrPos);
+        atomicOr(a.err, kErrPos);
         k = k < 0 ? 0 : a.L - 1;
     }
     int nk = a.n_keep[row];
     if (nk < 0 || nk > a.T) {
-        atomicOr(&a.work[a.nslots], kErrKeep);
+        atomicOr(a.err, kErrKeep);
         nk = nk < 0 ? 0 : a.T;
     }
     a.pos[b] = k + nk;
@@ -318,7 +320,7 @@ __global__ void __launch_bounds__(256) load_f32_kernel(ReplayParams a) {
     const int row = blockIdx.x / a.H, h = blockIdx.x - row * a.H;
     const int b = a.slot_idx ? a.slot_idx[row] : row;
     if (b < 0 || b >= a.nslots) {
-        if (threadIdx.x == 0 && (b < -1 || b >= a.nslots)) atomicOr(&a.work[a.nslots], kErrSlot);
+        if (threadIdx.x == 0 && (b < -1 || b >= a.nslots)) atomicOr(a.err, kErrSlot);
         return;
     }
     const float *src = a.src + ((size_t)row * a.H + h) * kP * kN;
@@ -451,6 +453,47 @@ hipError_t launch_load_f32(const ReplayParams &p, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
     hipLaunchKernelGGL(load_f32_kernel, dim3(p.batch * p.H), dim3(256), 0, stream, p);
     return hipGetLastError();
+}
+
+// ------------------------------------------------ no-allocation scratch --
+// Per-slot arrival counters for callers that cannot allocate (or bring) the
+// workspace: a file-scope device array, one copy per device, held until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol); it uses the device address
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) int32_t scratch[kNoAllocMaxSlots];
+
+namespace {
+
+__global__ void zero_i32_kernel(int32_t *p, int n) {
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t *g_scratch[kMaxDevices] = {};
+
+}  // namespace
+
+hipError_t noalloc_work(int32_t **work, hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        // the counters must start at zero (every complete call leaves them so)
+        hipLaunchKernelGGL(zero_i32_kernel, dim3(64), dim3(256), 0, stream, static_cast<int32_t *>(ptr),
+                           kNoAllocMaxSlots);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        g_scratch[dev] = static_cast<int32_t *>(ptr);
+    }
+    *work = g_scratch[dev];
+    return hipSuccess;
 }
 
 }  // namespace rssm
