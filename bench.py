@@ -52,6 +52,24 @@ def replay_bytes_per_token(H, G, P=64, N=128, L=16, in_bytes=2, state_bytes=4):
     return state + state / L + cur + entry * (L - 1) / L + entry * (L - 1) / 2 + y
 
 
+def replay_step_bytes(H, G, k, L, P=64, N=128, in_bytes=2, state_bytes=4):
+    """Bytes one slot moves through one layer in a step taken at buffer
+    position k (0..L-1): checkpoint read; the checkpoint rewritten when the
+    step closes the interval (k = L-1), else the token appended; current
+    x, B, C, dt read; k buffered entries read; y written."""
+    state = H * P * N * state_bytes
+    entry = (H * P + G * N + H) * in_bytes
+    cur = (H * P + 2 * G * N + H) * in_bytes
+    return state + (state if k == L - 1 else entry) + cur + k * entry + H * P * 4
+
+
+def replay_window_bytes(H, G, L, pos0, steps, **kw):
+    """Bytes of `steps` consecutive steps of one slot and layer starting at
+    buffer position pos0 (lock-step phases: every commit that happens in
+    the window is counted, none that does not)."""
+    return sum(replay_step_bytes(H, G, (pos0 + i) % L, L, **kw) for i in range(steps))
+
+
 def split_bytes_per_token(fmt, H, G, P=64, N=128, L=16, in_bytes=2):
     """Replay step with a low-precision state (same buffer/input/output terms
     as the fp32 replay): every step reads the output source; once per
@@ -91,7 +109,8 @@ def main():
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-steps", type=int, default=160)
+    ap.add_argument("--repeats", type=int, default=5, help="timed repeats of the headline window (median)")
+    ap.add_argument("--cpu-steps", type=int, default=64)
     ap.add_argument("--summarize-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="write the counter summary from two rocprofv3 --pmc runs of --probe")
     ap.add_argument("--summarize-trace", nargs=3, metavar=("STATS_CSV", "OUT_MD", "RUN"),
@@ -254,15 +273,35 @@ def main():
         us = e0.elapsed_time(e1) * 1e3 / (reps * w.interval)
         return {"graph_us_per_step": us, "graph_tokens_per_s": y[0].shape[0] / us * 1e6}
 
-    def run_standard(w, batch, steps, warmup, with_recurrent=True, per_launch=True):
+    def median(v):
+        v = sorted(v)
+        return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+    def run_standard(w, batch, steps, warmup, with_recurrent=True, per_launch=True, repeats=1):
+        """Replay (and recurrent) decode of `steps` steps after `warmup`
+        untimed ones, timed `repeats` times back to back (median)."""
         n_in = min(steps + warmup, 64) if batch <= 32 else steps + warmup
         layers = make_layers(w, batch, n_in)
         y = [torch.empty(batch, w.heads, 64, device=dev) for _ in layers]
         replay_loop(layers, 0, warmup, y)
-        sec = timed(replay_loop, layers, warmup, steps, y)
+        pos0 = layers[0]["ls"].pos.cpu()
+        assert bool((pos0 == pos0[0]).all()), "lock-step phases expected"
+        pos0 = int(pos0[0])
+        secs = [timed(replay_loop, layers, warmup + r * steps, steps, y) for r in range(repeats)]
+        sec = median(secs)
+        # bytes of the window from the positions it actually covered (the
+        # commits inside it), identical for every repeat when steps % L == 0
+        wb = replay_window_bytes(w.heads, w.groups, w.interval, pos0, steps) * batch * w.layers
         out = {"batch": batch, "layers": w.layers, "heads": w.heads, "groups": w.groups,
-               "steps": steps, "replay_ms_per_step": sec / steps * 1e3,
-               "replay_tokens_per_s": batch * steps / sec}
+               "steps": steps, "repeats": repeats, "window_start_pos": pos0,
+               "window_commits_per_slot_layer": sum(1 for i in range(steps) if (pos0 + i) % w.interval
+                                                    == w.interval - 1),
+               "replay_ms_per_step": sec / steps * 1e3,
+               # the timed region holds nothing but back-to-back step launches
+               "replay_launch_avg_us": sec / (steps * w.layers) * 1e6,
+               "replay_ms_per_step_repeats": [round(x / steps * 1e3, 4) for x in secs],
+               "replay_tokens_per_s": batch * steps / sec,
+               "replay_window_GB": wb / 1e9, "replay_window_GBps": wb / sec / 1e9}
         if per_launch:
             ev = []
             replay_loop(layers, warmup + steps, 4 * w.interval, y, ev)
@@ -270,7 +309,8 @@ def main():
         if with_recurrent:
             states = [lay["S0"].clone() for lay in layers]
             recurrent_loop(layers, states, 0, warmup, y)
-            rsec = timed(recurrent_loop, layers, states, warmup, steps, y)
+            rsec = median([timed(recurrent_loop, layers, states, warmup + r * steps, steps, y)
+                           for r in range(repeats)])
             out["recurrent_ms_per_step"] = rsec / steps * 1e3
             out["recurrent_tokens_per_s"] = batch * steps / rsec
             out["replay_speedup_vs_recurrent"] = rsec / sec
@@ -284,7 +324,7 @@ def main():
         cb = recurrent_bytes_per_token(w.heads, w.groups)
         out["replay_bytes_per_token_layer"] = rb
         out["recurrent_bytes_per_token_layer"] = cb
-        out["replay_GBps_stack"] = rb * batch * w.layers * steps / sec / 1e9
+        out["replay_GBps_stack"] = out["replay_window_GBps"]
         del layers
         torch.cuda.empty_cache()
         return out
@@ -345,11 +385,14 @@ def main():
 
     # ------------------------------------------------- practical HBM ceilings
     def hbm_ceilings(nbytes=4 << 30, reps=5):
+        """Practical HBM rates: plain read and copy streams (8 loads in flight
+        per thread) and a read in the step kernel's shape (one 32 KB block per
+        wave, 16 loads in flight per lane); best over grid sizes."""
         src = torch.ones(nbytes // 4, device=dev)
         dst = torch.empty_like(src)
-        best = {"read": 0.0, "copy": 0.0}
-        for grid in (1024, 2048, 4096):
-            for mode, name in ((0, "read"), (1, "copy")):
+        best = {"read": 0.0, "copy": 0.0, "head_read": 0.0}
+        for grid in (1024, 2048, 4096, 8192):
+            for mode, name in ((0, "read"), (1, "copy"), (2, "head_read")):
                 rs.hbm_probe(mode, src, dst, grid)
                 torch.cuda.synchronize()
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -358,27 +401,44 @@ def main():
                     rs.hbm_probe(mode, src, dst, grid)
                 e1.record(stream)
                 torch.cuda.synchronize()
-                gbps = (nbytes if mode == 0 else 2 * nbytes) * reps / (e0.elapsed_time(e1) * 1e6)
+                gbps = (2 * nbytes if mode == 1 else nbytes) * reps / (e0.elapsed_time(e1) * 1e6)
                 best[name] = max(best[name], gbps)
         del src, dst
         torch.cuda.empty_cache()
-        return {"read_GBps": round(best["read"], 1), "copy_GBps": round(best["copy"], 1),
-                "probe": "4 GiB grid-stride stream, 16-byte non-temporal loads/stores, best of grids 1024/2048/4096"}
+        return {"read_GBps": round(max(best["read"], best["head_read"]), 1),
+                "plain_read_GBps": round(best["read"], 1), "head_read_GBps": round(best["head_read"], 1),
+                "copy_GBps": round(best["copy"], 1),
+                "probe": "4 GiB streams, 16-byte non-temporal accesses; read/copy: grid-stride, 8 loads in "
+                         "flight per thread; head_read: one 32 KB block per wave, 16 loads in flight per lane; "
+                         "best of grids 1024-8192"}
 
     # -------------------------------------------------------------- headline
-    log(f"[bench] {w.describe()} batch={args.batch} steps={args.steps} warmup={args.warmup}")
-    main_res = run_standard(w, args.batch, args.steps, args.warmup)
+    # the timed window covers whole intervals and starts at an interval
+    # boundary (lock-step phases), whatever --steps / --warmup say: every
+    # window then holds exactly steps / L commits per slot and layer
+    Lw = w.interval
+    steps_t = max(Lw, -(-args.steps // Lw) * Lw)
+    warm_t = max(Lw, -(-args.warmup // Lw) * Lw)
+    log(f"[bench] {w.describe()} batch={args.batch} steps={steps_t} (asked {args.steps}) "
+        f"warmup={warm_t} (asked {args.warmup}) repeats={args.repeats}")
+    main_res = run_standard(w, args.batch, steps_t, warm_t, repeats=max(1, args.repeats))
     log(f"[bench] replay {main_res['replay_tokens_per_s']:.0f} tok/s, "
         f"recurrent {main_res.get('recurrent_tokens_per_s', 0):.0f} tok/s")
 
     rb = main_res["replay_bytes_per_token_layer"]
-    avg_us = main_res["replay_kernel_avg_us"]
+    # average launch duration over the timed region (HIP events on the launch
+    # stream around steps x layers back-to-back launches of this kernel; the
+    # window is whole intervals, so commits are in their true proportion);
+    # the per-launch event pairs of a separate pass add ~2 us of event
+    # overhead to each launch and are reported beside it
+    avg_us = main_res["replay_launch_avg_us"]
     achieved = rb * args.batch / (avg_us * 1e-6) / 1e9
     traffic = _load_traffic()
     roofline = {"bound": "hbm", "kernel": "replay_step_kernel<bf16,16>",
                 "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "bytes_per_launch": rb * args.batch, "avg_launch_us": round(avg_us, 2)}
+                "bytes_per_launch": rb * args.batch, "avg_launch_us": round(avg_us, 2),
+                "avg_launch_us_event_pairs": round(main_res["replay_kernel_avg_us"], 2)}
 
     ceil = hbm_ceilings()
     log(f"[bench] practical HBM ceilings: read {ceil['read_GBps']:.0f} GB/s, copy {ceil['copy_GBps']:.0f} GB/s")
@@ -422,15 +482,15 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, args.cpu_steps, log)
+        cpu = cpu_baseline(w, synth.WORKLOADS["120b"], args.cpu_steps, log)
 
     res = {
         "metric": "SSM-layer decode tokens/s @B=256,L=16 + achieved HBM GB/s (% of peak)",
         "value": round(main_res["replay_tokens_per_s"], 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps_t,
+        "warmup": warm_t,
         "ms_per_step": round(main_res["replay_ms_per_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -441,6 +501,13 @@ def main():
                                "P=64, N=128, 8 groups, L=16, fp32 checkpoint, bf16 inputs",
                    "batch": args.batch, "layers": w.layers, "heads": w.heads, "groups": w.groups,
                    "interval": w.interval, "parallelism": "single GPU"},
+        "timing": {"protocol": "HIP events on the launch stream around the stacked-layer loop; the window "
+                              "is rounded up to whole 16-step intervals and starts at an interval boundary; "
+                              f"median of {main_res['repeats']} back-to-back repeats",
+                   "steps_asked": args.steps, "warmup_asked": args.warmup,
+                   "ms_per_step_repeats": main_res["replay_ms_per_step_repeats"],
+                   "window_commits_per_slot_layer": main_res["window_commits_per_slot_layer"],
+                   "window_GB": round(main_res["replay_window_GB"], 4)},
         "hbm_GBps_stack": round(main_res["replay_GBps_stack"], 1),
         "hbm_frac_stack": round(main_res["replay_GBps_stack"] / HBM_PEAK_GBS, 4),
         "roofline": roofline,
@@ -744,33 +811,76 @@ def run_split(rs, L, torch, synth, dev, stream, sh, log, steps=256, warm=16, dri
     return out
 
 
-def cpu_baseline(w, steps, log, slots=None):
-    """fp64 oracle (the plain per-token recurrence) on the host cores: the
-    full batch of the workload for `steps` decode steps through all layers."""
-    import numpy as np
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_rate(w, steps, slots, log, tag):
+    """Decode tokens/s of the fp64 oracle over `slots` slots of workload w,
+    all its layers, `steps` steps (each layer's inputs generated outside the
+    timed region)."""
     import oracle
     import synth
-    b = slots or w.batch
     total = 0.0
+    for l in range(w.layers):
+        A, D = (oracle._f64(t) for t in synth.layer_params(w, l))
+        S = oracle._f64(synth.init_state(w, l, batch=slots))
+        ins = [oracle._f64(t) for t in synth.token_inputs(w, l, steps, batch=slots)]
+        # the call's fixed cost (copying the state) is timed on zero steps and
+        # taken out, so the rate is the per-step work
+        t0 = time.perf_counter()
+        oracle.recurrent(S, *(t[:0] for t in ins), A, D, w.groups)
+        t1 = time.perf_counter()
+        oracle.recurrent(S, *ins, A, D, w.groups)
+        total += (time.perf_counter() - t1) - (t1 - t0)
+        del S, ins
+    tok = slots * steps / total
+    log(f"[bench] cpu oracle {tag}: {tok:.1f} tok/s on {oracle.num_threads()} threads "
+        f"({slots} slots x {w.layers} layers x {steps} steps, {total:.1f}s)")
+    return {"tokens_per_s": round(tok, 2), "ms_per_step": round(total / steps * 1e3, 2),
+            "threads": oracle.num_threads(), "slots": slots, "layers": w.layers, "heads": w.heads,
+            "steps": steps, "seconds": round(total, 2)}
+
+
+def cpu_baseline(w, w2, steps, log):
+    """fp64 oracle (the plain per-token recurrence, OpenMP over slot x head)
+    on the host: the full 4B-class and 120B-class batches on all the cores
+    the process may use, and a 16-slot sample of each on one core (the cost
+    per slot is the same for every slot).  `steps` decode steps per layer."""
+    import oracle
+    import synth
     # warm the library and its thread pool on a tiny call
     S, x, Bm, Cm, dt = (oracle._f64(t) for t in (synth.init_state(w, 0, batch=1),
                                                  *synth.token_inputs(w, 0, 1, batch=1)))
     A, D = (oracle._f64(t) for t in synth.layer_params(w, 0))
     oracle.recurrent(S, x, Bm, Cm, dt, A, D, w.groups)
-    for l in range(w.layers):
-        A, D = (oracle._f64(t) for t in synth.layer_params(w, l))
-        S = oracle._f64(synth.init_state(w, l, batch=b))
-        ins = [oracle._f64(t) for t in synth.token_inputs(w, l, steps, batch=b)]
-        t0 = time.perf_counter()
-        oracle.recurrent(S, *ins, A, D, w.groups)
-        total += time.perf_counter() - t0
-        del S, ins
-    tok = b * steps / total
-    log(f"[bench] cpu oracle: {tok:.1f} tok/s on {oracle.num_threads()} threads ({total:.1f}s)")
-    return {"value": round(tok, 2), "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"full workload batch {b} x {w.layers} layers x {steps} decode steps "
-                      f"(fp64 per-token recurrence, OpenMP over slot x head)",
-            "seconds": round(total, 2)}
+    allc = oracle.num_threads()
+    res = {"all_cores": {}, "one_core": {}}
+    res["all_cores"]["4b"] = _oracle_rate(w, steps, w.batch, log, "4b, all cores")
+    res["all_cores"]["120b"] = _oracle_rate(w2, steps, w2.batch, log, "120b, all cores")
+    oracle.set_num_threads(1)
+    try:
+        res["one_core"]["4b"] = _oracle_rate(w, steps, 16, log, "4b, 1 core")
+        res["one_core"]["120b"] = _oracle_rate(w2, steps, 16, log, "120b, 1 core")
+    finally:
+        oracle.set_num_threads(allc)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
+    head = res["all_cores"]["4b"]
+    return {"value": head["tokens_per_s"], "unit": "tokens/s", "cores": head["threads"], "kind": "oracle",
+            "sample": f"4B-class workload, all {w.batch} slots x {w.layers} layers x {steps} decode steps "
+                      f"(per-step cost is constant), fp64 per-token recurrence, OpenMP over slot x head; "
+                      f"1-core figures on 16 slots",
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": affinity,
+            "omp_threads": allc, **res}
 
 
 TRAFFIC_MD = os.path.join(ROOT, "profiles", "replay_step_4b_b256_counters.md")

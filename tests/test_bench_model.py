@@ -46,6 +46,16 @@ def test_replay_bytes_match_enumeration(H, G, L):
     assert bench.replay_bytes_per_token(H, G, L=L) == pytest.approx(brute, rel=1e-12)
 
 
+@pytest.mark.parametrize("pos0,steps", [(0, 16), (0, 32), (5, 20), (0, 20), (15, 1), (3, 0)])
+def test_window_bytes_count_the_commits_inside(pos0, steps):
+    H, G, L = 96, 8, 16
+    brute = sum(_step_bytes(H, G, L, (pos0 + i) % L) for i in range(steps))
+    assert bench.replay_window_bytes(H, G, L, pos0, steps) == brute
+    if pos0 == 0 and steps % L == 0:   # whole intervals: exactly the per-token average
+        assert bench.replay_window_bytes(H, G, L, pos0, steps) == pytest.approx(
+            steps * bench.replay_bytes_per_token(H, G, L=L), rel=1e-12)
+
+
 def test_replay_bytes_headline_value():
     # 4B-class layer (H=96, G=8, L=16, bf16 inputs): the per-token figure the
     # roofline uses (x 256 slots = 897,553,408 bytes per launch)
