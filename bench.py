@@ -122,6 +122,14 @@ def main():
                          "launches, then 3 plain 1 GiB device copies (calibration)")
     ap.add_argument("--summarize-verify-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
                     help="write the verify kernel's counter summary from two --probe-verify runs")
+    ap.add_argument("--probe-kernels", action="store_true",
+                    help="short fixed run for profiler counters of the other kernels: each precision-split "
+                         "format (one 4B-class layer, batch 256, 32 steps), a prompt prefill (batch 256, 256 "
+                         "tokens), 8 speculative rounds with deferred and 8 with eager accepts (batch 512, 5 "
+                         "positions), then 3 plain 1 GiB device copies (calibration)")
+    ap.add_argument("--summarize-kernels", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD", "EXTRA_CSV"),
+                    help="write the per-kernel counter summary from two --probe-kernels runs (FETCH_SIZE, "
+                         "WRITE_SIZE) and a third run's counters ('-' for none)")
     ap.add_argument("--probe", action="store_true",
                     help="short fixed run for profiler counters: 16 warm-up + 16 replay steps, "
                          "16 recurrent steps, then 3 plain 1 GiB device copies (calibration)")
@@ -156,6 +164,9 @@ def main():
         cmd = ("rocprofv3 --pmc COUNTER -f csv -d gpurun_out/pmc_verify_COUNTER -o pmc -- "
                "python -u bench.py --probe-verify")
         summarize_verify_counters(*args.summarize_verify_counters, command=cmd)
+        return
+    if args.summarize_kernels:
+        summarize_kernels(*args.summarize_kernels)
         return
     if args.summarize_counters:
         cmd = ("rocprofv3 --pmc COUNTER -f csv -d gpurun_out/pmc_COUNTER -o pmc -- "
@@ -368,6 +379,9 @@ def main():
 
     if args.probe_verify:
         probe_verify(rs, L, torch, synth, dev, stream, sh, log)
+        return
+    if args.probe_kernels:
+        probe_kernels(rs, torch, synth, dev, log)
         return
     if args.probe:
         layers = make_layers(w, args.batch, 32)
@@ -981,6 +995,184 @@ def probe_verify(rs, L, torch, synth, dev, stream, sh, log, launches=16):
         dst.copy_(src)
     torch.cuda.synchronize()
     log(f"[bench] verify probe done: {PROBE_VERIFY_ROUNDS} eager rounds, {launches} verifies, 3 x 1 GiB copies")
+
+
+PROBE_SPLIT_FORMATS = ("split-bf16", "split-e4m3", "shared-fp4", "low-bf16", "low-e4m3")
+PROBE_SPLIT_STEPS = 32
+PROBE_PREFILL = (256, 256)   # batch, prompt tokens
+PROBE_SPEC_ROUNDS = 8
+
+
+def probe_kernels(rs, torch, synth, dev, log):
+    """Counter probe of the kernels other than the fp32 step and verify, each
+    in its benchmark shape (see --probe-kernels)."""
+    w = synth.WORKLOADS["split"]
+    A, D = synth.layer_params(w, 0, device=dev)
+    S0 = synth.init_state(w, 0, device=dev)
+    x, Bm, Cm, dt = synth.token_inputs(w, 0, PROBE_SPLIT_STEPS, device=dev)
+    for fmt in PROBE_SPLIT_FORMATS:
+        ls = rs.LayerState(w.batch, w.heads, w.groups, A, D, interval=w.interval, in_dtype=x.dtype, device=dev,
+                           state_format=fmt, seed=0x5EED)
+        rs.load_checkpoint(ls, S0)
+        y = torch.empty(w.batch, w.heads, 64, device=dev)
+        for t in range(PROBE_SPLIT_STEPS):
+            rs.step(ls, x[t], Bm[t], Cm[t], dt[t], y=y)
+        rs.check_device_errors(ls)
+        del ls
+    del x, Bm, Cm, dt
+    batch, Tp = PROBE_PREFILL
+    w4 = synth.WORKLOADS["4b"]
+    A4, D4 = synth.layer_params(w4, 0, device=dev)
+    px, pB, pC, pdt = (t.transpose(0, 1).contiguous() for t in synth.token_inputs(w4, 0, Tp, device=dev, batch=batch))
+    ls = rs.LayerState(batch, w4.heads, w4.groups, A4, D4, interval=16, in_dtype=px.dtype, device=dev)
+    rs.prefill(ls, px, pB, pC, pdt, from_zero=True, y=torch.empty(batch, Tp, w4.heads, 64, device=dev))
+    rs.check_device_errors(ls)
+    del ls, px, pB, pC, pdt
+    ws = synth.WORKLOADS["spec"]
+    T = ws.drafts + 1
+    A, D = synth.layer_params(ws, 0, device=dev)
+    S0 = synth.init_state(ws, 0, device=dev)
+    x, Bm, Cm, dt = (t.transpose(1, 2).contiguous()
+                     for t in synth.token_inputs(ws, 0, PROBE_SPEC_ROUNDS, device=dev, tokens=T))
+    nk = synth.n_keep(ws, PROBE_SPEC_ROUNDS).to(dev)
+    y = torch.empty(ws.batch, T, ws.heads, 64, device=dev)
+    for deferred in (True, False):
+        ls = rs.LayerState(ws.batch, ws.heads, ws.groups, A, D, interval=ws.interval, max_draft=T,
+                           in_dtype=x.dtype, device=dev, deferred_commit=deferred)
+        rs.load_checkpoint(ls, S0)
+        for r in range(PROBE_SPEC_ROUNDS):
+            rs.verify(ls, x[r], Bm[r], Cm[r], dt[r], y=y)
+            (rs.accept_deferred if deferred else rs.accept)(ls, nk[r], T)
+        rs.check_device_errors(ls)
+        del ls
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"[bench] kernel probe done: {len(PROBE_SPLIT_FORMATS)} split formats x {PROBE_SPLIT_STEPS} steps, "
+        f"a prefill, {PROBE_SPEC_ROUNDS} deferred + {PROBE_SPEC_ROUNDS} eager speculative rounds, 3 x 1 GiB copies")
+
+
+def _kernel_label(name: str) -> str:
+    """Short kernel label: the function name with its template arguments."""
+    base = name.replace("rssm::(anonymous namespace)::", "").replace("rssm::", "").replace("void ", "")
+    return base.split("(")[0].strip()
+
+
+def summarize_kernels(fetch_csv: str, write_csv: str, out_md: str, extra_csv: str) -> None:
+    """Per-kernel counter summary of `bench.py --probe-kernels`: FETCH_SIZE /
+    WRITE_SIZE per dispatch scaled by the probe's 1 GiB copies, against the
+    algorithmic bytes where the byte model covers the launch; split-step
+    launches are split into the interval-closing (commit) launches and the
+    others.  A third run's counters (EXTRA_CSV, e.g. VALU activity) are
+    averaged per kernel as read."""
+    import csv
+    import synth
+    copy_bytes = float(1 << 30)
+
+    def load(path):
+        rows = list(csv.DictReader(open(path)))
+        rows.sort(key=lambda r: int(r.get("Dispatch_Id", 0)))
+        return rows
+
+    def calib(rows, counter):
+        cp = [r for r in rows if "copyBuffer" in r["Kernel_Name"] and r["Counter_Name"] == counter]
+        big = max(int(r["Grid_Size"]) for r in cp)
+        vals = [float(r["Counter_Value"]) for r in cp if int(r["Grid_Size"]) == big][-3:]
+        return copy_bytes / (sum(vals) / len(vals) * 1024)
+
+    fr, wr = load(fetch_csv), load(write_csv)
+    fcal, wcal = calib(fr, "FETCH_SIZE"), calib(wr, "WRITE_SIZE")
+    ours = lambda r: "rssm::" in r["Kernel_Name"]
+    fseq = [(_kernel_label(r["Kernel_Name"]), float(r["Counter_Value"]) * 1024 * fcal)
+            for r in fr if ours(r) and r["Counter_Name"] == "FETCH_SIZE"]
+    wseq = [(_kernel_label(r["Kernel_Name"]), float(r["Counter_Value"]) * 1024 * wcal)
+            for r in wr if ours(r) and r["Counter_Name"] == "WRITE_SIZE"]
+    assert [k for k, _ in fseq] == [k for k, _ in wseq], "the two runs dispatched different kernel sequences"
+    ws = synth.WORKLOADS["split"]
+    E = ws.heads * 64 * 128
+    groups = {}
+    split_i = {}
+    for (k, f), (_, wv) in zip(fseq, wseq):
+        key = k
+        if k.startswith("split_step_kernel"):
+            i = split_i.get(k, 0)
+            split_i[k] = i + 1
+            key = k + (" [commit launches]" if i % ws.interval == ws.interval - 1 else " [other launches]")
+        groups.setdefault(key, []).append((f, wv))
+    extra = {}
+    if extra_csv != "-":
+        for r in load(extra_csv):
+            if ours(r):
+                extra.setdefault((_kernel_label(r["Kernel_Name"]), r["Counter_Name"]), []).append(
+                    float(r["Counter_Value"]))
+    modes = {0: "split-bf16", 1: "split-e4m3", 2: "shared-fp4", 3: "low-bf16", 4: "low-e4m3"}
+    fp4 = 0.5 + 1.0 / 32
+
+    def model(key):
+        """Algorithmic bytes of one launch (None where the model does not
+        cover it)."""
+        if key.startswith("split_step_kernel"):
+            mode = int(key.split("<")[1].split(">")[0].split(",")[-1])
+            fmt = modes[mode]
+            out_r, upd_r, cw = {"split-bf16": (fp4, 2, 2 + fp4), "split-e4m3": (fp4, 1, 1 + fp4),
+                                "shared-fp4": (fp4, fp4, fp4), "low-bf16": (2, 0, 2),
+                                "low-e4m3": (1, 0, 1)}[fmt]
+            L = ws.interval
+            entry = (ws.heads * 64 + ws.groups * 128 + ws.heads) * 2
+            cur = (ws.heads * 64 + 2 * ws.groups * 128 + ws.heads) * 2
+            if "commit" in key:   # position L-1: read L-1 entries, read U and write U / O, no append
+                b = E * (out_r + upd_r + cw) + cur + (L - 1) * entry + ws.heads * 64 * 4
+            else:                 # positions 0..L-2, averaged
+                b = E * out_r + cur + entry + (L - 2) / 2 * entry + ws.heads * 64 * 4
+            return b * ws.batch
+        if key.startswith("prefill_kernel"):
+            batch, Tp = PROBE_PREFILL
+            w4 = synth.WORKLOADS["4b"]
+            return batch * (Tp * (w4.heads * 64 + 2 * w4.groups * 128 + w4.heads) * 2 + Tp * w4.heads * 64 * 4
+                            + w4.heads * 64 * 128 * 4)
+        return None
+
+    lines = ["# HBM traffic counters: precision-split, prefill, fold and commit kernels",
+             "",
+             "Commands (from the repository root; one counter set per run):",
+             "",
+             "    rocprofv3 --pmc FETCH_SIZE -f csv -d gpurun_out/pmc_k_FETCH_SIZE -o pmc -- python -u bench.py --probe-kernels",
+             "    rocprofv3 --pmc WRITE_SIZE -f csv -d gpurun_out/pmc_k_WRITE_SIZE -o pmc -- python -u bench.py --probe-kernels",
+             ]
+    if extra_csv != "-":
+        names = sorted({c for _, c in extra})
+        lines.append(f"    rocprofv3 --pmc {' '.join(names)} -f csv -d gpurun_out/pmc_k_extra -o pmc -- "
+                     "python -u bench.py --probe-kernels")
+    lines += ["",
+              f"`bench.py --probe-kernels`: each precision-split format on one 4B-class layer (batch {ws.batch}, "
+              f"H={ws.heads}, G={ws.groups}, L={ws.interval}, lock-step phases, {PROBE_SPLIT_STEPS} steps: "
+              f"{PROBE_SPLIT_STEPS // ws.interval} commit launches each); a prompt prefill (batch {PROBE_PREFILL[0]}, "
+              f"{PROBE_PREFILL[1]} tokens, 4B-class heads, from zero, with outputs); {PROBE_SPEC_ROUNDS} speculative "
+              "rounds with deferred accepts, then as many with eager accepts (batch 512, H=128, 5 positions); "
+              "three 1 GiB copies calibrate the counters.",
+              "",
+              f"Calibration: FETCH_SIZE x {fcal:.4f}, WRITE_SIZE x {wcal:.4f} (known bytes / counter bytes "
+              "of the 1 GiB copy).", "",
+              "| kernel | launches | FETCH MB / launch | WRITE MB / launch | algorithmic MB / launch | ratio |",
+              "|---|---|---|---|---|---|"]
+    for key, v in groups.items():
+        f = sum(a for a, _ in v) / len(v)
+        wv = sum(b for _, b in v) / len(v)
+        m = model(key)
+        ms = f"{m / 1e6:.1f}" if m else "-"
+        rt = f"{(f + wv) / m:.3f}" if m else "-"
+        lines.append(f"| `{key}` | {len(v)} | {f / 1e6:.1f} | {wv / 1e6:.1f} | {ms} | {rt} |")
+    if extra:
+        names = sorted({c for _, c in extra})
+        lines += ["", "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+        for k in dict.fromkeys(k for k, _ in extra):
+            vals = [extra.get((k, c)) for c in names]
+            lines.append(f"| `{k}` | " + " | ".join(f"{sum(x) / len(x):.4g}" if x else "-" for x in vals) + " |")
+    lines.append("")
+    open(out_md, "w").write("\n".join(lines))
+    print("\n".join(lines))
 
 
 def summarize_verify_counters(fetch_csv: str, write_csv: str, out_md: str, command: str,

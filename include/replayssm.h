@@ -41,7 +41,10 @@
  *  - Device-side range errors (a position count out of range, n_keep > T, a
  *    row mapped to a slot outside 0..S-1) are clamped or skipped and
  *    recorded in a sticky flag read by
- *    replayssm_check_device_errors().
+ *    replayssm_check_device_errors().  Two rows of one call mapped to the
+ *    same slot race (results undefined); the position-publishing kernels
+ *    flag it in the same word when they see it (more arrivals on the slot
+ *    than one row brings, or its position changed during the call).
  *
  * Shapes (B = batch, H = n_heads, P = head_dim, N = d_state, G = n_groups,
  * L = interval, Tmax = max_draft, Lcap = L + Tmax - 1):
@@ -148,7 +151,8 @@ typedef struct rssm_state {
     float *debug_prequant;/* optional [B,H,P,N] fp32: commit values before rounding (split path tests); NULL */
     const int32_t *slot_idx; /* [batch] device: state slot of each call row, -1 = padding row (nothing
                                 read or written for it); NULL = row b uses slot b.  Slots of one call
-                                must be distinct.  Rows mapped outside 0..S-1 are skipped and flagged */
+                                must be distinct (a duplicate is flagged when detected, see above).
+                                Rows mapped outside 0..S-1 are skipped and flagged */
 } rssm_state;
 
 /*
@@ -244,8 +248,14 @@ int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t st
  * The state after the prompt becomes the checkpoint (pos = 0, intv + 1).
  * When y is not NULL the outputs of all prompt tokens are written.  Each
  * head's state stays on chip for the whole prompt, which is processed in
- * 16-token chunks; results are bit-identical to decoding the prompt token
- * by token with L = 16 and flushing at the end.  F32 checkpoints only.
+ * 16-token chunks; with an F32 checkpoint, results are bit-identical to
+ * decoding the prompt token by token with L = 16 and flushing at the end.
+ * With a low-precision state (article section 4) the prompt runs in fp32 on
+ * chip from the decoded update source (update checkpoint, or the FP4 copy of
+ * the shared mode) and the final state is written once, like a commit: the
+ * update checkpoint by stochastic rounding with stream index intv + 1, the
+ * FP4 copy quantised from the same fp32 values (debug_prequant receives
+ * them when set); the prompt outputs come from the fp32 recurrence.
  * x [B,Tp,H,P], B, C [B,Tp,G,N], dt [B,Tp,H] (in_dtype); y [B,Tp,H,P] fp32
  * or NULL (then C may be NULL).
  */

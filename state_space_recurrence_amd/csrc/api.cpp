@@ -285,7 +285,6 @@ int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t st
 int replayssm_prefill(const rssm_desc *desc, const rssm_state *st, int32_t Tp, int32_t from_zero, const void *x,
                       const void *B, const void *C, const void *dt, float *y, hipStream_t stream) {
     RSSM_TRY(check_desc(desc));
-    if (split_mode(desc) >= 0) return fail(RSSM_E_UNSUPPORTED, "prefill: F32 checkpoints only");
     if (Tp < 0) return fail(RSSM_E_ARG, "prefill: Tp = %d < 0", Tp);
     if (from_zero != 0 && from_zero != 1) return fail(RSSM_E_ARG, "prefill: from_zero must be 0 or 1");
     if ((int64_t)desc->batch * Tp * desc->n_heads > (int64_t)1 << 31)
@@ -302,7 +301,8 @@ int replayssm_prefill(const rssm_desc *desc, const rssm_state *st, int32_t Tp, i
     p.y = y;
     p.T = Tp;
     p.from_zero = from_zero;
-    return hip_status(rssm::launch_prefill(p, desc->in_dtype == RSSM_BF16, y != nullptr, stream), "prefill launch");
+    return hip_status(rssm::launch_prefill(p, desc->in_dtype == RSSM_BF16, y != nullptr, split_mode(desc), stream),
+                      "prefill launch");
 }
 
 int replayssm_load_checkpoint(const rssm_desc *desc, const rssm_state *st, const float *src,
@@ -427,7 +427,7 @@ int replayssm_check_device_errors(const rssm_state *st, int32_t n_slots, hipStre
                         "check_device_errors clear"));
     return fail(RSSM_E_DEVICE,
                 "device range error flags 0x%x (1: position out of range, 2: n_keep out of range, "
-                "4: row mapped to a slot out of range)",
+                "4: row mapped to a slot out of range, 8: two rows of one call on the same slot)",
                 word);
 }
 

@@ -212,5 +212,6 @@ __device__ __forceinline__ int xcd_remap(int bid, int nwg) {
 constexpr int kErrPos = 1;    // position count out of range on entry
 constexpr int kErrKeep = 2;   // n_keep outside 0..T
 constexpr int kErrSlot = 4;   // a call row mapped to a slot outside 0..nslots-1 (row skipped)
+constexpr int kErrDup = 8;    // two rows of one call on the same slot (a race; results undefined)
 
 }  // namespace rssm

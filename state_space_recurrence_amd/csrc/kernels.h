@@ -68,7 +68,8 @@ hipError_t launch_replay_commit(const ReplayParams &p, bool in_bf16, bool accept
 hipError_t launch_zero_pos(const ReplayParams &p, hipStream_t s);
 hipError_t launch_load_f32(const ReplayParams &p, hipStream_t s);   // ckpt[slot] <- src[row]
 hipError_t launch_defer_accept(const ReplayParams &p, hipStream_t s);
-hipError_t launch_prefill(const ReplayParams &p, bool in_bf16, bool outputs, hipStream_t s);   // p.T = prompt length
+// p.T = prompt length; mode -1 = fp32 checkpoint, else the SplitMode of a low-precision state
+hipError_t launch_prefill(const ReplayParams &p, bool in_bf16, bool outputs, int mode, hipStream_t s);
 hipError_t launch_split_step(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
 hipError_t launch_split_verify(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
 hipError_t launch_split_commit(const ReplayParams &p, bool in_bf16, int mode, bool accept, hipStream_t s);

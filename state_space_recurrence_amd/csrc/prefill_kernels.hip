@@ -12,9 +12,17 @@
 // decoding the prompt token by token with a 16-token interval and flushing
 // at the end, while HBM sees only the prompt inputs, the outputs and one
 // read and one write of the state.
+//
+// With a low-precision state (precision split, section 4) the prompt runs the
+// same way in fp32 on chip; the start state is the decoded update source (the
+// update checkpoint, or the FP4 copy of the shared mode) and the final state
+// is written once, like a commit: the update checkpoint stochastically rounded
+// with the stream index of the interval it starts (intv + 1), the FP4 output
+// copy quantised from the same fp32 values.
 #include "device_common.h"
 #include "kernels.h"
 #include "replay_common.h"
+#include "split_common.h"
 
 namespace rssm {
 
@@ -62,7 +70,21 @@ __device__ __forceinline__ void advance_chunk(float4 (&st)[kPerChunk], int c, fl
     }
 }
 
-template <typename TIn, bool OUT>
+// Rounds and stores the lane's rows of chunk C (a template argument, so the
+// state array is indexed statically and stays in registers).
+template <int MODE, int C>
+__device__ __forceinline__ void quantize_chunk(const ReplayParams &a, const Slot &s, size_t hrow,
+                                               const float4 (&st)[kPerChunk], uint32_t interval) {
+#pragma unroll
+    for (int m = 0; m < kPerChunk; m += 2) {
+        quantize_store_rows<MODE>(a, hrow + 2 * chunk_index(C, m), hrow + 2 * chunk_index(C, m + 1), s.c, s.lane,
+                                  st[m], st[m + 1], interval);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// MODE: -1 for the fp32 checkpoint, else the SplitMode of a low-precision state.
+template <typename TIn, bool OUT, int MODE>
 __global__ void __launch_bounds__(256) prefill_kernel(ReplayParams a) {
     __shared__ PrefillSmem sm;
 
@@ -70,6 +92,7 @@ __global__ void __launch_bounds__(256) prefill_kernel(ReplayParams a) {
     if (s.b < 0) return;   // padding row
     const int Tp = a.T;
     const HeadState sp = head_state(a.ckpt, s, a.H);
+    const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;   // the lane's first row (low-precision state)
     float4 st[kChunks][kPerChunk];
     if (a.from_zero) {
 #pragma unroll
@@ -77,8 +100,17 @@ __global__ void __launch_bounds__(256) prefill_kernel(ReplayParams a) {
 #pragma unroll
             for (int m = 0; m < kPerChunk; ++m) st[c][m] = make_float4(0.f, 0.f, 0.f, 0.f);
     } else {
+        if constexpr (MODE < 0) {
 #pragma unroll
-        for (int c = 0; c < kChunks; ++c) load_chunk(st[c], sp, c);
+            for (int c = 0; c < kChunks; ++c) load_chunk(st[c], sp, c);
+        } else {   // the decoded update source, in the same lane layout
+            constexpr int UB = ModeTraits<MODE>::ubits;
+#pragma unroll
+            for (int c = 0; c < kChunks; ++c)
+#pragma unroll
+                for (int m = 0; m < kPerChunk; ++m)
+                    st[c][m] = decode_row4<UB>(load_row4<UB>(a, hrow + 2 * chunk_index(c, m), s.c));
+        }
         if (threadIdx.x == 0 && a.pos[s.b] != 0) atomicOr(a.err, kErrPos);   // buffer not empty
     }
     const size_t HP = (size_t)a.H * kP, GN = (size_t)a.G * kN;
@@ -182,22 +214,46 @@ __global__ void __launch_bounds__(256) prefill_kernel(ReplayParams a) {
 #pragma unroll
         for (int c = 0; c < kChunks; ++c) advance_chunk(st[c], c, lamq, sm.cs[s.wave], sm.B, s.hf, Kr);
     }
+    if constexpr (MODE < 0) {
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) store_chunk(sp, c, st[c]);
-    publish_position(a, s.b, 0, true);
+        for (int c = 0; c < kChunks; ++c) store_chunk(sp, c, st[c]);
+    } else {
+        // stream index of the interval the written state starts (read before
+        // the slot's position and interval count are published)
+        const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;
+        quantize_chunk<MODE, 0>(a, s, hrow, st[0], interval);
+        quantize_chunk<MODE, 1>(a, s, hrow, st[1], interval);
+        quantize_chunk<MODE, 2>(a, s, hrow, st[2], interval);
+        quantize_chunk<MODE, 3>(a, s, hrow, st[3], interval);
+    }
+    publish_position(a, s.b, 0, true, -1);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const ReplayParams &p, bool in_bf16, bool outputs, hipStream_t stream) {
+template <int MODE>
+static void launch_prefill_m(const ReplayParams &p, bool in_bf16, bool outputs, dim3 grid, dim3 block,
+                             hipStream_t stream) {
+    if (in_bf16) {
+        if (outputs) hipLaunchKernelGGL((prefill_kernel<uint16_t, true, MODE>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_kernel<uint16_t, false, MODE>), grid, block, 0, stream, p);
+    } else {
+        if (outputs) hipLaunchKernelGGL((prefill_kernel<float, true, MODE>), grid, block, 0, stream, p);
+        else hipLaunchKernelGGL((prefill_kernel<float, false, MODE>), grid, block, 0, stream, p);
+    }
+}
+
+hipError_t launch_prefill(const ReplayParams &p, bool in_bf16, bool outputs, int mode, hipStream_t stream) {
     if (p.batch == 0 || p.T == 0) return hipSuccess;
     dim3 grid(p.batch * p.wg_per_slot), block(64 * p.hpw);
-    if (in_bf16) {
-        if (outputs) hipLaunchKernelGGL((prefill_kernel<uint16_t, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((prefill_kernel<uint16_t, false>), grid, block, 0, stream, p);
-    } else {
-        if (outputs) hipLaunchKernelGGL((prefill_kernel<float, true>), grid, block, 0, stream, p);
-        else hipLaunchKernelGGL((prefill_kernel<float, false>), grid, block, 0, stream, p);
+    switch (mode) {
+        case -1: launch_prefill_m<-1>(p, in_bf16, outputs, grid, block, stream); break;
+        case kSplitBF16: launch_prefill_m<kSplitBF16>(p, in_bf16, outputs, grid, block, stream); break;
+        case kSplitE4M3: launch_prefill_m<kSplitE4M3>(p, in_bf16, outputs, grid, block, stream); break;
+        case kSharedFP4: launch_prefill_m<kSharedFP4>(p, in_bf16, outputs, grid, block, stream); break;
+        case kLowBF16: launch_prefill_m<kLowBF16>(p, in_bf16, outputs, grid, block, stream); break;
+        case kLowE4M3: launch_prefill_m<kLowE4M3>(p, in_bf16, outputs, grid, block, stream); break;
+        default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

@@ -89,13 +89,19 @@ __device__ __forceinline__ void store_chunk(const HeadState &hs, int c, const fl
 }
 
 // Last-arriving workgroup of slot b publishes the slot's new position (and
-// interval count).  Every workgroup of the slot read pos[b] before arriving.
+// interval count).  Every workgroup of the slot read pos[b] (as `seen`, or
+// -1 where the caller checks it otherwise) before arriving.  Two rows of one
+// call on the same slot are a race the caller must avoid; it shows up as more
+// than wg_per_slot arrivals before a reset, or as a position that changed
+// between a workgroup's read and its publication, and is flagged (kErrDup).
 __device__ __forceinline__ void publish_position(const ReplayParams &a, int b, int new_pos,
-                                                 bool committed) {
+                                                 bool committed, int seen) {
     __syncthreads();
     if (threadIdx.x == 0) {
         int old = atomicAdd(&a.work[b], 1);
+        if (old >= a.wg_per_slot) atomicOr(a.err, kErrDup);
         if (old == a.wg_per_slot - 1) {
+            if (seen >= 0 && a.pos[b] != seen) atomicOr(a.err, kErrDup);
             a.work[b] = 0;
             a.pos[b] = new_pos;
             if (committed) a.intv[b] += 1;
@@ -154,6 +160,7 @@ struct __align__(16) StepSmem {
 
 struct StepIn {
     int k, K;
+    int seen;   // pos[b] as read (before clamping)
     bool commit;
     size_t HP, GN;
     const void *xin, *Bin, *Cin, *dtin, *xb, *bb, *db;   // typed by the caller
@@ -166,6 +173,7 @@ template <typename TIn>
 __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s, int kmax) {
     StepIn in;
     int k = a.pos[s.b];
+    in.seen = k;
     if (k < 0 || k > kmax) {
         if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
         k = k < 0 ? 0 : kmax;
@@ -323,6 +331,7 @@ struct VerifySmem {
 
 struct VerifyIn {
     int k, KL;
+    int seen;   // pos[b] as read (before clamping)
     size_t HP, GN;
     const void *xin, *Bin, *Cin, *dtin, *xb, *bb, *db;
 };
@@ -331,6 +340,7 @@ template <typename TIn, int T>
 __device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const Slot &s, int kmax) {
     VerifyIn in;
     int k = a.pos[s.b];
+    in.seen = k;
     if (k < 0 || k > kmax) {
         if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
         k = k < 0 ? 0 : kmax;
@@ -637,11 +647,12 @@ struct CommitSmem {
 };
 
 template <bool ACCEPT>
-__device__ __forceinline__ int commit_count(const ReplayParams &a, const Slot &s, bool *commit) {
+__device__ __forceinline__ int commit_count(const ReplayParams &a, const Slot &s, bool *commit, int *seen) {
     // an accept follows a verify (k <= L-1); a flush also folds the up to
     // Lcap entries a deferred accept can leave
     const int kmax = ACCEPT ? a.L - 1 : a.Lcap;
     int k = a.pos[s.b];
+    *seen = k;
     if (k < 0 || k > kmax) {
         if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
         k = k < 0 ? 0 : kmax;
@@ -825,13 +836,16 @@ __device__ __forceinline__ float fold_prologue(const ReplayParams &a, const Slot
 // with the others' reads, while the last arrival knows they are all done.
 // Bin: the slot's [T,G,N] input B (contiguous, as are entries 0..T-1).
 template <typename TIn>
-__device__ __forceinline__ void publish_fold(const ReplayParams &a, int b, int new_pos, const TIn *Bin, int T) {
+__device__ __forceinline__ void publish_fold(const ReplayParams &a, int b, int new_pos, const TIn *Bin, int T,
+                                             int seen) {
     __shared__ int last;
     __syncthreads();
     if (threadIdx.x == 0) {
         const int old = atomicAdd(&a.work[b], 1);
+        if (old >= a.wg_per_slot) atomicOr(a.err, kErrDup);
         last = old == a.wg_per_slot - 1;
         if (last) {
+            if (a.pos[b] != seen) atomicOr(a.err, kErrDup);
             a.work[b] = 0;
             a.pos[b] = new_pos;
             a.intv[b] += 1;

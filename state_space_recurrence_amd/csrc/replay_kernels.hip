@@ -71,7 +71,7 @@ replay_step_kernel(ReplayParams a) {
     a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + s.prow] = lam * y0 + ybuf;
 
     if (!in.commit) step_append<TIn>(a, s, in);
-    publish_position(a, s.b, in.commit ? 0 : in.K, in.commit);
+    publish_position(a, s.b, in.commit ? 0 : in.K, in.commit, in.seen);
 }
 
 // ------------------------------------------------------------------------
@@ -125,7 +125,7 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
         a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + s.prow] = lam * y0 + ybuf;
         if (!in.commit) step_append<TIn>(a, s, in);
     }
-    publish_position(a, s.b, in.commit ? 0 : in.K, in.commit);
+    publish_position(a, s.b, in.commit ? 0 : in.K, in.commit, in.seen);
 }
 
 // ------------------------------------------------------------------------
@@ -246,7 +246,7 @@ replay_fold_verify_kernel(ReplayParams a) {
     }
     in.k = 0;
     verify_append<TIn, T, false>(a, s, in);
-    publish_fold<TIn>(a, s.b, 0, reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.row * T * in.GN, T);
+    publish_fold<TIn>(a, s.b, 0, reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.row * T * in.GN, T, in.seen);
 }
 
 // ------------------------------------------------------------------------
@@ -261,7 +261,8 @@ __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
     bool commit;
-    const int K = commit_count<ACCEPT>(a, s, &commit);
+    int seen;
+    const int K = commit_count<ACCEPT>(a, s, &commit, &seen);
     if (commit) {
         const HeadState sp = head_state(a.ckpt, s, a.H);
         float4 buf[kNB][kPerChunk];
@@ -280,7 +281,7 @@ __global__ void __launch_bounds__(256) replay_commit_kernel(ReplayParams a) {
             if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
         }
     }
-    publish_position(a, s.b, commit ? 0 : K, commit);
+    publish_position(a, s.b, commit ? 0 : K, commit, seen);
 }
 
 // Deferred accept: pos += n_keep only; a slot reaching L keeps its entries

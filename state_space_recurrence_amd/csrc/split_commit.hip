@@ -13,7 +13,8 @@ __global__ void __launch_bounds__(256) split_commit_kernel(ReplayParams a) {
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
     bool commit;
-    const int K = commit_count<ACCEPT>(a, s, &commit);
+    int seen;
+    const int K = commit_count<ACCEPT>(a, s, &commit, &seen);
     if (commit) {
         const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;   // read only where a commit needs it
         const size_t GN = (size_t)a.G * kN;
@@ -23,7 +24,7 @@ __global__ void __launch_bounds__(256) split_commit_kernel(ReplayParams a) {
         const float lam = commit_prologue<TIn, KMAX, false>(a, s, K, sm.l, sm.w, sm.cs, unused);
         commit_head<KMAX, MODE>(a, s, lam, sm.cs[s.wave], sB, interval);
     }
-    publish_position(a, s.b, commit ? 0 : K, commit);
+    publish_position(a, s.b, commit ? 0 : K, commit, seen);
 }
 
 // Quantise an fp32 state into the mode's formats with stream index intv[b].

@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(MODE =
     }
 
     if (!in.commit) step_append<TIn>(a, s, in);
-    publish_position(a, s.b, in.commit ? 0 : in.K, in.commit);
+    publish_position(a, s.b, in.commit ? 0 : in.K, in.commit, in.seen);
 }
 
 #define RSSM_MODE_SWITCH(MODEVAR, CALL)                                  \

@@ -125,8 +125,10 @@ def test_prefill_arguments_checked(rs):
     d = _desc(rs)
     assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), -1, 0, None, None, None, None, None, None) == -1
     assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), 4, 2, None, None, None, None, None, None) == -1
+    # a low-precision state is accepted (the missing state buffers are what is refused)
     d = _desc(rs, ckpt_dtype=rs.BF16, out_dtype=rs.FP4_E2M1)
-    assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), 4, 0, None, None, None, None, None, None) == -2
+    assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), 4, 0, None, None, None, None, None, None) == -1
+    assert "state" in L.replayssm_last_error().decode()
     d = _desc(rs, batch=0)
     assert L.replayssm_prefill(ctypes.byref(d), ctypes.byref(st), 4, 0, None, None, None, None, None, None) == 0
 

@@ -115,3 +115,56 @@ def test_prefill_edge_cases(rs):
     rs.prefill(ls, _bt(x).cuda(), _bt(Bm).cuda(), _bt(Cm).cuda(), _bt(dt).cuda())
     with pytest.raises(rs.ReplaySSMError, match="device"):
         rs.check_device_errors(ls)
+
+
+SPLIT_FORMATS = ["split-bf16", "split-e4m3", "shared-fp4", "low-bf16", "low-e4m3"]
+SEED, LAYER = 0x5EED_0000_1234_ABCD, 3
+
+
+def _update_source(rs, fmt, ls):
+    """The decoded state a low-precision layer updates from (exactly)."""
+    import numpy as np
+    if fmt == "shared-fp4":
+        return oracle.fp4_dequantize(ls.out_q.cpu().numpy(), ls.out_scale.cpu().numpy())
+    u = ls.ckpt.cpu().numpy()
+    return oracle.bf16_decode_array(u.view(np.uint16)) if "bf16" in fmt else oracle.e4m3_decode_array(u)
+
+
+@pytest.mark.parametrize("from_zero", [False, True])
+@pytest.mark.parametrize("fmt", SPLIT_FORMATS)
+def test_prefill_into_low_precision_state(rs, fmt, from_zero):
+    """Prefill into a low-precision state: the prompt runs in fp32 on chip
+    from the decoded update source (or zero) and the final state is written
+    once like a commit.  Bars: prompt outputs and the pre-rounding final
+    state (debug dump) at 2e-5 against the oracle's recurrence from the same
+    decoded start; stored bytes bit-exact against the oracle's quantisers
+    applied to the dumped values (stream index intv + 1, the slot's element
+    offset); positions 0 and intv + 1."""
+    import numpy as np
+    w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
+    batch, Tp = 3, 37
+    A, D, S0, x, Bm, Cm, dt = _case(rs, w, batch, Tp, layer=1, stream=23)
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=16, in_dtype=x.dtype, state_format=fmt,
+                       seed=SEED, layer_id=LAYER, debug_prequant=True)
+    ls.intv.fill_(4)
+    rs.load_checkpoint(ls, S0.cuda())
+    start = np.zeros(S0.shape) if from_zero else _update_source(rs, fmt, ls)
+    y = rs.prefill(ls, _bt(x).cuda(), _bt(Bm).cuda(), _bt(Cm).cuda(), _bt(dt).cuda(), from_zero=from_zero)
+    rs.check_device_errors(ls)
+    S_ref, y_ref = oracle.recurrent(start, x, Bm, Cm, dt, A, D, w.groups)
+    for t in range(Tp):
+        assert_close(y[:, t].cpu(), y_ref[t], f"{fmt} prompt output {t}")
+    dump = ls.debug_prequant.cpu()
+    assert_close(dump, S_ref, f"{fmt} final state before rounding")
+    assert ls.pos.cpu().tolist() == [0] * batch and ls.intv.cpu().tolist() == [5] * batch
+    v = dump.numpy().astype(np.float32)
+    if fmt != "shared-fp4":
+        ufmt = "bf16" if "bf16" in fmt else "e4m3"
+        ref = oracle.sr_quantize(v.reshape(-1), ufmt, SEED, LAYER, 5).reshape(v.shape)
+        got = ls.ckpt.cpu().numpy()
+        got = got.view(np.uint16) if ufmt == "bf16" else got
+        assert np.array_equal(got, ref), f"{fmt}: update checkpoint bytes differ"
+    if fmt.startswith("split") or fmt == "shared-fp4":
+        codes, scales = oracle.fp4_quantize(v)
+        assert np.array_equal(ls.out_q.cpu().numpy(), codes), f"{fmt}: FP4 codes differ"
+        assert np.array_equal(ls.out_scale.cpu().numpy(), scales), f"{fmt}: FP4 scales differ"

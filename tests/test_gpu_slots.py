@@ -194,3 +194,25 @@ def test_prefill_into_slots(rs):
         for t in range(21):
             assert_close(y[r, t].cpu(), y_ref[t, 0], f"slot {b} token {t}")
     assert torch.equal(pool.ckpt[1], S0[1].cuda())
+
+
+@pytest.mark.parametrize("heads,batch", [(8, 16), (96, 40)])
+def test_duplicate_slots_are_flagged(rs, heads, batch):
+    """Every row of a call on one slot (a race the caller must avoid): the
+    position-publishing kernel sees more arrivals on the slot than one row
+    brings and records it in the sticky error word.  All accesses stay in
+    bounds (the racing rows write the same slot's valid entries), so the
+    kernels end normally; only the slot's contents are undefined.  Both step
+    kernels: 16 rows of 8 one-head workgroups (row split) and 40 rows of 24
+    four-head tiles."""
+    w = synth.WORKLOADS["tiny"] if heads == 8 else synth.WORKLOADS["4b"]
+    A, D = synth.layer_params(w, 0)
+    x, Bm, Cm, dt = synth.token_inputs(w, 0, 1, batch=batch, stream=37)
+    pool = rs.LayerState(3, w.heads, w.groups, A, D, in_dtype=x.dtype)
+    before = {k: v.clone() for k, v in pool.tensors().items()}
+    rs.step(pool, x[0].cuda(), Bm[0].cuda(), Cm[0].cuda(), dt[0].cuda(), slots=_idx([1] * batch))
+    with pytest.raises(rs.ReplaySSMError, match="same slot"):
+        rs.check_device_errors(pool)
+    for b in (0, 2):   # the other slots are untouched
+        assert torch.equal(pool.ckpt[b], before["ckpt"][b]) and pool.pos[b].item() == 0
+    rs.check_device_errors(pool)   # the flag was cleared by the read
