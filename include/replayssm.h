@@ -134,6 +134,9 @@ typedef struct rssm_desc {
                              covers `batch` rows, mapped to slots by rssm_state.slot_idx */
 } rssm_desc;
 
+/* Extra int32 words of rssm_state.commit_list beyond one per slot. */
+#define RSSM_COMMIT_LIST_EXTRA 32
+
 /* Device buffers of one layer (host struct of device pointers). */
 typedef struct rssm_state {
     void *ckpt;           /* [B,H,P,N] ckpt_dtype (2, 1 or 4 bytes per element); NULL when shared_lowp */
@@ -153,6 +156,10 @@ typedef struct rssm_state {
                                 read or written for it); NULL = row b uses slot b.  Slots of one call
                                 must be distinct (a duplicate is flagged when detected, see above).
                                 Rows mapped outside 0..S-1 are skipped and flagged */
+    int32_t *commit_list; /* [S + RSSM_COMMIT_LIST_EXTRA] int32, zero-initialise once: the slots whose
+                             interval a low-precision step closes, committed by the step's second
+                             launch (needed by replayssm_step with BF16 / FP8 / shared-FP4 states;
+                             left all zero by every call; unused, may be NULL, otherwise) */
 } rssm_state;
 
 /*
@@ -176,11 +183,12 @@ int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x,
  * cannot allocate device memory at any point (code under HIP graph capture,
  * tight serving loops, harnesses that forbid allocation).  Same arguments,
  * kernels and results as replayssm_step (bit-identical outputs and state),
- * but the per-slot arrival counters live in library scratch: a device array
- * of 65536 counters (256 KB) per GPU, set up on the first call on that
- * device and held until the process ends.  Of st->work only the sticky
- * error word work[n_slots] is used (read it with
- * replayssm_check_device_errors as usual).  Calls nothing that allocates.
+ * but the per-slot arrival counters and the low-precision states' commit
+ * list live in library scratch: a device array of 65536 counters and a
+ * 65536-slot list (512 KB) per GPU, set up on the first call on that device
+ * and held until the process ends.  Of st->work only the sticky error word
+ * work[n_slots] is used (read it with replayssm_check_device_errors as
+ * usual); st->commit_list is not used.  Calls nothing that allocates.
  * Every call on one GPU shares that GPU's counters: calls that overlap on
  * one GPU (different streams, different layers) race and must be ordered by
  * the caller.  Returns RSSM_E_CAPACITY when the state holds more than 65536

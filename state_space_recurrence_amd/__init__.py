@@ -50,8 +50,12 @@ class RssmState(ctypes.Structure):
         ("xbuf", ctypes.c_void_p), ("bbuf", ctypes.c_void_p), ("dtbuf", ctypes.c_void_p),
         ("pos", ctypes.c_void_p), ("intv", ctypes.c_void_p), ("work", ctypes.c_void_p),
         ("A", ctypes.c_void_p), ("D", ctypes.c_void_p), ("debug_prequant", ctypes.c_void_p),
-        ("slot_idx", ctypes.c_void_p),
+        ("slot_idx", ctypes.c_void_p), ("commit_list", ctypes.c_void_p),
     ]
+
+
+#: extra int32 words of the commit list beyond one per slot (RSSM_COMMIT_LIST_EXTRA)
+COMMIT_LIST_EXTRA = 32
 
 
 _LIB = None
@@ -182,6 +186,7 @@ class LayerState:
         self.pos = torch.zeros(batch, dtype=torch.int32, device=dev)
         self.intv = torch.zeros(batch, dtype=torch.int32, device=dev)
         self.work = torch.zeros(batch + 1, dtype=torch.int32, device=dev)
+        self.commit_list = torch.zeros(batch + COMMIT_LIST_EXTRA, dtype=torch.int32, device=dev)
         if tuple(A.shape) != (heads,) or tuple(D.shape) != (heads,):
             raise ReplaySSMError(f"A and D must have shape ({heads},), got {tuple(A.shape)}, {tuple(D.shape)}")
         self.A = A.to(device=dev, dtype=torch.float32).contiguous()
@@ -197,7 +202,8 @@ class LayerState:
     def cstate(self) -> RssmState:
         return RssmState(_ptr(self.ckpt), _ptr(self.out_q), _ptr(self.out_scale), _ptr(self.xbuf),
                          _ptr(self.bbuf), _ptr(self.dtbuf), _ptr(self.pos), _ptr(self.intv),
-                         _ptr(self.work), _ptr(self.A), _ptr(self.D), _ptr(self.debug_prequant))
+                         _ptr(self.work), _ptr(self.A), _ptr(self.D), _ptr(self.debug_prequant),
+                         None, _ptr(self.commit_list))
 
     def tensors(self):
         t = {"ckpt": self.ckpt, "out_q": self.out_q, "out_scale": self.out_scale, "xbuf": self.xbuf,

@@ -132,6 +132,7 @@ rssm::ReplayParams replay_params(const rssm_desc *d, const rssm_state *s) {
     p.intv = s->intv;
     p.work = s->work;
     p.err = s->work + nslots_of(d);
+    p.clist = s->commit_list;
     p.A = s->A;
     p.D = s->D;
     p.batch = d->batch;
@@ -159,6 +160,13 @@ rssm::ReplayParams replay_params(const rssm_desc *d, const rssm_state *s) {
         int rc_ = (expr);           \
         if (rc_ != RSSM_OK) return rc_; \
     } while (0)
+
+// Low-precision step: outputs and appends, then the commit pass over the
+// slots whose interval that step closed.
+int split_step(const rssm::ReplayParams &p, bool bf, int mode, hipStream_t stream) {
+    RSSM_TRY(hip_status(rssm::launch_split_step(p, bf, mode, stream), "split step launch"));
+    return hip_status(rssm::launch_split_commit_list(p, bf, mode, stream), "split commit launch");
+}
 
 }  // namespace
 
@@ -188,7 +196,10 @@ int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x, c
     p.y = y;
     const bool bf = desc->in_dtype == RSSM_BF16;
     const int mode = split_mode(desc);
-    if (mode >= 0) return hip_status(rssm::launch_split_step(p, bf, mode, stream), "split step launch");
+    if (mode >= 0) {
+        if (!st->commit_list) return fail(RSSM_E_ARG, "step: a low-precision state needs state->commit_list");
+        return split_step(p, bf, mode, stream);
+    }
     return hip_status(rssm::launch_replay_step(p, bf, stream), "replay step launch");
 }
 
@@ -202,7 +213,7 @@ int replayssm_step_noalloc(const rssm_desc *desc, const rssm_state *st, const vo
     if (desc->batch == 0) return RSSM_OK;
     if (!x || !B || !C || !dt || !y) return fail(RSSM_E_ARG, "step_noalloc: an input/output pointer is NULL");
     rssm::ReplayParams p = replay_params(desc, st);
-    RSSM_TRY(hip_status(rssm::noalloc_work(&p.work, stream), "step_noalloc: library scratch"));
+    RSSM_TRY(hip_status(rssm::noalloc_work(&p.work, &p.clist, stream), "step_noalloc: library scratch"));
     p.x = x;
     p.Bm = B;
     p.Cm = C;
@@ -210,7 +221,7 @@ int replayssm_step_noalloc(const rssm_desc *desc, const rssm_state *st, const vo
     p.y = y;
     const bool bf = desc->in_dtype == RSSM_BF16;
     const int mode = split_mode(desc);
-    if (mode >= 0) return hip_status(rssm::launch_split_step(p, bf, mode, stream), "split step launch");
+    if (mode >= 0) return split_step(p, bf, mode, stream);
     return hip_status(rssm::launch_replay_step(p, bf, stream), "replay step launch");
 }
 

@@ -21,6 +21,7 @@ struct ReplayParams {
     int32_t *intv;          // [B]
     int32_t *work;          // [nslots] per-slot arrival counters (zero between calls)
     int32_t *err;           // sticky device error word (work[nslots] of the caller's state)
+    int32_t *clist;         // low-precision step: slots whose interval closed (see kListHead)
     const float *A;         // [H]
     const float *D;         // [H]
     const int32_t *n_keep;  // [B] (accept)
@@ -79,10 +80,18 @@ hipError_t launch_probe(int mode, const float *src, float *dst, size_t bytes, in
 hipError_t launch_recurrent_accept(int32_t *sel, const int32_t *n_keep, int batch, int T,
                                    int Tmax, hipStream_t s);
 
+// Commit list of the low-precision step (int32, kListHead + slots entries):
+// [0] number of listed slots, [1 .. kListGroups + 1] completion counters of
+// the commit pass, slot indices from kListHead.  All zero between calls.
+constexpr int kListGroups = 16;
+constexpr int kListHead = 32;
+hipError_t launch_split_commit_list(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
+
 // Library scratch for callers that cannot allocate: per-slot arrival counters
-// of up to kNoAllocMaxSlots slots, one array per device.  *work receives the
-// current device's copy (set up, and cleared on `s`, on its first use).
+// of up to kNoAllocMaxSlots slots and a commit list of as many slots, one
+// array per device.  *work / *clist receive the current device's copies (set
+// up, and cleared on `s`, on its first use).
 constexpr int kNoAllocMaxSlots = 1 << 16;
-hipError_t noalloc_work(int32_t **work, hipStream_t s);
+hipError_t noalloc_work(int32_t **work, int32_t **clist, hipStream_t s);
 
 }  // namespace rssm

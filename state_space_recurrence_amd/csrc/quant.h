@@ -60,16 +60,16 @@ __device__ __forceinline__ Philox4 philox4x32_10(uint32_t c0, uint32_t c1, uint3
 // ------------------------------------------------------------------- bf16 --
 __device__ __forceinline__ float bf16_decode(uint32_t code16) { return __uint_as_float(code16 << 16); }
 
+// Written without branches (selects only): the quantisers run on every
+// element of a commit.  An infinity needs no case of its own: its code
+// 0x7F80 is above the saturation code and is clamped like an overflow.
 __device__ __forceinline__ uint32_t bf16_sr(float v, uint32_t r16) {
     const uint32_t bits = __float_as_uint(v);
     const uint32_t mag = bits & 0x7FFFFFFFu;
-    if (mag > 0x7F800000u) return 0x7FC0u;                     // NaN
     const uint32_t sign = (bits >> 16) & 0x8000u;
-    if (mag == 0x7F800000u) return sign | 0x7F7Fu;             // inf saturates
-    uint32_t code = mag >> 16;
-    if (r16 < (mag & 0xFFFFu)) code += 1;                       // carries into the exponent
-    if (code > 0x7F7Fu) code = 0x7F7Fu;                         // saturate instead of inf
-    return sign | code;
+    uint32_t code = (mag >> 16) + (r16 < (mag & 0xFFFFu) ? 1u : 0u);   // a carry moves into the exponent
+    code = code < 0x7F7Fu ? code : 0x7F7Fu;                             // saturate instead of inf
+    return mag > 0x7F800000u ? 0x7FC0u : (sign | code);                 // NaN -> canonical NaN
 }
 
 // ------------------------------------------------------------------- E4M3 --
@@ -130,33 +130,31 @@ constexpr uint32_t kE4M3MaxBits = 0x43E00000u;   // 448.0f
 __device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t r16) {
     const uint32_t bits = __float_as_uint(v);
     const uint32_t mag = bits & 0x7FFFFFFFu;
-    if (mag > 0x7F800000u) return 0x7Fu;                      // NaN
     const uint32_t sign = (bits >> 24) & 0x80u;
-    if (mag >= kE4M3MaxBits) return sign | 0x7Eu;              // saturate at 448
-    const GridSplit g = e4m3_split(mag);
-    // up iff r16 * 2^s < rem * 2^16  (s >= 20 here)
-    const int sh = g.s - 16;
-    const bool up = sh >= 40 ? (r16 == 0u && g.rem != 0u) : (((uint64_t)r16 << sh) < (uint64_t)g.rem);
-    uint32_t code = e4m3_encode_grid(g.lo + (up ? 1u : 0u), g.qe);
-    if (code > 0x7Eu) code = 0x7Eu;
-    return sign | code;
+    const GridSplit g = e4m3_split(mag < kE4M3MaxBits ? mag : 0u);
+    // up iff r16 * 2^s < rem * 2^16, i.e. r16 < ceil(rem / 2^d) with d = s - 16
+    // (d >= 4); rem < 2^24, so clamping d at 31 keeps the ceiling exact
+    const int d = g.s - 16 < 31 ? g.s - 16 : 31;
+    const uint32_t ceilq = (g.rem >> d) + ((g.rem & ((1u << d) - 1u)) != 0u ? 1u : 0u);
+    uint32_t code = e4m3_encode_grid(g.lo + (r16 < ceilq ? 1u : 0u), g.qe);
+    code = code < 0x7Eu ? code : 0x7Eu;
+    code = mag >= kE4M3MaxBits ? 0x7Eu : code;                  // saturate at 448 (inf too)
+    return mag > 0x7F800000u ? 0x7Fu : (sign | code);          // NaN -> canonical NaN
 }
 
 // Round-to-nearest-even of a non-negative finite fp32 magnitude to E4M3,
 // saturating at 448.
 __device__ __forceinline__ uint32_t e4m3_rne_mag(float m) {
     const uint32_t mag = __float_as_uint(m);
-    if (mag >= kE4M3MaxBits) return 0x7Eu;
-    const GridSplit g = e4m3_split(mag);
-    // compare rem with half a quantum (2^(s-1)); ties to even k
-    bool up;
-    if (g.s >= 33) up = false;                          // rem < 2^24 <= half quantum
-    else {
-        const uint64_t half = (uint64_t)1 << (g.s - 1);
-        up = (uint64_t)g.rem > half || ((uint64_t)g.rem == half && (g.lo & 1u));
-    }
+    const GridSplit g = e4m3_split(mag < kE4M3MaxBits ? mag : 0u);
+    // compare rem with half a quantum (2^(s-1)); ties to even k.  rem < 2^24,
+    // so from s - 1 >= 24 on the half quantum is larger and nothing rounds up
+    const bool small = g.s - 1 < 24;
+    const uint32_t half = 1u << (small ? g.s - 1 : 0);
+    const bool up = small & ((g.rem > half) | ((g.rem == half) & ((g.lo & 1u) != 0u)));   // no short circuits
     uint32_t code = e4m3_encode_grid(g.lo + (up ? 1u : 0u), g.qe);
-    return code > 0x7Eu ? 0x7Eu : code;
+    code = code < 0x7Eu ? code : 0x7Eu;
+    return mag >= kE4M3MaxBits ? 0x7Eu : code;
 }
 
 // ------------------------------------------------------------------- FP4 --
@@ -168,20 +166,22 @@ __device__ __forceinline__ float e2m1_decode(uint32_t code4) {
 }
 
 // Scale code of a 32-element block from its max magnitude: RNE_E4M3(amax/6),
-// decided exactly: start from the rounded quotient and fix the result with
-// exact comparisons against 6 x the midpoints between neighbouring codes.
+// decided exactly: start from the code of amax * (1/6) (within one code of
+// the exact one: the product is within an ulp of the quotient, the codes are
+// 2^-3 apart relatively) and fix it with exact comparisons against 6 x the
+// midpoints between neighbouring codes.
+// Both corrections are evaluated unconditionally (no branches; codes at the
+// ends of the range compare against a midpoint that cannot be reached).
 __device__ __forceinline__ uint32_t fp4_scale_code(float amax) {
-    uint32_t c = e4m3_rne_mag(amax / 6.0f);
-    // step up while amax is beyond the midpoint to the next code
-    if (c < 0x7Eu) {
-        const float mid6 = 3.0f * (e4m3_decode(c) + e4m3_decode(c + 1));   // 6 * midpoint, exact
-        if (amax > mid6 || (amax == mid6 && (c & 1u))) c += 1;
-    }
-    if (c > 0u) {
-        const float mid6 = 3.0f * (e4m3_decode(c - 1) + e4m3_decode(c));
-        if (amax < mid6 || (amax == mid6 && (c & 1u))) c -= 1;
-    }
-    return c;
+    uint32_t c = e4m3_rne_mag(amax * (1.0f / 6.0f));
+    // step up when amax is beyond the midpoint to the next code (none above 448)
+    const float up6 = 3.0f * (e4m3_decode(c) + e4m3_decode(c + 1u));   // 6 * midpoint, exact
+    const bool up = (c < 0x7Eu) & ((amax > up6) | ((amax == up6) & ((c & 1u) != 0u)));
+    c += up ? 1u : 0u;
+    // step down when amax is below the midpoint to the previous code (none below 0)
+    const float dn6 = 3.0f * (e4m3_decode(c - 1u) + e4m3_decode(c));
+    const bool dn = (c > 0u) & ((amax < dn6) | ((amax == dn6) & ((c & 1u) != 0u)));
+    return c - (dn ? 1u : 0u);
 }
 
 // E2M1 code (sign in bit 3) of v against scale s > 0, by exact threshold
@@ -195,6 +195,7 @@ __device__ __forceinline__ Fp4Thresholds fp4_thresholds(float s) {
     return {0.25f * s, 0.75f * s, 1.25f * s, 1.75f * s, 2.5f * s, 3.5f * s, 5.0f * s};
 }
 
+// The code is the number of thresholds |v| passes (counted without branches).
 __device__ __forceinline__ uint32_t fp4_encode(float v, const Fp4Thresholds &t, bool zero_scale) {
     const float a = fabsf(v);
     uint32_t k = (a > t.t025) + (a >= t.t075) + (a > t.t125) + (a >= t.t175) + (a > t.t250) +

@@ -121,15 +121,33 @@ __device__ __forceinline__ int cs_index(int hf, int c, int j, int m) {
 // workgroup's heads share one group): entries j < nbuf from the buffer, entry
 // nbuf (when < K) from the current input, entries >= K zero.  Visible after
 // the next __syncthreads.
+// Four pieces per thread are requested together (entries past K re-read
+// entry K - 1 and are zeroed afterwards), so the staging waits for one
+// memory latency, not one per piece.
 template <typename TIn, int KMAX>
 __device__ __forceinline__ void stage_B(float (*sB)[kN], const TIn *bb, const TIn *Bin, size_t GN, int nbuf,
                                         int K) {
-#pragma unroll 4
-    for (int q = threadIdx.x; q < KMAX * kN / 4; q += blockDim.x) {
-        const int j = q / (kN / 4), n = 4 * (q - j * (kN / 4));
-        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (j < K) v = io<TIn>::load4((j < nbuf ? bb + (size_t)j * GN : Bin) + n);
-        *reinterpret_cast<float4 *>(&sB[j][n]) = v;
+    constexpr int total = KMAX * kN / 4;
+    for (int q0 = threadIdx.x; q0 < total; q0 += 4 * blockDim.x) {
+        typename io<TIn>::raw4 r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            int q = q0 + u * blockDim.x;
+            q = q < total ? q : total - 1;
+            int j = q / (kN / 4);
+            const int n = 4 * (q - j * (kN / 4));
+            j = j < K ? j : K - 1;
+            r[u] = io<TIn>::load_raw4((j < nbuf ? bb + (size_t)j * GN : Bin) + n);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * blockDim.x;
+            if (q < total) {
+                const int j = q / (kN / 4), n = 4 * (q - j * (kN / 4));
+                const float4 v = io<TIn>::widen(r[u]);
+                *reinterpret_cast<float4 *>(&sB[j][n]) = j < K ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+            }
+        }
     }
 }
 
@@ -150,11 +168,24 @@ __device__ __forceinline__ void store16(void *p, uint4 v) { *reinterpret_cast<ui
 // ------------------------------------------------------------------------
 template <typename TIn, int KMAX>
 struct __align__(16) StepSmem {
+    static constexpr bool kCommit = true;
     float gram[KMAX];              // B_j . C  (one group per workgroup)
     float cs[kMaxHpw][kP * KMAX];  // commit coefficients w_j x_j[r] (cs_index layout)
     union {
         TIn X[kMaxHpw][KMAX][kP];  // prologue, per head: x rows of the K entries as stored (rows >= K unset)
         float B[KMAX][kN];         // commit steps, after the prologue: the group's B entries, zero past K
+    } u;
+};
+
+// The same for steps that never commit (the low-precision step, whose
+// interval-closing commits run in a kernel of their own): no coefficient
+// table, so the workgroup's LDS is a third of StepSmem's.
+template <typename TIn, int KMAX>
+struct __align__(16) StepSmemNoCommit {
+    static constexpr bool kCommit = false;
+    float gram[KMAX];
+    union {
+        TIn X[kMaxHpw][KMAX][kP];
     } u;
 };
 
@@ -199,9 +230,9 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
 // *lam and sum_j w_j g_j x_j[prow] + D x[prow] in *ybuf.  The head's x rows
 // arrive with a few 16-byte loads and are read back per row from LDS, so the
 // prologue holds few registers next to the checkpoint chunks in flight.
-template <typename TIn, int KMAX>
+template <typename TIn, int KMAX, typename SM>
 __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot &s, const StepIn &in,
-                                              int prow, StepSmem<TIn, KMAX> &sm, float *lam, float *ybuf) {
+                                              int prow, SM &sm, float *lam, float *ybuf) {
     const int k = in.k, K = in.K;
     const TIn *xin = static_cast<const TIn *>(in.xin);
     const TIn *Bin = static_cast<const TIn *>(in.Bin);
@@ -282,17 +313,19 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
         }
     }
     *ybuf = yb;
-    if (in.commit) {
-        // row prow of the commit coefficients; any lane -> row bijection fills them all
-        const int i = prow >> 1, hf = prow & 1;
+    if constexpr (SM::kCommit) {
+        if (in.commit) {
+            // row prow of the commit coefficients; any lane -> row bijection fills them all
+            const int i = prow >> 1, hf = prow & 1;
 #pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
-            const float cf = w * io<TIn>::load1(xrow + j * kP);
-            sm.cs[s.wave][cs_index<KMAX>(hf, i & 3, j, i >> 2)] = (j < K) ? cf : 0.f;
+            for (int j = 0; j < KMAX; ++j) {
+                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
+                const float cf = w * io<TIn>::load1(xrow + j * kP);
+                sm.cs[s.wave][cs_index<KMAX>(hf, i & 3, j, i >> 2)] = (j < K) ? cf : 0.f;
+            }
+            __syncthreads();   // every head is done with its x rows; B takes their place
+            stage_B<TIn, KMAX>(sm.u.B, bb, Bin, in.GN, k, K);
         }
-        __syncthreads();   // every head is done with its x rows; B takes their place
-        stage_B<TIn, KMAX>(sm.u.B, bb, Bin, in.GN, k, K);
     }
     __syncthreads();
 }

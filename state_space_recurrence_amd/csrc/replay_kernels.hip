@@ -457,12 +457,12 @@ hipError_t launch_load_f32(const ReplayParams &p, hipStream_t stream) {
 }
 
 // ------------------------------------------------ no-allocation scratch --
-// Per-slot arrival counters for callers that cannot allocate (or bring) the
-// workspace: a file-scope device array, one copy per device, held until the
-// process ends.  Host code never passes the array's name to a kernel (on the
+// Per-slot arrival counters and the low-precision step's commit list for
+// callers that cannot allocate (or bring) them: a file-scope device array,
+// one copy per device, held until the process ends.  Host code never passes the array's name to a kernel (on the
 // host it is only a stand-in for the symbol); it uses the device address
 // hipGetSymbolAddress returns for the current device.
-static __device__ __align__(256) int32_t scratch[kNoAllocMaxSlots];
+static __device__ __align__(256) int32_t scratch[2 * kNoAllocMaxSlots + kListHead];
 
 namespace {
 
@@ -476,7 +476,7 @@ int32_t *g_scratch[kMaxDevices] = {};
 
 }  // namespace
 
-hipError_t noalloc_work(int32_t **work, hipStream_t stream) {
+hipError_t noalloc_work(int32_t **work, int32_t **clist, hipStream_t stream) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
@@ -488,12 +488,13 @@ hipError_t noalloc_work(int32_t **work, hipStream_t stream) {
         if (e != hipSuccess) return e;
         // the counters must start at zero (every complete call leaves them so)
         hipLaunchKernelGGL(zero_i32_kernel, dim3(64), dim3(256), 0, stream, static_cast<int32_t *>(ptr),
-                           kNoAllocMaxSlots);
+                           2 * kNoAllocMaxSlots + kListHead);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         g_scratch[dev] = static_cast<int32_t *>(ptr);
     }
     *work = g_scratch[dev];
+    *clist = g_scratch[dev] + kNoAllocMaxSlots;
     return hipSuccess;
 }
 

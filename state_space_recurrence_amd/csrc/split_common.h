@@ -89,10 +89,12 @@ __device__ __forceinline__ float4 decode_row4(typename Raw4<UB>::T r) {
                            bf16_decode(r.y >> 16));
     } else if constexpr (UB == 8) {
         return e4m3_decode4(r);
-    } else {
+    } else {   // two codes per byte, decoded by the packed FP4 -> f32 conversion (exact, unit scale)
         const float s = e4m3_decode(r >> 16);
-        return make_float4(e2m1_decode(r & 0xFu) * s, e2m1_decode((r >> 4) & 0xFu) * s,
-                           e2m1_decode((r >> 8) & 0xFu) * s, e2m1_decode((r >> 12) & 0xFu) * s);
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        const f2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r, 1.0f, 0);
+        const f2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(r, 1.0f, 1);
+        return make_float4(lo.x * s, lo.y * s, hi.x * s, hi.y * s);
     }
 }
 
