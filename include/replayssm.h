@@ -324,6 +324,25 @@ const char *replayssm_last_error(void);
 int replayssm_check_device_errors(const rssm_state *st, int32_t n_slots, hipStream_t stream);
 
 /*
+ * Self-check of the device conversions the low-precision commit relies on
+ * (a diagnostic for the hardware, not a compute call).  For every fp32 bit
+ * pattern p with begin <= p < end (end <= 2^32), NaNs skipped, it counts
+ *   counts[0]: patterns where gfx950's f32 -> E2M1 conversion at unit scale
+ *              differs from the exact round-to-nearest-even FP4 encoding
+ *              (saturating at 6, sign kept) the quantiser defines; the commit
+ *              takes FP4 codes from that conversion bracketed from both sides
+ *              of |v| / scale (precision split, article section 4);
+ *   counts[1]: patterns with |v| <= 0x7F7F0000 where bf16 stochastic rounding
+ *              by integer addition differs from the selecting form (a draw
+ *              hashed from the pattern).
+ * counts: device array of 2 unsigned 64-bit counters, zeroed by the caller;
+ * the kernel adds to them.  Asynchronous on stream; RSSM_E_ARG for a NULL
+ * counts or begin > end or end > 2^32.  Both counts are 0 on a conforming
+ * device.
+ */
+int replayssm_check_conversions(uint64_t begin, uint64_t end, unsigned long long *counts, hipStream_t stream);
+
+/*
  * Diagnostic: stream `bytes` (a multiple of 16) through HBM with the same
  * 16-byte non-temporal accesses as the state-streaming kernels, so callers
  * can time the practical ceiling next to the kernels' achieved bandwidth.

@@ -96,6 +96,8 @@ def lib() -> ctypes.CDLL:
         L.replayssm_version.restype = ctypes.c_char_p
         L.replayssm_hbm_probe.argtypes = [i32, _vp, _vp, ctypes.c_size_t, i32, _vp]
         L.replayssm_hbm_probe.restype = ctypes.c_int
+        L.replayssm_check_conversions.argtypes = [ctypes.c_uint64, ctypes.c_uint64, _vp, _vp]
+        L.replayssm_check_conversions.restype = ctypes.c_int
         for name in ("replayssm_step", "replayssm_step_noalloc", "replayssm_verify", "replayssm_accept", "replayssm_accept_deferred",
                      "replayssm_commit", "replayssm_prefill",
                      "replayssm_load_checkpoint", "replayssm_recurrent_step",
@@ -348,6 +350,15 @@ def hbm_probe(mode: int, src: torch.Tensor, dst: torch.Tensor, grid: int, stream
     """Launch the library's HBM streaming probe (0 = read src, 1 = copy src to dst)."""
     _check(lib().replayssm_hbm_probe(mode, _ptr(src), _ptr(dst), src.numel() * src.element_size(), grid,
                                      _stream(stream)))
+
+
+def check_conversions(begin: int = 0, end: int = 1 << 32, stream=None) -> tuple:
+    """Run the device conversion self-check over fp32 bit patterns
+    [begin, end); returns (FP4 conversion mismatches, bf16 rounding
+    mismatches) -- both 0 on a conforming device."""
+    counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    _check(lib().replayssm_check_conversions(begin, end, _ptr(counts), _stream(stream)))
+    return tuple(int(c) for c in counts.cpu())
 
 
 def check_device_errors(ls: LayerState, stream=None) -> None:

@@ -36,6 +36,8 @@ def hipcc() -> str:
 # every kernel that inlines it (results do not depend on the calling kernel).
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-ffp-contract=on", "-I", INCLUDE, "-I", CSRC,
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+          # matrix-core accumulators in ordinary VGPRs (no AGPR copies around each MFMA)
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1",
           "-Wno-unused-command-line-argument"]
 
 

@@ -455,6 +455,12 @@ int replayssm_hbm_probe(int32_t mode, const void *src, void *dst, size_t bytes, 
                       "hbm probe launch");
 }
 
+int replayssm_check_conversions(uint64_t begin, uint64_t end, unsigned long long *counts, hipStream_t stream) {
+    if (!counts) return fail(RSSM_E_ARG, "check_conversions: NULL counts");
+    if (end > (1ull << 32) || begin > end) return fail(RSSM_E_ARG, "check_conversions: need begin <= end <= 2^32");
+    return hip_status(rssm::launch_conversion_check(begin, end, counts, stream), "conversion check launch");
+}
+
 const char *replayssm_version(void) { return "replayssm-gfx950 0.3"; }
 
 }  // extern "C"

@@ -76,6 +76,7 @@ hipError_t launch_split_verify(const ReplayParams &p, bool in_bf16, int mode, hi
 hipError_t launch_split_commit(const ReplayParams &p, bool in_bf16, int mode, bool accept, hipStream_t s);
 hipError_t launch_split_load(const ReplayParams &p, int mode, hipStream_t s);
 hipError_t launch_recurrent(const RecurrentParams &p, bool in_bf16, bool pool, hipStream_t s);
+hipError_t launch_conversion_check(uint64_t begin, uint64_t end, unsigned long long *counts, hipStream_t stream);
 hipError_t launch_probe(int mode, const float *src, float *dst, size_t bytes, int grid, hipStream_t s);
 hipError_t launch_recurrent_accept(int32_t *sel, const int32_t *n_keep, int batch, int T,
                                    int Tmax, hipStream_t s);

@@ -2,8 +2,11 @@
 // bandwidth of the device, measured with the same 16-byte non-temporal
 // accesses the state-streaming kernels use.  Used to put the kernels'
 // achieved bandwidth next to what the memory system sustains in practice.
+// Also the self-check of the device conversions the low-precision commit
+// relies on.
 #include "device_common.h"
 #include "kernels.h"
+#include "quant.h"
 
 namespace rssm {
 
@@ -67,7 +70,49 @@ __global__ void __launch_bounds__(256) probe_head_read_kernel(const float *src, 
     sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;
 }
 
+// For every fp32 bit pattern in [begin, end), NaNs skipped: (0) gfx950's
+// f32 -> E2M1 conversion at unit scale against the threshold encoding at
+// scale 1 (the commit takes FP4 codes from the conversion of |v| / s
+// bracketed from both sides, which is exact only if the conversion is the
+// round-to-nearest-even, saturating, sign-keeping encoding everywhere);
+// (1) for |v| <= 0x7F7F0000, bf16 stochastic rounding by integer addition
+// against the selecting form, with a draw hashed from the pattern.  Each
+// thread adds its mismatch counts to counts[0..1] only when nonzero.
+__global__ void __launch_bounds__(256) conversion_check_kernel(uint64_t begin, uint64_t end,
+                                                               unsigned long long *counts) {
+    const Fp4Thresholds t = fp4_thresholds(1.0f);
+    unsigned long long bad_fp4 = 0, bad_sr = 0;
+    const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
+    for (uint64_t i = begin + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < end; i += step) {
+        const uint32_t bits = (uint32_t)i;
+        const uint32_t mag = bits & 0x7FFFFFFFu;
+        if (mag > 0x7F800000u) continue;
+        const float v = __uint_as_float(bits);
+        const uint32_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 0xFu;
+        bad_fp4 += hw != fp4_encode(v, t, false);
+        if (mag <= 0x7F7F0000u) {
+            uint32_t w = bits * 0x9E3779B1u;
+            w ^= w >> 15;
+            w *= 0x85EBCA77u;
+            w ^= w >> 13;
+            const uint32_t r16 = w & 0xFFFFu;
+            bad_sr += ((bits + (r16 ^ 0xFFFFu)) >> 16) != bf16_sr(v, r16);
+        }
+    }
+    if (bad_fp4) atomicAdd(&counts[0], bad_fp4);
+    if (bad_sr) atomicAdd(&counts[1], bad_sr);
+}
+
 }  // namespace
+
+hipError_t launch_conversion_check(uint64_t begin, uint64_t end, unsigned long long *counts, hipStream_t stream) {
+    if (end <= begin) return hipSuccess;
+    const uint64_t n = end - begin;
+    const uint64_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(conversion_check_kernel, dim3((unsigned)(blocks < 8192 ? blocks : 8192)), dim3(256), 0,
+                       stream, begin, end, counts);
+    return hipGetLastError();
+}
 
 hipError_t launch_probe(int mode, const float *src, float *dst, size_t bytes, int grid, hipStream_t stream) {
     const size_t n4 = bytes / 16;

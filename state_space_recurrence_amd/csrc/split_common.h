@@ -109,10 +109,11 @@ __device__ __forceinline__ uint32_t swap_pair_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, kDppQuadSwap1, 0xF, 0xF, false);
 }
 
-__device__ __forceinline__ void sr_draws4_pair(uint64_t seed, uint32_t layer, uint32_t interval, uint32_t e0,
-                                               uint32_t e1, int lane, uint32_t (&r0)[4], uint32_t (&r1)[4]) {
+__device__ __forceinline__ void sr_draws4_pair(uint64_t seed, uint32_t layer, uint32_t interval, size_t e0,
+                                               size_t e1, int lane, uint32_t (&r0)[4], uint32_t (&r1)[4]) {
     const bool odd = lane & 1;
-    const Philox4 o = philox4x32_10((odd ? e1 : e0) >> 3, interval, layer, 0, (uint32_t)seed,
+    // the counter is the low word of e / 8 (e itself may pass 2^32 in a large pool)
+    const Philox4 o = philox4x32_10((uint32_t)((odd ? e1 : e0) >> 3), interval, layer, 0, (uint32_t)seed,
                                     (uint32_t)(seed >> 32));
     // an even lane's columns use words x, y of a counter, an odd lane's z, w
     const uint32_t own_a = odd ? o.z : o.x, own_b = odd ? o.w : o.y;
@@ -167,8 +168,7 @@ __device__ __forceinline__ void quantize_store_rows(const ReplayParams &a, size_
                                                     float4 v0, float4 v1, uint32_t interval) {
     uint32_t r0[4] = {0, 0, 0, 0}, r1[4] = {0, 0, 0, 0};
     if constexpr (ModeTraits<MODE>::has_u)
-        sr_draws4_pair(a.seed, (uint32_t)a.layer, interval, (uint32_t)(row0 * kN + 4 * c),
-                       (uint32_t)(row1 * kN + 4 * c), lane, r0, r1);
+        sr_draws4_pair(a.seed, (uint32_t)a.layer, interval, row0 * kN + 4 * c, row1 * kN + 4 * c, lane, r0, r1);
     quantize_store_row<MODE>(a, row0, c, lane, v0, r0);
     __builtin_amdgcn_sched_barrier(0);   // the rows' quantisers one after the other
     quantize_store_row<MODE>(a, row1, c, lane, v1, r1);
@@ -357,6 +357,331 @@ __device__ __forceinline__ void rows4_dot(const typename Raw4<UB>::T (&raw)[32],
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) y0[t] = chunk_combine4(r[t], lane);
+}
+
+
+// -------------------------------------------------- matrix-core commit --
+// A commit's rank-K update S_new = lam U + sum_j cs[r][j] B_j is a dense
+// contraction (per wave: 16 rows x 128 columns x K entries) and runs on the
+// matrix cores, v_mfma_f32_16x16x4_f32, with the state transposed (the MFMA
+// row index is the state column) so that the accumulators land in the
+// layout the quantisers want: lane l = 16 g + pl of a wave holds state row
+// pl of the wave's 16 rows, columns 32g .. 32g+31 -- one whole FP4 scale
+// block and the 32 draws of four whole Philox counters, so the block scale
+// needs no cross-lane step and the draws no exchange.
+//   A (16 x 4; lane i + 16k holds A[i][k]):  A[i][k] = B_{4kb+k}[8i + t]
+//   B (4 x 16; lane j + 16k holds B[k][j]):  B[k][j] = cs[row j][4kb + k]
+//   D (16 x 16; lane j + 16(i/4), register i % 4, holds D[i][j]):
+//      state row j, column 8i + t  ->  lane (pl = j, g = i / 4), register
+//      v = i % 4 of tile t: column 32g + 8v + t.
+// A lane's block is held as e[32], e[i] = column 32g + i (i = 8v + t).
+
+// Raw update-source values of one lane's 32-column block.
+template <int UB> struct RawBlock;
+template <> struct RawBlock<16> { uint4 q[4]; };               // 32 bf16
+template <> struct RawBlock<8> { uint4 q[2]; };                // 32 E4M3
+template <> struct RawBlock<4> { uint4 q[1]; uint32_t sc; };   // 32 E2M1 codes + the block's E4M3 scale
+
+// base + byte_off with the offset kept 32-bit, so that a wave-uniform base
+// and a per-lane offset address memory as scalar base + vector offset.
+template <typename T>
+__device__ __forceinline__ T *off_bytes(T *base, uint32_t byte_off) {
+    return reinterpret_cast<T *>(reinterpret_cast<char *>(base) + byte_off);
+}
+template <typename T>
+__device__ __forceinline__ const T *off_bytes(const T *base, uint32_t byte_off) {
+    return reinterpret_cast<const T *>(reinterpret_cast<const char *>(base) + byte_off);
+}
+
+// Where a lane's block lives: the first state row of the wave's 16 rows
+// (wave-uniform, so the pointers below are a scalar base plus a 32-bit lane
+// offset), the lane's row among them and its column block.
+struct BlockAt {
+    size_t row0;
+    int r, g;
+};
+
+template <int UB>
+__device__ __forceinline__ void load_block(const ReplayParams &a, const BlockAt &at, RawBlock<UB> &r) {
+    if constexpr (UB == 16 || UB == 8) {
+        constexpr int eb = UB / 8;   // bytes per element
+        const uint4 *p = off_bytes(reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(a.u) + at.row0 * (kN * eb)),
+                                   (uint32_t)((at.r * kN + 32 * at.g) * eb));
+#pragma unroll
+        for (int k = 0; k < 2 * eb; ++k) r.q[k] = p[k];
+    } else {
+        r.q[0] = *off_bytes(reinterpret_cast<const uint4 *>(a.oq + at.row0 * (kN / 2)), (uint32_t)(at.r * (kN / 2) + 16 * at.g));
+        r.sc = *off_bytes(a.os + at.row0 * (kN / 32), (uint32_t)(at.r * (kN / 32) + at.g));
+    }
+}
+
+__device__ __forceinline__ void words_of(const uint4 &q, uint32_t (&w)[4]) {
+    w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+}
+
+template <int UB>
+__device__ __forceinline__ void decode_block(const RawBlock<UB> &r, float (&e)[32]) {
+    if constexpr (UB == 16) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t w[4];
+            words_of(r.q[k], w);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                e[8 * k + 2 * m] = __uint_as_float(w[m] << 16);
+                e[8 * k + 2 * m + 1] = __uint_as_float(w[m] & 0xFFFF0000u);
+            }
+        }
+    } else if constexpr (UB == 8) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            uint32_t w[4];
+            words_of(r.q[k], w);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const float4 d = e4m3_decode4(w[m]);
+                e[16 * k + 4 * m] = d.x; e[16 * k + 4 * m + 1] = d.y;
+                e[16 * k + 4 * m + 2] = d.z; e[16 * k + 4 * m + 3] = d.w;
+            }
+        }
+    } else {
+        const float s = e4m3_decode(r.sc);
+        uint32_t w[4];
+        words_of(r.q[0], w);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            float d[8];
+            e2m1_decode8(w[m], d);
+#pragma unroll
+            for (int n = 0; n < 8; ++n) e[8 * m + n] = d[n] * s;
+        }
+    }
+}
+
+// The lane's A operands of entry block kb: B_{4kb+g}[8pl .. 8pl+7] as
+// stored (8 bf16 or 8 fp32 values).
+template <typename TIn>
+struct B8 {
+    uint4 q[sizeof(TIn) / 2];
+};
+
+template <typename TIn>
+__device__ __forceinline__ void load_b8(const TIn *p, B8<TIn> &r) {
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(TIn) / 2); ++i) r.q[i] = reinterpret_cast<const uint4 *>(p)[i];
+}
+
+template <typename TIn>
+__device__ __forceinline__ void widen_b8(const B8<TIn> &r, float (&v)[8]) {
+    if constexpr (sizeof(TIn) == 2) {
+        uint32_t w[4];
+        words_of(r.q[0], w);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            v[2 * m] = __uint_as_float(w[m] << 16);
+            v[2 * m + 1] = __uint_as_float(w[m] & 0xFFFF0000u);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            uint32_t w[4];
+            words_of(r.q[i], w);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) v[4 * i + m] = __uint_as_float(w[m]);
+        }
+    }
+}
+
+// e <- lam e + sum_{j<K} cf_j B_j on the lane's block; cf[kb] is the
+// coefficient of entry j = 4kb + g for the lane's row (zero from K on), bo
+// the lane's A operands (entries from K on are replaced by zeros here).  K
+// is wave-uniform.
+template <typename TIn, int KMAX>
+__device__ __forceinline__ void mfma_update(float (&e)[32], float lam, const float (&cf)[KMAX / 4],
+                                            const B8<TIn> (&bo)[KMAX / 4], int g, int K) {
+    f4v acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) acc[t] = f4v{lam * e[t], lam * e[8 + t], lam * e[16 + t], lam * e[24 + t]};
+#pragma unroll
+    for (int kb = 0; kb < KMAX / 4; ++kb) {
+        if (4 * kb >= K) break;
+        // widened at each use, not once for all calls (32 or 64 VGPRs)
+        B8<TIn> braw = bo[kb];
+#pragma unroll
+        for (int i = 0; i < (int)(sizeof(TIn) / 2); ++i)
+            asm volatile("" : "+v"(braw.q[i].x), "+v"(braw.q[i].y), "+v"(braw.q[i].z), "+v"(braw.q[i].w));
+        float bv[8];
+        widen_b8<TIn>(braw, bv);
+        const bool live = 4 * kb + g < K;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) bv[t] = live ? bv[t] : 0.f;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) acc[t] = __builtin_amdgcn_mfma_f32_16x16x4f32(bv[t], cf[kb], acc[t], 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        e[t] = acc[t].x; e[8 + t] = acc[t].y; e[16 + t] = acc[t].z; e[24 + t] = acc[t].w;
+    }
+}
+
+// bf16 stochastic rounding of two values by integer addition: adding
+// 0xFFFF - r16 to the fp32 bits carries into bit 16 exactly when the dropped
+// low half exceeds r16 (the rounding rule of bf16_sr), the carry moving into
+// the exponent where it must.  Valid for |v| <= 0x7F7F0000 as bits (finite,
+// no rounding past the largest bf16); draws: low half of w for v0, high
+// half for v1.  Returns the two codes packed (v0 low).
+__device__ __forceinline__ uint32_t bf16_sr_pair_plain(float v0, float v1, uint32_t w) {
+    const uint32_t nw = ~w;
+    const uint32_t x0 = __float_as_uint(v0) + (nw & 0xFFFFu);
+    const uint32_t x1 = __float_as_uint(v1) + (nw >> 16);
+    return __builtin_amdgcn_perm(x1, x0, 0x07060302u);   // high halves of x0, x1
+}
+
+// FP4 codes of 8 values (element n in nibble n) scaled by r, by gfx950's
+// f32 -> E2M1 conversion at unit scale (round to nearest even, saturating at
+// 6, sign kept: identical to the threshold encoding for every non-NaN fp32).
+__device__ __forceinline__ uint32_t fp4_cvt8(const float *v, float r) {
+    uint32_t w = 0;
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[0] * r, v[1] * r, 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2] * r, v[3] * r, 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4] * r, v[5] * r, 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6] * r, v[7] * r, 1.0f, 3);
+    return w;
+}
+
+// FP4 codes of 8 values by the exact threshold comparisons.
+__device__ __forceinline__ uint32_t fp4_exact8(const float *v, const Fp4Thresholds &t, bool z) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int n = 0; n < 8; ++n) w |= fp4_encode(v[n], t, z) << (4 * n);
+    return w;
+}
+
+// Rounds and stores a lane's block of a new state (row row0 + r, columns
+// 32g..32g+31): the update checkpoint by stochastic rounding with the draws
+// of stream index `interval` (through `stage`, the wave's LDS tile of
+// 16 x (128 x bytes + 16) bytes), the output copy by FP4 quantisation with
+// the block's own scale.  Called by the whole wave with one row0.
+//
+// FP4 codes: RNE_E2M1(|v| / s) is decided exactly without comparing against
+// the seven thresholds t s: with r = rcp(s), every product v r (1 -+ 2^-20)
+// lies strictly below / above |v| / s in magnitude (rcp and the products
+// are within a few ulps), so where the two products convert to the same
+// code (monotone conversion) that code is the exact one.  Otherwise --
+// |v| / s within about 2^-20 of a threshold, ties included -- the block is
+// encoded again by the threshold comparisons.  Blocks holding a value
+// beyond the largest bf16 (infinities, NaN) take the general quantisers.
+template <int MODE>
+__device__ __forceinline__ void quantize_store_block(const ReplayParams &a, const BlockAt &at, const float (&e)[32],
+                                                     uint32_t interval, uint8_t *stage) {
+    using MT = ModeTraits<MODE>;
+    const int g = at.g;
+    const uint32_t lrow = (uint32_t)(at.r * kN + 32 * g);   // the lane's element offset from row0
+    if (a.dbg) {
+        float *db = off_bytes(a.dbg + at.row0 * kN, lrow * 4);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            stream_store4(db + 4 * k, make_float4(e[4 * k], e[4 * k + 1], e[4 * k + 2], e[4 * k + 3]));
+    }
+    // twice the largest magnitude bit pattern (sign shifted out; a form no
+    // later quantiser step shares, so none of the 32 values is kept for it)
+    uint32_t mmax2 = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) mmax2 = max(mmax2, __float_as_uint(e[i]) << 1);
+    const bool plain = mmax2 <= (0x7F7F0000u << 1);
+    if constexpr (MT::has_u) {
+        // The rounded block goes through the wave's LDS tile (16 rows of the
+        // update checkpoint) and leaves it in 1 KB contiguous stores: the
+        // MFMA layout would store 16 or 8 bytes per lane 64 or 32 bytes
+        // apart (four times the write requests of a contiguous store).
+        constexpr int eb = MT::ubits / 8;               // bytes per element
+        constexpr int rowb = kN * eb, pitch = rowb + 16;   // padded tile rows: no bank conflicts
+        uint8_t *tile = stage + at.r * pitch + 32 * g * eb;
+        // the draws of the lane's four counters (element index / 8 =
+        // row * 16 + 4g + k); the key and the uniform counter words are
+        // fenced per call so the uniform parts of the rounds are recomputed
+        // (scalar ALU) rather than hoisted out of the caller's loops
+        auto draws = [&](int k) {
+            uint32_t k0 = (uint32_t)a.seed, k1 = (uint32_t)(a.seed >> 32), c1 = interval, c2 = (uint32_t)a.layer;
+            asm volatile("" : "+s"(k0), "+s"(k1), "+s"(c1), "+s"(c2));
+            return philox4x32_10((uint32_t)(at.row0 * (kN / 8)) + (lrow >> 3) + k, c1, c2, 0, k0, k1);
+        };
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const Philox4 o = draws(k);
+            const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+            const float *v = e + 8 * k;
+            if constexpr (MT::ubits == 16) {
+                uint32_t q[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) q[m] = bf16_sr_pair_plain(v[2 * m], v[2 * m + 1], w[m]);
+                *reinterpret_cast<uint4 *>(tile + 16 * k) = make_uint4(q[0], q[1], q[2], q[3]);
+            } else {
+                uint32_t q[2];
+#pragma unroll
+                for (int m = 0; m < 2; ++m)
+                    q[m] = e4m3_sr(v[4 * m], w[2 * m] & 0xFFFFu) | (e4m3_sr(v[4 * m + 1], w[2 * m] >> 16) << 8) |
+                           (e4m3_sr(v[4 * m + 2], w[2 * m + 1] & 0xFFFFu) << 16) |
+                           (e4m3_sr(v[4 * m + 3], w[2 * m + 1] >> 16) << 24);
+                *reinterpret_cast<uint2 *>(tile + 8 * k) = make_uint2(q[0], q[1]);
+            }
+        }
+        if constexpr (MT::ubits == 16) {
+            if (!plain) {   // rare: a value beyond the largest bf16 (inf, NaN): the general rounding again
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const Philox4 o = draws(k);
+                    const uint32_t w[4] = {o.x, o.y, o.z, o.w};
+                    uint32_t q[4];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const float v0 = e[8 * k + 2 * m], v1 = e[8 * k + 2 * m + 1];
+                        q[m] = bf16_sr(v0, w[m] & 0xFFFFu) | (bf16_sr(v1, w[m] >> 16) << 16);
+                    }
+                    *reinterpret_cast<uint4 *>(tile + 16 * k) = make_uint4(q[0], q[1], q[2], q[3]);
+                }
+            }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // 16 contiguous rows: lane l copies bytes 16 l + 1024 m of the tile
+        uint8_t *ub = reinterpret_cast<uint8_t *>(a.u) + at.row0 * rowb;
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int m = 0; m < 16 * rowb / 1024; ++m) {
+            const uint32_t i = 1024 * m + 16 * lane;   // byte within the 16 rows
+            const uint4 d = *reinterpret_cast<const uint4 *>(stage + (i / rowb) * pitch + i % rowb);
+            *off_bytes(reinterpret_cast<uint4 *>(ub), i) = d;
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+    if constexpr (MT::has_o) {
+        uint32_t c[4];
+        uint32_t sc;
+        bool exact = !plain;
+        if (plain) {
+            sc = fp4_scale_code(__uint_as_float(mmax2 >> 1));
+            const float r = sc == 0u ? 0.f : __builtin_amdgcn_rcpf(e4m3_decode(sc));
+            const float rlo = r * (1.0f - 0x1p-20f), rhi = r * (1.0f + 0x1p-20f);
+            uint32_t diff = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                c[k] = fp4_cvt8(e + 8 * k, rlo);
+                diff |= c[k] ^ fp4_cvt8(e + 8 * k, rhi);
+            }
+            exact = diff != 0u;
+        }
+        if (exact) {   // rare: a value within ~2^-20 of a threshold, or a non-plain block
+            float amax = 0.f;
+#pragma unroll
+            for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(e[i]));
+            sc = fp4_scale_code(amax);
+            const Fp4Thresholds t = fp4_thresholds(e4m3_decode(sc));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) c[k] = fp4_exact8(e + 8 * k, t, sc == 0u);
+        }
+        *off_bytes(reinterpret_cast<uint4 *>(a.oq + at.row0 * (kN / 2)), lrow / 2) = make_uint4(c[0], c[1], c[2], c[3]);
+        *off_bytes(a.os + at.row0 * (kN / 32), lrow / 32) = (uint8_t)sc;
+    }
 }
 
 }  // namespace

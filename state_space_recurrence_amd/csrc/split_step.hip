@@ -6,9 +6,8 @@
 // token that closes the interval, so a slot that reaches L entries is left
 // at pos == L and listed in the commit list.  The commit kernel then rewrites
 // the listed slots' state (update checkpoint by stochastic rounding, FP4
-// copy) from the update source and the L buffered entries, one workgroup per
-// head with each wave taking a quarter of the head's rows, and publishes
-// pos = 0, intv + 1.  Keeping the commit out of the step kernel keeps the
+// copy) from the update source and the L buffered entries, one wave per
+// head, and publishes pos = 0, intv + 1.  Keeping the commit out of the step kernel keeps the
 // step's registers and LDS small (no spills, more waves per SIMD on the
 // latency-bound steps), and spreads each interval's commit work over the
 // whole chip whether the slots commit together (lock-step phases) or a few
@@ -105,117 +104,173 @@ split_step_kernel(ReplayParams a) {
     publish_step(a, s.b, in.K, in.seen);
 }
 
-// Commit pass over the listed slots: item = (listed slot, head), one
-// workgroup per item, wave w rewrites the head's chunk w (rows 2(w + 4m) + hf).
-// The workgroups loop over the items; the last slot to finish empties the
-// list.
-template <int KMAX>
-struct ListCommitSmem {
-    float B[KMAX][kN];      // the head's group's B entries, zero past K
-    float cs[kP * KMAX];    // the head's commit coefficients (cs_index layout)
-};
+// Commit pass over the listed slots: item = (listed slot, head), one wave
+// per item rewriting the head's 64 rows as four 16-row quarters on the
+// matrix cores (lane layout of mfma_update), with no LDS and no barrier.
+// Per item the wave loads its A operands (the group's B entries, the same
+// for all quarters), the x rows of all quarters and the entries' steps
+// once, computes the interval's weights once, and streams the quarters'
+// source blocks with the next quarter's loads in flight under the current
+// quarter's arithmetic.  Waves loop over the items, and an item's loads are
+// issued before the previous item's arrival is counted, so the wait for
+// that atomic (and for the stores before it) overlaps them.  The last wave
+// of a slot publishes it; the last slot to finish empties the list.
 
-// Arrival of one head of listed slot b (list index li of n): the slot's last
-// head publishes the commit (pos = 0, intv + 1) and counts the slot done in
-// its group of list indices (li mod kListGroups); the last slot of a group
-// counts the group, and the last group empties the list.  Items are assigned
-// to workgroups statically, so a workgroup that still reads the list has
-// items of its own pending and the list cannot have been emptied under it.
-__device__ __forceinline__ void publish_listed(const ReplayParams &a, int b, int seen, int li, int n) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int old = atomicAdd(&a.work[b], 1);
-        if (old >= a.wg_per_slot) atomicOr(a.err, kErrDup);
-        if (old == a.wg_per_slot - 1) {
-            if (a.pos[b] != seen) atomicOr(a.err, kErrDup);
-            a.work[b] = 0;
-            a.pos[b] = 0;
-            a.intv[b] += 1;
-            const int grp = li % kListGroups;
-            const int ngrp = n < kListGroups ? n : kListGroups;
-            const int members = (n - grp + kListGroups - 1) / kListGroups;
-            if (atomicAdd(&a.clist[1 + grp], 1) == members - 1) {
-                a.clist[1 + grp] = 0;
-                if (atomicAdd(&a.clist[1 + kListGroups], 1) == ngrp - 1) {
-                    a.clist[1 + kListGroups] = 0;
-                    a.clist[0] = 0;
-                }
+// Arrival of one wave of listed slot b (list index li of n), counted by its
+// lane 0 with the value `old` its atomicAdd on the slot's counter returned:
+// the slot's last wave publishes the commit (pos = 0, intv + 1) and counts
+// the slot done in its group of list indices (li mod kListGroups); the last
+// slot of a group counts the group, and the last group empties the list.
+// Items are assigned to waves statically and a wave reads the list entry of
+// its next item before its current item arrives, so the list cannot be
+// emptied under a wave that still reads it.
+__device__ __forceinline__ void finish_arrival(const ReplayParams &a, int old, int b, int seen, int li, int n) {
+    if (old >= a.wg_per_slot) atomicOr(a.err, kErrDup);
+    if (old == a.wg_per_slot - 1) {
+        if (a.pos[b] != seen) atomicOr(a.err, kErrDup);
+        a.work[b] = 0;
+        a.pos[b] = 0;
+        a.intv[b] += 1;
+        const int grp = li % kListGroups;
+        const int ngrp = n < kListGroups ? n : kListGroups;
+        const int members = (n - grp + kListGroups - 1) / kListGroups;
+        if (atomicAdd(&a.clist[1 + grp], 1) == members - 1) {
+            a.clist[1 + grp] = 0;
+            if (atomicAdd(&a.clist[1 + kListGroups], 1) == ngrp - 1) {
+                a.clist[1 + kListGroups] = 0;
+                a.clist[0] = 0;
             }
         }
     }
 }
 
+// Waves per SIMD of the commit pass: three where the registers allow it
+// without spilling (bf16 inputs, up to 16 entries), two otherwise.
+template <typename TIn>
+constexpr int commit_waves(int kmax) { return sizeof(TIn) == 2 && kmax == 16 ? 3 : 2; }
+
 template <typename TIn, int KMAX, int MODE>
-__global__ void __launch_bounds__(256) split_commit_list_kernel(ReplayParams a) {
+__global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(commit_waves<TIn>(KMAX))))
+split_commit_list_kernel(ReplayParams a) {
     constexpr int UB = ModeTraits<MODE>::ubits;
-    __shared__ ListCommitSmem<KMAX> sm;
+    constexpr int NKB = KMAX / 4;
+    // the wave's staging tile for the update checkpoint's rows (bf16 or E4M3)
+    __shared__ __align__(16) uint8_t stage[16 * (kN * (UB >= 8 ? UB / 8 : 1) + 16)];
     const int nlisted = a.clist[0];
     if (nlisted == 0) return;   // most steps: nothing closed an interval
-    const int items = nlisted * a.H;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const size_t HP = (size_t)a.H * kP, GN = (size_t)a.G * kN;
-    for (int it = blockIdx.x; it < items; it += gridDim.x) {
-        Slot s;
-        s.b = a.clist[kListHead + it / a.H];
-        s.h = it - (it / a.H) * a.H;
-        s.row = s.b;
-        s.tile = s.h;
-        s.wave = wave;
-        s.lane = lane;
-        s.hpg = a.H / a.G;
-        s.g = s.h / s.hpg;
-        s.c = lane & 31;
-        s.hf = lane >> 5;
-        s.prow = 2 * s.c + s.hf;
-        int K = a.pos[s.b];
-        const int seen = K;
-        if (K < 1 || K > KMAX) {   // a listed slot holds L entries
-            if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
-            K = K < 1 ? 1 : KMAX;
+    const int H = a.H;
+    const int items = nlisted * H;
+    const int lane = threadIdx.x & 63, pl = lane & 15, g = lane >> 4;
+    const size_t HP = (size_t)H * kP, GN = (size_t)a.G * kN;
+    const int hpg = H / a.G;
+    const int stride = gridDim.x;
+    int it = blockIdx.x;
+    if (it >= items) return;
+    // Slot facts are read ahead: the list entry two items ahead and the
+    // position and stream index one item ahead, each issued before the
+    // current item's loads so that waiting for them never waits for those.
+    // Indices past the end re-read the last item's entries.
+    const int *lst = a.clist + kListHead;
+    int b = __builtin_amdgcn_readfirstlane(lst[it / H]);
+    int pos = __builtin_amdgcn_readfirstlane(a.pos[b]);
+    int intv = __builtin_amdgcn_readfirstlane(a.intv[b]);
+    int nb = lst[min(it + stride, items - 1) / H];
+    int pend_old = 0, pend_b = -1, pend_seen = 0, pend_li = 0;
+    for (; it < items; it += stride) {
+        const int li = it / H;
+        const int h = it - li * H;
+        const int nb_u = __builtin_amdgcn_readfirstlane(nb);
+        const int npos = a.pos[nb_u], nintv = a.intv[nb_u];
+        const int nnb = lst[min(it + 2 * stride, items - 1) / H];
+        int K = pos;
+        if (K != a.L) {   // a listed slot holds L entries
+            if (lane == 0) atomicOr(a.err, kErrPos);
+            K = K < 1 ? 1 : (K > a.L ? a.L : K);
         }
-        const uint32_t interval = (uint32_t)a.intv[s.b] + 1u;
-        const TIn *xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)s.b * a.Lcap * HP + (size_t)s.h * kP;
-        const TIn *bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * GN + (size_t)s.g * kN;
-        const TIn *db = reinterpret_cast<const TIn *>(a.dtbuf) + (size_t)s.b * a.Lcap * a.H + s.h;
-        // this wave's source rows first, the coefficients under them
-        const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
-        typename Raw4<UB>::T raw[kPerChunk];
+        const uint32_t interval = (uint32_t)intv + 1u;
+        const TIn *xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)b * a.Lcap * HP + (size_t)h * kP;
+        const TIn *bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)b * a.Lcap * GN + (size_t)(h / hpg) * kN;
+        const TIn *db = reinterpret_cast<const TIn *>(a.dtbuf) + (size_t)b * a.Lcap * H + h;
+        const size_t hrow0 = ((size_t)b * H + h) * kP;   // the head's first state row
+        // loads in the order they are consumed: steps, x rows, quarter 0's
+        // source block, A operands
+        const float dt_l = io<TIn>::load1(off_bytes(db, (uint32_t)((lane < K ? lane : K - 1) * H * sizeof(TIn))));
+        const float Ah = a.A[h];
+        int jrow[NKB];   // the lane's entries 4kb + g, clamped into the interval
 #pragma unroll
-        for (int m = 0; m < kPerChunk; ++m) raw[m] = load_row4<UB>(a, hrow + 2 * chunk_index(wave, m), s.c);
-        __syncthreads();   // the previous item's LDS reads are done
-        stage_B<TIn, KMAX>(sm.B, bb, bb, GN, K, K);
+        for (int kb = 0; kb < NKB; ++kb) jrow[kb] = 4 * kb + g < K ? 4 * kb + g : K - 1;
+        uint32_t xoff[NKB];   // byte offsets of the lane's x_j[pl] from the head's quarter
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) xoff[kb] = (uint32_t)((jrow[kb] * (int)HP + pl) * sizeof(TIn));
+        // x rows and source block of a quarter
+        auto load_quarter = [&](int q, RawBlock<UB> &raw, float (&xq)[NKB]) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) xq[kb] = io<TIn>::load1(off_bytes(xb + 16 * q, xoff[kb]));
+            load_block<UB>(a, BlockAt{hrow0 + 16 * q, pl, g}, raw);
+        };
+        RawBlock<UB> raw0, raw1;
+        float x0[NKB], x1[NKB];
+        load_quarter(0, raw0, x0);
+        B8<TIn> bo[NKB];
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+            load_b8<TIn>(off_bytes(bb, (uint32_t)((jrow[kb] * (int)GN + 8 * pl) * sizeof(TIn))), bo[kb]);
+        // the previous item's arrival (its atomic was issued before these loads)
+        if (pend_b >= 0 && lane == 0) finish_arrival(a, pend_old, pend_b, pend_seen, pend_li, nlisted);
         // l_i = A dt_i in lane i; Lambda_K and w_j = dt_j exp(sum_{j<i<K} l_i)
         // with the sums grown in ascending i (the commit arithmetic of every
         // other commit path)
-        const float dl = lane < K ? io<TIn>::load1(db + (size_t)lane * a.H) : 0.f;
-        const float l = a.A[s.h] * dl;
+        const float dl = lane < K ? dt_l : 0.f;
+        const float l = Ah * dl;
         float tot = 0.f, suf = 0.f;
         for (int i = 0; i < K; ++i) {
-            const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
-            tot += li;
-            if (i > lane) suf += li;
+            const float li_ = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
+            tot += li_;
+            if (i > lane) suf += li_;
         }
         const float wj = lane < K ? dl * expf(suf) : 0.f;
         const float lam = expf(tot);
-        // coefficients w_j x_j[r] of all 64 rows, entries j = wave (mod 4)
-        {
-            const int i = s.prow >> 1;
+        float w[NKB];
 #pragma unroll
-            for (int j0 = 0; j0 < KMAX; j0 += 4) {
-                const int j = j0 + wave;
-                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
-                const int jj = j < K ? j : K - 1;
-                const float cf = w * io<TIn>::load1(xb + (size_t)jj * HP + s.prow);
-                sm.cs[cs_index<KMAX>(s.hf, i & 3, j, i >> 2)] = (j < K) ? cf : 0.f;
-            }
+        for (int kb = 0; kb < NKB; ++kb) w[kb] = __shfl(wj, 4 * kb + g);
+        // one quarter: coefficients w_j x_j[r] of the lane's row for entries
+        // j = 4kb + g, the update, the rounding and the stores
+        auto commit_quarter = [&](int q, const RawBlock<UB> &raw, const float (&xq)[NKB]) {
+            float cf[NKB];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) cf[kb] = 4 * kb + g < K ? w[kb] * xq[kb] : 0.f;
+            float e[32];
+            decode_block<UB>(raw, e);
+            mfma_update<TIn, KMAX>(e, lam, cf, bo, g, K);
+            quantize_store_block<MODE>(a, BlockAt{hrow0 + 16 * q, pl, g}, e, interval, stage);
+        };
+        // quarters in pairs, each one's loads in flight under the other's
+        // arithmetic (static buffer names: a dynamic index would move the
+        // buffers to scratch memory)
+#pragma nounroll
+        for (int q = 0; q < 4; q += 2) {
+            load_quarter(q + 1, raw1, x1);
+            commit_quarter(q, raw0, x0);
+            __builtin_amdgcn_sched_barrier(0);   // one quarter's arithmetic at a time
+            if (q + 2 < 4) load_quarter(q + 2, raw0, x0);
+            commit_quarter(q + 1, raw1, x1);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __syncthreads();
-        float4 st[kPerChunk];
-#pragma unroll
-        for (int m = 0; m < kPerChunk; ++m) st[m] = decode_row4<UB>(raw[m]);
-        commit_chunk_q<KMAX, MODE>(a, s, st, wave, lam, sm.cs, sm.B, interval);
-        publish_listed(a, s.b, seen, it / a.H, nlisted);
+        // the arrival: an address the compiler cannot prove uniform keeps the
+        // atomic a single-lane one whose result is waited for only where the
+        // next item uses it
+        int zero = 0;
+        asm volatile("" : "+v"(zero));
+        if (lane == 0) pend_old = atomicAdd(&a.work[b + zero], 1);
+        pend_b = b;
+        pend_seen = pos;
+        pend_li = li;
+        b = nb_u;
+        pos = __builtin_amdgcn_readfirstlane(npos);
+        intv = __builtin_amdgcn_readfirstlane(nintv);
+        nb = nnb;
     }
+    if (lane == 0) finish_arrival(a, pend_old, pend_b, pend_seen, pend_li, nlisted);
 }
 
 #define RSSM_MODE_SWITCH(MODEVAR, CALL)                                  \
@@ -253,16 +308,16 @@ hipError_t launch_split_step(const ReplayParams &p, bool in_bf16, int mode, hipS
                    : split_step_t<float, 32>(p, mode, grid, block, stream);
 }
 
-// Workgroups of the commit pass: enough for every head of the call's slots,
-// at most four per CU of the chip (they loop over the items).
-constexpr int kCommitListGrid = 1024;
+// Waves of the commit pass: enough for every item (slot, head) of the call's
+// slots, at most sixteen per CU of the chip (they loop over the items).
+constexpr int kCommitListGrid = 4096;
 
 hipError_t launch_split_commit_list(const ReplayParams &p0, bool in_bf16, int mode, hipStream_t stream) {
     if (p0.batch == 0) return hipSuccess;
     ReplayParams p = p0;
-    p.wg_per_slot = p.H;   // one arrival per head of a committed slot
-    const long heads = (long)p.batch * p.H;
-    dim3 grid((unsigned)(heads < kCommitListGrid ? heads : kCommitListGrid)), block(256);
+    p.wg_per_slot = p.H;   // one arrival per wave (one head) of a committed slot
+    const long items = (long)p.batch * p.wg_per_slot;
+    dim3 grid((unsigned)(items < kCommitListGrid ? items : kCommitListGrid)), block(64);
     if (p.L <= 16) return in_bf16 ? split_commit_list_t<uint16_t, 16>(p, mode, grid, block, stream)
                                    : split_commit_list_t<float, 16>(p, mode, grid, block, stream);
     return in_bf16 ? split_commit_list_t<uint16_t, 32>(p, mode, grid, block, stream)

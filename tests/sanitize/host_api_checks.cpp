@@ -30,6 +30,7 @@ RSSM_STUB(hipError_t launch_split_commit(const ReplayParams &, bool, int, bool, 
 RSSM_STUB(hipError_t launch_split_load(const ReplayParams &, int, hipStream_t))
 RSSM_STUB(hipError_t launch_recurrent(const RecurrentParams &, bool, bool, hipStream_t))
 RSSM_STUB(hipError_t launch_probe(int, const float *, float *, size_t, int, hipStream_t))
+RSSM_STUB(hipError_t launch_conversion_check(uint64_t, uint64_t, unsigned long long *, hipStream_t))
 RSSM_STUB(hipError_t launch_recurrent_accept(int32_t *, const int32_t *, int, int, int, hipStream_t))
 RSSM_STUB(hipError_t noalloc_work(int32_t **, int32_t **, hipStream_t))
 RSSM_STUB(hipError_t launch_split_commit_list(const ReplayParams &, bool, int, hipStream_t))

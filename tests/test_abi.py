@@ -169,3 +169,14 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(rs, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(rs.ReplaySSMError, match="missing"):
         rs.lib()
+
+
+def test_conversion_check_arguments_checked(rs):
+    """The conversion self-check refuses a NULL counter array and a range
+    outside 0..2^32 on the host, before any launch."""
+    L = rs.lib()
+    assert L.replayssm_check_conversions(0, 16, None, None) == -1
+    assert "counts" in L.replayssm_last_error().decode()
+    buf = (ctypes.c_uint64 * 2)()
+    assert L.replayssm_check_conversions(8, 4, buf, None) == -1
+    assert L.replayssm_check_conversions(0, (1 << 32) + 1, buf, None) == -1

@@ -268,6 +268,16 @@ def test_split_drift_ordering(rs):
     assert drift["split-bf16"] < drift["shared-fp4"]
 
 
+def test_device_conversions_exhaustive(rs):
+    """The matrix-core commit takes FP4 codes from gfx950's f32 -> E2M1
+    conversion of v / scale bracketed from both sides, and rounds bf16 by
+    integer addition.  Over every non-NaN fp32 bit pattern the conversion
+    equals the exact threshold encoding (round to nearest even, saturating
+    at 6, sign kept) and the addition form equals the selecting form; the
+    bit-exact byte checks of the other tests then rest on no untested input."""
+    assert rs.check_conversions(0, 1 << 32) == (0, 0)
+
+
 @pytest.mark.parametrize("fmt", ["low-e4m3", "split-e4m3", "shared-fp4"])
 def test_e4m3_decode_of_every_code(rs, fmt):
     """Every E4M3 code (OCP E4M3FN: subnormals, signed zeros, 448, NaN) is
