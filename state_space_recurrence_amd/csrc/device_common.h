@@ -89,6 +89,15 @@ __device__ __forceinline__ void stream_store4(float *p, float4 v) {
 constexpr int kBufferRsrcWord3 = 0x00020000;
 constexpr int kNonTemporal = 2;
 
+// A buffer resource over `bytes` bytes at a wave-uniform address (pinned to
+// scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void *p, int bytes) {
+    const uint64_t u = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)u), hi = __builtin_amdgcn_readfirstlane((uint32_t)(u >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(((uint64_t)hi << 32) | lo), 0, bytes,
+                                             kBufferRsrcWord3);
+}
+
 // Load at byte offset vo + soff: vo in a VGPR (covered by the descriptor's
 // range check), soff a wave-uniform constant carried in the scalar offset
 // operand, which the range check does not cover -- callers keep vo + soff

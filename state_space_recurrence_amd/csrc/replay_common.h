@@ -201,9 +201,8 @@ struct StepIn {
 // input / buffer pointers.  kmax is L-1, or Lcap where deferred accepts can
 // leave k >= L entries: the step then replays and commits all k+1.
 template <typename TIn>
-__device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s, int kmax) {
+__device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s, int kmax, int k) {
     StepIn in;
-    int k = a.pos[s.b];
     in.seen = k;
     if (k < 0 || k > kmax) {
         if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
@@ -222,6 +221,11 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
     in.bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)s.b * a.Lcap * in.GN + (size_t)s.g * kN;
     in.db = reinterpret_cast<const TIn *>(a.dtbuf) + (size_t)s.b * a.Lcap * a.H + s.h;
     return in;
+}
+
+template <typename TIn>
+__device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s, int kmax) {
+    return step_inputs<TIn>(a, s, kmax, a.pos[s.b]);
 }
 
 // Decay prep, Gram row, replay weights and the buffer part of the output for
@@ -336,16 +340,25 @@ template <typename TIn>
 __device__ __forceinline__ void step_append(const ReplayParams &a, const Slot &s, const StepIn &in) {
     const TIn *xin = static_cast<const TIn *>(in.xin);
     const TIn *Bin = static_cast<const TIn *>(in.Bin);
-    TIn *xw = reinterpret_cast<TIn *>(a.xbuf) + ((size_t)s.b * a.Lcap + in.k) * in.HP + (size_t)s.h * kP;
-    io<TIn>::copy1(xw + s.lane, xin + s.lane);
-    if (s.lane == 0) {
-        TIn *dw = reinterpret_cast<TIn *>(a.dtbuf) + ((size_t)s.b * a.Lcap + in.k) * a.H + s.h;
-        io<TIn>::copy1(dw, static_cast<const TIn *>(in.dtin));
+    const bool dt_lane = s.lane == 0;
+    const bool b_wave = s.wave == 0 && (s.tile * a.hpw) % s.hpg == 0;   // the group's first workgroup
+    // every value is read before anything is written (the buffers could alias
+    // the inputs as far as the compiler knows, which would otherwise make each
+    // copy wait for its load on the spot)
+    const TIn xv = xin[s.lane];
+    TIn dv{}, b0{}, b1{};
+    if (dt_lane) dv = *static_cast<const TIn *>(in.dtin);
+    if (b_wave) {
+        b0 = Bin[s.lane];
+        b1 = Bin[s.lane + 64];
     }
-    if (s.wave == 0 && (s.tile * a.hpw) % s.hpg == 0) {
+    TIn *xw = reinterpret_cast<TIn *>(a.xbuf) + ((size_t)s.b * a.Lcap + in.k) * in.HP + (size_t)s.h * kP;
+    xw[s.lane] = xv;
+    if (dt_lane) reinterpret_cast<TIn *>(a.dtbuf)[((size_t)s.b * a.Lcap + in.k) * a.H + s.h] = dv;
+    if (b_wave) {
         TIn *bw = reinterpret_cast<TIn *>(a.bbuf) + ((size_t)s.b * a.Lcap + in.k) * in.GN + (size_t)s.g * kN;
-        io<TIn>::copy1(bw + s.lane, Bin + s.lane);
-        io<TIn>::copy1(bw + s.lane + 64, Bin + s.lane + 64);
+        bw[s.lane] = b0;
+        bw[s.lane + 64] = b1;
     }
 }
 

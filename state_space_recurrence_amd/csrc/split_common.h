@@ -268,14 +268,20 @@ struct Fp4Rows {
     uint32_t scale[16];  // E4M3 scale of the lane's 32-element block of those rows
 };
 
+// The head's codes (4 KB) and scales (256 B) as buffer resources: one
+// scalar base each, the lane's offset in one VGPR, and the row group in the
+// constant scalar offset (row 4i + rg: 256 i bytes of codes, 16 i of
+// scales), so the 32 loads need no address arithmetic.
 __device__ __forceinline__ void fp4_rows_load(const ReplayParams &a, const Slot &s, Fp4Rows &o) {
     const int rg = s.lane >> 4, cq = s.lane & 15;
     const size_t hrow = ((size_t)s.b * a.H + s.h) * kP;
+    const __amdgpu_buffer_rsrc_t rc = uniform_rsrc(a.oq + hrow * (kN / 2), kP * (kN / 2));
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(a.os + hrow * (kN / 32), kP * (kN / 32));
+    const int vc = rg * (kN / 2) + 4 * cq, vs = rg * (kN / 32) + (cq >> 2);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        const size_t row = hrow + 4 * i + rg;
-        o.code[i] = *reinterpret_cast<const uint32_t *>(a.oq + row * (kN / 2) + 4 * cq);
-        o.scale[i] = a.os[row * (kN / 32) + (cq >> 2)];
+        o.code[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, vc, 4 * i * (kN / 2), 0);
+        o.scale[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, vs, 4 * i * (kN / 32), 0);
     }
 }
 

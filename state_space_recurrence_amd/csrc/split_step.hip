@@ -56,7 +56,9 @@ split_step_kernel(ReplayParams a) {
     const int prow = MT::fp4_out ? fp4_prow(s.lane) : s.prow;
     const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
 
-    // output-source rows are requested first; the prologue runs under them
+    // the position first (the prologue's first need), then the output-source
+    // rows; the prologue runs under them
+    const int pos_in = a.pos[s.b];
     Fp4Rows o;
     typename Raw4<UB>::T raw[kNB][kPerChunk];   // update-source chunks (low modes)
     if constexpr (MT::fp4_out) {
@@ -68,7 +70,7 @@ split_step_kernel(ReplayParams a) {
             for (int m = 0; m < kPerChunk; ++m) raw[q][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q, m), s.c);
     }
 
-    StepIn in = step_inputs<TIn>(a, s, a.L - 1);
+    StepIn in = step_inputs<TIn>(a, s, a.L - 1, pos_in);
     in.commit = false;   // the interval-closing commit is the commit kernel's
     float lam, ybuf;
     step_prologue<TIn, KMAX>(a, s, in, prow, sm, &lam, &ybuf);
