@@ -151,6 +151,33 @@ __device__ __forceinline__ void stage_B(float (*sB)[kN], const TIn *bb, const TI
     }
 }
 
+// stage_B keeping the entries as stored (TIn), zero past K.
+template <typename TIn, int KMAX>
+__device__ __forceinline__ void stage_B_raw(TIn (*sB)[kN], const TIn *bb, const TIn *Bin, size_t GN, int nbuf,
+                                            int K) {
+    constexpr int total = KMAX * kN / 4;
+    for (int q0 = threadIdx.x; q0 < total; q0 += 4 * blockDim.x) {
+        typename io<TIn>::raw4 r[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            int q = q0 + u * blockDim.x;
+            q = q < total ? q : total - 1;
+            int j = q / (kN / 4);
+            const int n = 4 * (q - j * (kN / 4));
+            j = j < K ? j : K - 1;
+            r[u] = io<TIn>::load_raw4((j < nbuf ? bb + (size_t)j * GN : Bin) + n);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = q0 + u * blockDim.x;
+            if (q < total) {
+                const int j = q / (kN / 4), n = 4 * (q - j * (kN / 4));
+                *reinterpret_cast<typename io<TIn>::raw4 *>(&sB[j][n]) = j < K ? r[u] : typename io<TIn>::raw4{};
+            }
+        }
+    }
+}
+
 // x rows of one head (64 elements each) are fetched with 16-byte loads:
 // xt_elems elements per lane, xt_rows rows per wave-wide load.
 template <typename TIn>
@@ -169,11 +196,28 @@ __device__ __forceinline__ void store16(void *p, uint4 v) { *reinterpret_cast<ui
 template <typename TIn, int KMAX>
 struct __align__(16) StepSmem {
     static constexpr bool kCommit = true;
+    static constexpr bool kCoefFromX = false;
     float gram[KMAX];              // B_j . C  (one group per workgroup)
     float cs[kMaxHpw][kP * KMAX];  // commit coefficients w_j x_j[r] (cs_index layout)
     union {
         TIn X[kMaxHpw][KMAX][kP];  // prologue, per head: x rows of the K entries as stored (rows >= K unset)
         float B[KMAX][kN];         // commit steps, after the prologue: the group's B entries, zero past K
+    } u;
+};
+
+// The 64-entry step: no coefficient table (it alone would be 64 KB for four
+// heads).  Commit steps form the coefficients w_j x_j[r] as they use them,
+// from the x rows, which therefore stay in LDS next to the B entries, and
+// keep the B entries as stored: 48 KB per workgroup with bf16 inputs
+// instead of 96 KB, so three workgroups fit on a CU.
+template <typename TIn, int KMAX>
+struct __align__(16) StepSmemX {
+    static constexpr bool kCommit = true;
+    static constexpr bool kCoefFromX = true;
+    float gram[KMAX];
+    struct {
+        TIn X[kMaxHpw][KMAX][kP];
+        TIn B[KMAX][kN];   // as stored (widened where the commit reads them), zero past K
     } u;
 };
 
@@ -236,7 +280,7 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
 // prologue holds few registers next to the checkpoint chunks in flight.
 template <typename TIn, int KMAX, typename SM>
 __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot &s, const StepIn &in,
-                                              int prow, SM &sm, float *lam, float *ybuf) {
+                                              int prow, SM &sm, float *lam, float *ybuf, float *wj_out = nullptr) {
     const int k = in.k, K = in.K;
     const TIn *xin = static_cast<const TIn *>(in.xin);
     const TIn *Bin = static_cast<const TIn *>(in.Bin);
@@ -317,18 +361,24 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
         }
     }
     *ybuf = yb;
+    if (wj_out) *wj_out = wj;
     if constexpr (SM::kCommit) {
         if (in.commit) {
-            // row prow of the commit coefficients; any lane -> row bijection fills them all
-            const int i = prow >> 1, hf = prow & 1;
+            if constexpr (!SM::kCoefFromX) {
+                // row prow of the commit coefficients; any lane -> row bijection fills them all
+                const int i = prow >> 1, hf = prow & 1;
 #pragma unroll
-            for (int j = 0; j < KMAX; ++j) {
-                const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
-                const float cf = w * io<TIn>::load1(xrow + j * kP);
-                sm.cs[s.wave][cs_index<KMAX>(hf, i & 3, j, i >> 2)] = (j < K) ? cf : 0.f;
+                for (int j = 0; j < KMAX; ++j) {
+                    const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
+                    const float cf = w * io<TIn>::load1(xrow + j * kP);
+                    sm.cs[s.wave][cs_index<KMAX>(hf, i & 3, j, i >> 2)] = (j < K) ? cf : 0.f;
+                }
+                __syncthreads();   // every head is done with its x rows; B takes their place
             }
-            __syncthreads();   // every head is done with its x rows; B takes their place
-            stage_B<TIn, KMAX>(sm.u.B, bb, Bin, in.GN, k, K);
+            if constexpr (SM::kCoefFromX)
+                stage_B_raw<TIn, KMAX>(sm.u.B, bb, Bin, in.GN, k, K);
+            else
+                stage_B<TIn, KMAX>(sm.u.B, bb, Bin, in.GN, k, K);
         }
     }
     __syncthreads();
@@ -783,6 +833,45 @@ __device__ __forceinline__ void commit_chunk_lds(float4 (&st)[kPerChunk], int c,
             const float4 c0 = *reinterpret_cast<const float4 *>(cp);
             const float4 c1 = *reinterpret_cast<const float4 *>(cp + 4);
             const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+            for (int m = 0; m < kPerChunk; ++m) {
+                st[m].x += cf[m] * b.x;
+                st[m].y += cf[m] * b.y;
+                st[m].z += cf[m] * b.z;
+                st[m].w += cf[m] * b.w;
+            }
+        }
+    }
+    store_chunk(dst, c, st);
+}
+
+// commit_chunk_lds with the coefficients formed as they are used: w_j (lane
+// j of wj) times x_j[r] from the head's x rows in LDS (sX[j][r]; entries
+// from K on are unset there and masked), the same products as the table
+// the other commit paths fill, so the results are bit-identical.
+template <typename TIn, int KMAX>
+__device__ __forceinline__ void commit_chunk_x(float4 (&st)[kPerChunk], int c, float lam, float wj,
+                                               const TIn (*sX)[kP], const TIn (*sB)[kN], int hf, int K,
+                                               const HeadState &dst) {
+#pragma unroll
+    for (int m = 0; m < kPerChunk; ++m) {
+        st[m].x *= lam; st[m].y *= lam; st[m].z *= lam; st[m].w *= lam;
+    }
+    int col = 4 * (threadIdx.x & 31);
+    asm volatile("" : "+v"(col));
+    const int Kr = (K + 3) & ~3;
+    for (int j0 = 0; j0 < Kr; j0 += 4) {
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+            const int j = j0 + jj;
+            const float4 b = io<TIn>::widen(*reinterpret_cast<const typename io<TIn>::raw4 *>(&sB[j][col]));
+            const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, wj), j));
+            float cf[kPerChunk];
+#pragma unroll
+            for (int m = 0; m < kPerChunk; ++m) {
+                const float prod = w * io<TIn>::load1(&sX[j][2 * chunk_index(c, m) + hf]);
+                cf[m] = (j < K) ? prod : 0.f;
+            }
 #pragma unroll
             for (int m = 0; m < kPerChunk; ++m) {
                 st[m].x += cf[m] * b.x;

@@ -21,6 +21,7 @@
 // Decays are formed as exp of segment sums of A dt (never as ratios of
 // prefix products, which underflow to 0/0 over an interval).
 #include <mutex>
+#include <type_traits>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -38,10 +39,19 @@ namespace {
 // registers are held on every step).  With them out of the register budget
 // the 16-entry kernel runs three waves per SIMD (measured +5% over two waves
 // with B in registers).
+// The 64-entry instance keeps no coefficient table and its B entries as
+// stored (StepSmemX): three workgroups per CU with bf16 inputs instead of one.
+template <typename TIn>
+constexpr int step64_waves() { return sizeof(TIn) == 2 ? 3 : 1; }
+
 template <typename TIn, int KMAX>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KMAX == 16 ? 3 : 1)))
+using StepLds = typename std::conditional<KMAX == 64, StepSmemX<TIn, KMAX>, StepSmem<TIn, KMAX>>::type;
+
+template <typename TIn, int KMAX>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KMAX == 16 ? 3 : (KMAX == 64 ? step64_waves<TIn>() : 1))))
 replay_step_kernel(ReplayParams a) {
-    __shared__ StepSmem<TIn, KMAX> sm;
+    using SM = StepLds<TIn, KMAX>;
+    __shared__ SM sm;
 
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
@@ -53,8 +63,8 @@ replay_step_kernel(ReplayParams a) {
 
     const StepIn in = step_inputs<TIn>(a, s, a.kmax);
     const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
-    float lam, ybuf;
-    step_prologue<TIn, KMAX>(a, s, in, s.prow, sm, &lam, &ybuf);
+    float lam, ybuf, wj = 0.f;
+    step_prologue<TIn, KMAX>(a, s, in, s.prow, sm, &lam, &ybuf, &wj);
 
     float r[kChunks];
 #pragma unroll
@@ -64,7 +74,12 @@ replay_step_kernel(ReplayParams a) {
 #pragma unroll
         for (int m = 0; m < kPerChunk; ++m) v[m] = dot4(cur[m], C4);
         r[c] = chunk_reduce8(v, s.lane);
-        if (in.commit) commit_chunk_lds<KMAX>(cur, c, lam, sm.cs[s.wave], sm.u.B, s.hf, (in.K + 3) & ~3, sp);
+        if (in.commit) {
+            if constexpr (SM::kCoefFromX)
+                commit_chunk_x<TIn, KMAX>(cur, c, lam, wj, sm.u.X[s.wave], sm.u.B, s.hf, in.K, sp);
+            else
+                commit_chunk_lds<KMAX>(cur, c, lam, sm.cs[s.wave], sm.u.B, s.hf, (in.K + 3) & ~3, sp);
+        }
         if (c + kNB < kChunks) load_chunk(cur, sp, c + kNB);
     }
     const float y0 = chunk_combine4(r, s.lane);
