@@ -1096,36 +1096,49 @@ def summarize_kernels(fetch_csv: str, write_csv: str, out_md: str, extra_csv: st
     split_i = {}
     for (k, f), (_, wv) in zip(fseq, wseq):
         key = k
-        if k.startswith("split_step_kernel"):
+        if k.startswith("split_commit_list_kernel"):
             i = split_i.get(k, 0)
             split_i[k] = i + 1
-            key = k + (" [commit launches]" if i % ws.interval == ws.interval - 1 else " [other launches]")
+            key = k + (" [commit launches]" if i % ws.interval == ws.interval - 1 else " [empty launches]")
         groups.setdefault(key, []).append((f, wv))
     extra = {}
     if extra_csv != "-":
+        by_dispatch = {}
         for r in load(extra_csv):
             if ours(r):
-                extra.setdefault((_kernel_label(r["Kernel_Name"]), r["Counter_Name"]), []).append(
-                    float(r["Counter_Value"]))
+                by_dispatch.setdefault(int(r["Dispatch_Id"]), []).append(r)
+        extra_i = {}
+        for d in sorted(by_dispatch):
+            rs_ = by_dispatch[d]
+            k = _kernel_label(rs_[0]["Kernel_Name"])
+            if k.startswith("split_commit_list_kernel"):
+                i = extra_i.get(k, 0)
+                extra_i[k] = i + 1
+                k = k + (" [commit launches]" if i % ws.interval == ws.interval - 1 else " [empty launches]")
+            for r in rs_:
+                extra.setdefault((k, r["Counter_Name"]), []).append(float(r["Counter_Value"]))
     modes = {0: "split-bf16", 1: "split-e4m3", 2: "shared-fp4", 3: "low-bf16", 4: "low-e4m3"}
     fp4 = 0.5 + 1.0 / 32
 
     def model(key):
         """Algorithmic bytes of one launch (None where the model does not
         cover it)."""
-        if key.startswith("split_step_kernel"):
+        if key.startswith("split_step_kernel") or key.startswith("split_commit_list_kernel"):
             mode = int(key.split("<")[1].split(">")[0].split(",")[-1])
             fmt = modes[mode]
+            # bytes per element: output source read, update source read, state written
             out_r, upd_r, cw = {"split-bf16": (fp4, 2, 2 + fp4), "split-e4m3": (fp4, 1, 1 + fp4),
-                                "shared-fp4": (fp4, fp4, fp4), "low-bf16": (2, 0, 2),
-                                "low-e4m3": (1, 0, 1)}[fmt]
+                                "shared-fp4": (fp4, fp4, fp4), "low-bf16": (2, 2, 2),
+                                "low-e4m3": (1, 1, 1)}[fmt]
             L = ws.interval
             entry = (ws.heads * 64 + ws.groups * 128 + ws.heads) * 2
             cur = (ws.heads * 64 + 2 * ws.groups * 128 + ws.heads) * 2
-            if "commit" in key:   # position L-1: read L-1 entries, read U and write U / O, no append
-                b = E * (out_r + upd_r + cw) + cur + (L - 1) * entry + ws.heads * 64 * 4
-            else:                 # positions 0..L-2, averaged
-                b = E * out_r + cur + entry + (L - 2) / 2 * entry + ws.heads * 64 * 4
+            if key.startswith("split_step_kernel"):   # positions 0..L-1 averaged: read k entries, append one
+                b = E * out_r + cur + entry + (L - 1) / 2 * entry + ws.heads * 64 * 4
+            elif "[commit launches]" in key:          # every slot: read U and the L entries, write the state
+                b = E * (upd_r + cw) + L * entry
+            else:
+                return None
             return b * ws.batch
         if key.startswith("prefill_kernel"):
             batch, Tp = PROBE_PREFILL
@@ -1166,10 +1179,23 @@ def summarize_kernels(fetch_csv: str, write_csv: str, out_md: str, extra_csv: st
         lines.append(f"| `{key}` | {len(v)} | {f / 1e6:.1f} | {wv / 1e6:.1f} | {ms} | {rt} |")
     if extra:
         names = sorted({c for _, c in extra})
-        lines += ["", "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+        per_wave = "SQ_WAVES" in names
+        lines += ["", "Third run, averaged per launch" + (" (SQ_ counters other than SQ_WAVES per wave)" if per_wave else "")
+                  + ":", "", "| kernel | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
         for k in dict.fromkeys(k for k, _ in extra):
-            vals = [extra.get((k, c)) for c in names]
-            lines.append(f"| `{k}` | " + " | ".join(f"{sum(x) / len(x):.4g}" if x else "-" for x in vals) + " |")
+            waves = extra.get((k, "SQ_WAVES"))
+            nw = sum(waves) / len(waves) if waves else 0
+            cells = []
+            for c in names:
+                x = extra.get((k, c))
+                if not x:
+                    cells.append("-")
+                    continue
+                v = sum(x) / len(x)
+                if per_wave and c.startswith("SQ_") and c != "SQ_WAVES" and nw > 0:
+                    v /= nw
+                cells.append(f"{v:.4g}")
+            lines.append(f"| `{k}` | " + " | ".join(cells) + " |")
     lines.append("")
     open(out_md, "w").write("\n".join(lines))
     print("\n".join(lines))
