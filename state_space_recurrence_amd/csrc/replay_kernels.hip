@@ -146,14 +146,10 @@ __global__ void __launch_bounds__(256) replay_step_rows_kernel(ReplayParams a) {
 // ------------------------------------------------------------------------
 // Speculative verify: outputs of T draft positions, no state written.
 // ------------------------------------------------------------------------
+// The verify of one workgroup's heads (slot position k < L).
 template <typename TIn, int KMAX, int T>
-__global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
-    __shared__ VerifySmemF<TIn, KMAX, KMAX, T> sm;
-
-    const Slot s = slot_of(a);
-    if (s.b < 0) return;   // padding row
-    const VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
-    if (in.k >= a.L) return;   // deferred fold: replay_fold_verify_kernel, launched next
+__device__ __forceinline__ void verify_body(const ReplayParams &a, const Slot &s, const VerifyIn &in,
+                                            VerifySmemF<TIn, KMAX, KMAX, T> &sm) {
     const HeadState sp = head_state(a.ckpt, s, a.H);
 
     // prologue loads first (they retire before the checkpoint chunks)
@@ -203,20 +199,24 @@ __global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
     verify_append<TIn, T>(a, s, in);
 }
 
-// Verify on the slots a deferred accept left at pos >= L (the others were
-// done by replay_verify_kernel): fold the pos entries into the checkpoint
-// while streaming it, then the drafts are entries 0..T-1 of the next
-// interval (their outputs from the folded rows).  A commit: pos = 0, intv+1.
-// Launched only for layers that declare deferred commits.
 template <typename TIn, int KMAX, int T>
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KMAX <= 24 ? 3 : 1)))
-replay_fold_verify_kernel(ReplayParams a) {
-    __shared__ FoldSmem<TIn, KMAX, T> sm;
+__global__ void __launch_bounds__(256) replay_verify_kernel(ReplayParams a) {
+    __shared__ VerifySmemF<TIn, KMAX, KMAX, T> sm;
 
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
-    VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
-    if (in.k < a.L) return;
+    const VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
+    if (in.k >= a.L) return;   // layers with deferred commits use replay_verify_fold_kernel
+    verify_body<TIn, KMAX, T>(a, s, in, sm);
+}
+
+// Verify on a slot a deferred accept left at pos >= L: fold the pos entries
+// into the checkpoint while streaming it, then the drafts are entries
+// 0..T-1 of the next interval (their outputs from the folded rows).  A
+// commit: pos = 0, intv+1.
+template <typename TIn, int KMAX, int T>
+__device__ __forceinline__ void fold_body(const ReplayParams &a, const Slot &s, VerifyIn in,
+                                          FoldSmem<TIn, KMAX, T> &sm) {
     const HeadState sp = head_state(a.ckpt, s, a.H);
     float4 buf[kNB][kPerChunk];   // chunks in the order 0, 2, 1, 3 (as in the verify kernel)
     load_chunk(buf[0], sp, 0);
@@ -262,6 +262,30 @@ replay_fold_verify_kernel(ReplayParams a) {
     in.k = 0;
     verify_append<TIn, T, false>(a, s, in);
     publish_fold<TIn>(a, s.b, 0, reinterpret_cast<const TIn *>(a.Bm) + (size_t)s.row * T * in.GN, T, in.seen);
+}
+
+// Verify for layers that declare deferred commits: each workgroup folds or
+// verifies by its slot's position, in one launch (no second pass over the
+// grid for the folding slots, and the folding workgroups share the chip
+// with the verifying ones).  The LDS is either pass's layout.
+template <typename TIn, int KMAX, int FK, int T>
+union VerifyFoldSmem {
+    VerifySmemF<TIn, KMAX, KMAX, T> v;
+    FoldSmem<TIn, FK, T> f;
+};
+
+template <typename TIn, int KMAX, int FK, int T>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(FK <= 24 ? 3 : 1)))
+replay_verify_fold_kernel(ReplayParams a) {
+    __shared__ VerifyFoldSmem<TIn, KMAX, FK, T> sm;
+
+    const Slot s = slot_of(a);
+    if (s.b < 0) return;   // padding row
+    const VerifyIn in = verify_inputs<TIn, T>(a, s, a.kmax);
+    if (in.k >= a.L)
+        fold_body<TIn, FK, T>(a, s, in, sm.f);
+    else
+        verify_body<TIn, KMAX, T>(a, s, in, sm.v);
 }
 
 // ------------------------------------------------------------------------
@@ -395,9 +419,10 @@ static void launch_verify_t(const ReplayParams &p, dim3 grid, dim3 block, hipStr
     switch (p.T) {
 #define RSSM_VERIFY_CASE(TT)                                                                            \
     case TT:                                                                                            \
-        hipLaunchKernelGGL((replay_verify_kernel<TIn, KMAX, TT>), grid, block, 0, stream, p);           \
         if (p.kmax >= p.L)                                                                              \
-            hipLaunchKernelGGL((replay_fold_verify_kernel<TIn, FK, TT>), grid, block, 0, stream, p);        \
+            hipLaunchKernelGGL((replay_verify_fold_kernel<TIn, KMAX, FK, TT>), grid, block, 0, stream, p);  \
+        else                                                                                            \
+            hipLaunchKernelGGL((replay_verify_kernel<TIn, KMAX, TT>), grid, block, 0, stream, p);       \
         break;
         RSSM_VERIFY_CASE(1)
         RSSM_VERIFY_CASE(2)

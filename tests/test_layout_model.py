@@ -160,14 +160,25 @@ def test_commit_coefficient_maps_agree(kmax):
 
 # ---- StepSmem layout and phases --------------------------------------------
 def step_smem(tin_bytes, kmax):
-    """Byte ranges of StepSmem<TIn, KMAX> fields (natural layout, 16-byte aligned struct)."""
+    """Byte ranges of the step kernel's LDS fields (natural layout, 16-byte
+    aligned struct): StepSmem<TIn, KMAX> (gram, coefficient table, x rows and
+    fp32 B in a union), or for KMAX = 64 StepSmemX<TIn, KMAX> (gram, x rows,
+    then B as stored; no table)."""
     gram = (0, 4 * kmax)
+    if kmax == 64:
+        u0 = (gram[1] + 15) // 16 * 16
+        b0 = u0 + tin_bytes * MAX_HPW * kmax * P
+        b1 = b0 + tin_bytes * kmax * N
+        size = (b1 + 15) // 16 * 16
+        return {"gram": gram, "cs": None, "u": (u0, b0), "B": (b0, b1), "b_bytes": tin_bytes,
+                "b_phase": 1, "size": size}
     cs0 = gram[1]
     cs = (cs0, cs0 + 4 * MAX_HPW * P * kmax)
     u0 = (cs[1] + 15) // 16 * 16
     usz = max(tin_bytes * MAX_HPW * kmax * P, 4 * kmax * N)
     size = (u0 + usz + 15) // 16 * 16
-    return {"gram": gram, "cs": cs, "u": (u0, u0 + usz), "size": size}
+    return {"gram": gram, "cs": cs, "u": (u0, u0 + usz), "B": (u0, u0 + 4 * kmax * N), "b_bytes": 4,
+            "b_phase": 2, "size": size}
 
 
 def _phases(tin_bytes, kmax, K, commit):
@@ -176,7 +187,9 @@ def _phases(tin_bytes, kmax, K, commit):
     by the prologue's barriers."""
     L = step_smem(tin_bytes, kmax)
     acc = []
-    g0, cs0, u0 = L["gram"][0], L["cs"][0], L["u"][0]
+    g0, u0 = L["gram"][0], L["u"][0]
+    cs0 = L["cs"][0] if L["cs"] else None
+    b0, bb, bph = L["B"][0], L["b_bytes"], L["b_phase"]
     xe = 16 // tin_bytes                       # x elements per 16-byte load
     lpr = P // xe                              # lanes per x row
     for w in range(MAX_HPW):
@@ -202,23 +215,31 @@ def _phases(tin_bytes, kmax, K, commit):
                 acc.append((1, w, "r", a, a + tin_bytes))
             if commit:
                 i, hf = prow >> 1, prow & 1
-                for j in range(kmax):
-                    a = cs0 + 4 * (w * P * kmax + cs_index(kmax, hf, i & 3, j, i >> 2))
-                    acc.append((1, w, "w", a, a + 4))
-                # phase 2: every thread stages B entries (float4 pieces) over the union
+                if cs0 is not None:
+                    for j in range(kmax):
+                        a = cs0 + 4 * (w * P * kmax + cs_index(kmax, hf, i & 3, j, i >> 2))
+                        acc.append((1, w, "w", a, a + 4))
+                # phase b_phase: every thread stages B entries (pieces of 4) -- over the
+                # union after a barrier (StepSmem), or into B next to the x rows (StepSmemX)
                 for q in range(t, kmax * N // 4, MAX_HPW * WAVE):
                     j, n = q // (N // 4), 4 * (q % (N // 4))
-                    a = u0 + 4 * (j * N + n)
-                    acc.append((2, w, "w", a, a + 16))
-                # phase 3: commit loop reads coefficients and B
+                    a = b0 + bb * (j * N + n)
+                    acc.append((bph, w, "w", a, a + 4 * bb))
+                # phase 3: commit loop reads B and the coefficients (table, or x rows)
                 kr = (K + 3) & ~3
                 hf, c = lane >> 5, lane & 31
                 for ch in range(CHUNKS):
                     for j in range(kr):
-                        a = u0 + 4 * (j * N + 4 * c)
-                        acc.append((3, w, "r", a, a + 16))
-                        a = cs0 + 4 * (w * P * kmax + cs_index(kmax, hf, ch, j, 0))
-                        acc.append((3, w, "r", a, a + 32))
+                        a = b0 + bb * (j * N + 4 * c)
+                        acc.append((3, w, "r", a, a + 4 * bb))
+                        if cs0 is not None:
+                            a = cs0 + 4 * (w * P * kmax + cs_index(kmax, hf, ch, j, 0))
+                            acc.append((3, w, "r", a, a + 32))
+                        else:
+                            for m in range(8):
+                                row = 2 * (ch + 4 * m) + hf
+                                a = u0 + ((w * kmax + j) * P + row) * tin_bytes
+                                acc.append((3, w, "r", a, a + tin_bytes))
     return acc, L
 
 
@@ -243,10 +264,14 @@ def test_step_lds_phases_race_free(tin_bytes, kmax):
                     if w1 != w2:
                         clash = (W[w1] > 0) & ((W[w2] > 0) | R[w2])
                         assert not clash.any(), f"phase {ph}: waves {w1}/{w2} share byte {np.argmax(clash)}"
-            if ph == 2 and commit:   # B staging covers the B part of the union exactly once
+            if ph == 2 and commit and L["b_phase"] == 2:   # B staging covers the B part of the union once
                 cnt = W.sum(0)
-                u0, u1 = L["u"][0], L["u"][0] + 4 * kmax * N
+                u0, u1 = L["B"]
                 assert (cnt[u0:u1] == 1).all() and cnt[:u0].sum() == 0 and cnt[u1:].sum() == 0
+            if ph == 1 and commit and L["b_phase"] == 1:   # B staging covers B once, next to the x rows
+                cnt = W.sum(0)
+                u0, u1 = L["B"]
+                assert (cnt[u0:u1] == 1).all() and cnt[u1:].sum() == 0
 
 
 def _resources():
