@@ -134,8 +134,8 @@ typedef struct rssm_desc {
                              covers `batch` rows, mapped to slots by rssm_state.slot_idx */
 } rssm_desc;
 
-/* Extra int32 words of rssm_state.commit_list beyond one per slot. */
-#define RSSM_COMMIT_LIST_EXTRA 32
+/* int32 words of rssm_state.commit_list for S state slots. */
+#define RSSM_COMMIT_LIST_WORDS(S) (32 + 4 * (S))
 
 /* Device buffers of one layer (host struct of device pointers). */
 typedef struct rssm_state {
@@ -156,10 +156,11 @@ typedef struct rssm_state {
                                 read or written for it); NULL = row b uses slot b.  Slots of one call
                                 must be distinct (a duplicate is flagged when detected, see above).
                                 Rows mapped outside 0..S-1 are skipped and flagged */
-    int32_t *commit_list; /* [S + RSSM_COMMIT_LIST_EXTRA] int32, zero-initialise once: the slots whose
-                             interval a low-precision step closes, committed by the step's second
-                             launch (needed by replayssm_step with BF16 / FP8 / shared-FP4 states;
-                             left all zero by every call; unused, may be NULL, otherwise) */
+    int32_t *commit_list; /* [RSSM_COMMIT_LIST_WORDS(S)] int32, zero-initialise once and leave to the
+                             library afterwards: the slots whose interval a low-precision step
+                             closes, committed by the step's second launch (needed by
+                             replayssm_step with BF16 / FP8 / shared-FP4 states; unused, may be
+                             NULL, otherwise).  Calls on one state must not overlap */
 } rssm_state;
 
 /*
@@ -184,8 +185,8 @@ int replayssm_step(const rssm_desc *desc, const rssm_state *st, const void *x,
  * tight serving loops, harnesses that forbid allocation).  Same arguments,
  * kernels and results as replayssm_step (bit-identical outputs and state),
  * but the per-slot arrival counters and the low-precision states' commit
- * list live in library scratch: a device array of 65536 counters and a
- * 65536-slot list (512 KB) per GPU, set up on the first call on that device
+ * lists live in library scratch: a device array of 65536 counters and two
+ * 65536-slot lists (1.25 MB) per GPU, set up on the first call on that device
  * and held until the process ends.  Of st->work only the sticky error word
  * work[n_slots] is used (read it with replayssm_check_device_errors as
  * usual); st->commit_list is not used.  Calls nothing that allocates.

@@ -54,8 +54,9 @@ class RssmState(ctypes.Structure):
     ]
 
 
-#: extra int32 words of the commit list beyond one per slot (RSSM_COMMIT_LIST_EXTRA)
-COMMIT_LIST_EXTRA = 32
+def commit_list_words(slots: int) -> int:
+    """int32 words of a state's commit list for `slots` slots (RSSM_COMMIT_LIST_WORDS)."""
+    return 32 + 4 * slots
 
 
 _LIB = None
@@ -188,7 +189,7 @@ class LayerState:
         self.pos = torch.zeros(batch, dtype=torch.int32, device=dev)
         self.intv = torch.zeros(batch, dtype=torch.int32, device=dev)
         self.work = torch.zeros(batch + 1, dtype=torch.int32, device=dev)
-        self.commit_list = torch.zeros(batch + COMMIT_LIST_EXTRA, dtype=torch.int32, device=dev)
+        self.commit_list = torch.zeros(commit_list_words(batch), dtype=torch.int32, device=dev)
         if tuple(A.shape) != (heads,) or tuple(D.shape) != (heads,):
             raise ReplaySSMError(f"A and D must have shape ({heads},), got {tuple(A.shape)}, {tuple(D.shape)}")
         self.A = A.to(device=dev, dtype=torch.float32).contiguous()

@@ -81,15 +81,20 @@ hipError_t launch_probe(int mode, const float *src, float *dst, size_t bytes, in
 hipError_t launch_recurrent_accept(int32_t *sel, const int32_t *n_keep, int batch, int T,
                                    int Tmax, hipStream_t s);
 
-// Commit list of the low-precision step (int32, kListHead + slots entries):
-// [0] number of listed slots, [1 .. kListGroups + 1] completion counters of
-// the commit pass, slot indices from kListHead.  All zero between calls.
-constexpr int kListGroups = 16;
+// Commit lists of the low-precision step (int32, kListHead + 4 x slots
+// words): two lists used in turn, so that the commit pass never clears the
+// count it reads.  [0], [1] entries in list 0 / 1; [kListFill] the list the
+// next step fills; [kListLast] the list the last step filled; list e's
+// entries (slot, new interval index) from kListHead + 2 e slots.  Zero at
+// creation; afterwards the words between calls are the library's.
+constexpr int kListFill = 2;
+constexpr int kListLast = 3;
 constexpr int kListHead = 32;
+constexpr long list_words(long slots) { return kListHead + 4 * slots; }
 hipError_t launch_split_commit_list(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
 
 // Library scratch for callers that cannot allocate: per-slot arrival counters
-// of up to kNoAllocMaxSlots slots and a commit list of as many slots, one
+// of up to kNoAllocMaxSlots slots and the commit lists of as many slots, one
 // array per device.  *work / *clist receive the current device's copies (set
 // up, and cleared on `s`, on its first use).
 constexpr int kNoAllocMaxSlots = 1 << 16;

@@ -502,7 +502,7 @@ hipError_t launch_load_f32(const ReplayParams &p, hipStream_t stream) {
 // one copy per device, held until the process ends.  Host code never passes the array's name to a kernel (on the
 // host it is only a stand-in for the symbol); it uses the device address
 // hipGetSymbolAddress returns for the current device.
-static __device__ __align__(256) int32_t scratch[2 * kNoAllocMaxSlots + kListHead];
+static __device__ __align__(256) int32_t scratch[kNoAllocMaxSlots + list_words(kNoAllocMaxSlots)];
 
 namespace {
 
@@ -528,7 +528,7 @@ hipError_t noalloc_work(int32_t **work, int32_t **clist, hipStream_t stream) {
         if (e != hipSuccess) return e;
         // the counters must start at zero (every complete call leaves them so)
         hipLaunchKernelGGL(zero_i32_kernel, dim3(64), dim3(256), 0, stream, static_cast<int32_t *>(ptr),
-                           2 * kNoAllocMaxSlots + kListHead);
+                           (int)(kNoAllocMaxSlots + list_words(kNoAllocMaxSlots)));
         e = hipGetLastError();
         if (e != hipSuccess) return e;
         g_scratch[dev] = static_cast<int32_t *>(ptr);

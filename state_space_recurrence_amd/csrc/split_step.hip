@@ -3,24 +3,28 @@
 //
 // A step runs as two launches.  The step kernel computes every row's output
 // from the output source and appends the token to the buffer -- also the
-// token that closes the interval, so a slot that reaches L entries is left
-// at pos == L and listed in the commit list.  The commit kernel then rewrites
-// the listed slots' state (update checkpoint by stochastic rounding, FP4
-// copy) from the update source and the L buffered entries, one wave per
-// head, and publishes pos = 0, intv + 1.  Keeping the commit out of the step kernel keeps the
-// step's registers and LDS small (no spills, more waves per SIMD on the
+// token that closes the interval: a slot that reaches L entries is published
+// at once (pos = 0, intv + 1) and listed, with its new interval index, in
+// the commit list.  The commit kernel then rewrites the listed slots' state
+// (update checkpoint by stochastic rounding, FP4 copy) from the update
+// source and the L buffered entries, one wave per head (or per half or
+// quarter of a head when few slots commit), before any later launch reads
+// it.  Keeping the commit out of the step kernel keeps the step's registers and LDS small (no spills, more waves per SIMD on the
 // latency-bound steps), and spreads each interval's commit work over the
 // whole chip whether the slots commit together (lock-step phases) or a few
 // on every step (staggered phases).
+#include <atomic>
 #include "split_common.h"
 
 namespace rssm {
 
 namespace {
 
-// Last-arriving workgroup of slot b publishes its new position; when the
-// step closed the interval (new_pos == L) it lists the slot for the commit
-// kernel.  Duplicate rows are flagged as in publish_position.
+// Last-arriving workgroup of slot b publishes its new position.  When the
+// step closed the interval (new_pos == L) it publishes the committed state
+// (pos = 0, intv + 1) and lists the slot with the new interval index in the
+// list the step fills (kListFill, fixed while the step runs).  Duplicate rows
+// are flagged as in publish_position.
 __device__ __forceinline__ void publish_step(const ReplayParams &a, int b, int new_pos, int seen) {
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -29,11 +33,19 @@ __device__ __forceinline__ void publish_step(const ReplayParams &a, int b, int n
         if (old == a.wg_per_slot - 1) {
             if (a.pos[b] != seen) atomicOr(a.err, kErrDup);
             a.work[b] = 0;
-            a.pos[b] = new_pos;
             if (new_pos == a.L) {
-                const int i = atomicAdd(&a.clist[0], 1);
-                if (i < a.nslots) a.clist[kListHead + i] = b;
-                else atomicOr(a.err, kErrDup);   // more listings than slots: rows repeated a slot
+                const int e = a.clist[kListFill] & 1;
+                const int iv = a.intv[b] + 1;
+                a.pos[b] = 0;
+                a.intv[b] = iv;
+                const int i = atomicAdd(&a.clist[e], 1);
+                if (i < a.nslots) {
+                    *reinterpret_cast<int2 *>(a.clist + kListHead + (size_t)e * 2 * a.nslots + 2 * i) = make_int2(b, iv);
+                } else {
+                    atomicOr(a.err, kErrDup);   // more listings than slots: rows repeated a slot
+                }
+            } else {
+                a.pos[b] = new_pos;
             }
         }
     }
@@ -51,6 +63,8 @@ split_step_kernel(ReplayParams a) {
     constexpr int UB = MT::ubits;
     __shared__ StepSmemNoCommit<TIn, KMAX> sm;
 
+    // the list this step fills, for the commit pass (which flips kListFill)
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.clist[kListLast] = a.clist[kListFill];
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
     const int prow = MT::fp4_out ? fp4_prow(s.lane) : s.prow;
@@ -106,45 +120,22 @@ split_step_kernel(ReplayParams a) {
     publish_step(a, s.b, in.K, in.seen);
 }
 
-// Commit pass over the listed slots: item = (listed slot, head), one wave
-// per item rewriting the head's 64 rows as four 16-row quarters on the
-// matrix cores (lane layout of mfma_update), with no LDS and no barrier.
-// Per item the wave loads its A operands (the group's B entries, the same
-// for all quarters), the x rows of all quarters and the entries' steps
-// once, computes the interval's weights once, and streams the quarters'
+// Commit pass over the listed slots: item = (listed slot, head, part), one
+// wave per item rewriting its part of the head's 64 rows, as 16-row quarters
+// on the matrix cores (lane layout of mfma_update), with no LDS and no
+// barrier.  A part is the whole head when the list is long (every wave then
+// has several heads to stream), and a half or a single quarter when it is
+// short (a few slots closing their intervals on a step): then one head's
+// quarters run on different waves instead of one after the other on a
+// single one.  Per item the wave loads its A operands (the group's B
+// entries, the same for all quarters), the x rows and the entries' steps
+// once, computes the interval's weights once, and streams its quarters'
 // source blocks with the next quarter's loads in flight under the current
-// quarter's arithmetic.  Waves loop over the items, and an item's loads are
-// issued before the previous item's arrival is counted, so the wait for
-// that atomic (and for the stores before it) overlaps them.  The last wave
-// of a slot publishes it; the last slot to finish empties the list.
-
-// Arrival of one wave of listed slot b (list index li of n), counted by its
-// lane 0 with the value `old` its atomicAdd on the slot's counter returned:
-// the slot's last wave publishes the commit (pos = 0, intv + 1) and counts
-// the slot done in its group of list indices (li mod kListGroups); the last
-// slot of a group counts the group, and the last group empties the list.
-// Items are assigned to waves statically and a wave reads the list entry of
-// its next item before its current item arrives, so the list cannot be
-// emptied under a wave that still reads it.
-__device__ __forceinline__ void finish_arrival(const ReplayParams &a, int old, int b, int seen, int li, int n) {
-    if (old >= a.wg_per_slot) atomicOr(a.err, kErrDup);
-    if (old == a.wg_per_slot - 1) {
-        if (a.pos[b] != seen) atomicOr(a.err, kErrDup);
-        a.work[b] = 0;
-        a.pos[b] = 0;
-        a.intv[b] += 1;
-        const int grp = li % kListGroups;
-        const int ngrp = n < kListGroups ? n : kListGroups;
-        const int members = (n - grp + kListGroups - 1) / kListGroups;
-        if (atomicAdd(&a.clist[1 + grp], 1) == members - 1) {
-            a.clist[1 + grp] = 0;
-            if (atomicAdd(&a.clist[1 + kListGroups], 1) == ngrp - 1) {
-                a.clist[1 + kListGroups] = 0;
-                a.clist[0] = 0;
-            }
-        }
-    }
-}
+// quarter's arithmetic.  Waves loop over the items, reading the next item's
+// list entry ahead.  The step already published the slots, so the pass
+// counts no arrivals: the waves only read the list, and its bookkeeping
+// (which list the next step fills, that list's count cleared) is written by
+// one wave in words no wave of the pass reads.
 
 // Waves per SIMD of the commit pass: three where the registers allow it
 // without spilling (bf16 inputs, up to 16 entries), two otherwise.
@@ -158,38 +149,47 @@ split_commit_list_kernel(ReplayParams a) {
     constexpr int NKB = KMAX / 4;
     // the wave's staging tile for the update checkpoint's rows (bf16 or E4M3)
     __shared__ __align__(16) uint8_t stage[16 * (kN * (UB >= 8 ? UB / 8 : 1) + 16)];
-    const int nlisted = a.clist[0];
+    // counts of both lists, the list the next step fills, the list the last
+    // step filled, in one load
+    const int4 hd = *reinterpret_cast<const int4 *>(a.clist);
+    const int e = __builtin_amdgcn_readfirstlane(hd.w) & 1;
+    // (a count beyond the slots means rows repeated a slot, flagged by the
+    // step; only the entries written are read)
+    const int nlisted = min(__builtin_amdgcn_readfirstlane(e ? hd.y : hd.x), a.nslots);
     if (nlisted == 0) return;   // most steps: nothing closed an interval
+    if (blockIdx.x == 0 && threadIdx.x == 0) {   // the next step fills the other list, from empty
+        a.clist[1 - e] = 0;
+        a.clist[kListFill] = 1 - e;
+    }
     const int H = a.H;
-    const int items = nlisted * H;
+    const int stride = gridDim.x;
+    // parts per head: as many as keep every item on a wave of its own, one
+    // when the heads alone fill the grid (the grid is the resident waves)
+    const int parts = nlisted * H * 4 <= stride ? 4 : nlisted * H * 2 <= stride ? 2 : 1;
+    const int nq = 4 / parts;          // quarters per item
+    const int per_slot = H * parts;    // items per listed slot
+    const int items = nlisted * per_slot;
     const int lane = threadIdx.x & 63, pl = lane & 15, g = lane >> 4;
     const size_t HP = (size_t)H * kP, GN = (size_t)a.G * kN;
     const int hpg = H / a.G;
-    const int stride = gridDim.x;
     int it = blockIdx.x;
     if (it >= items) return;
-    // Slot facts are read ahead: the list entry two items ahead and the
-    // position and stream index one item ahead, each issued before the
-    // current item's loads so that waiting for them never waits for those.
-    // Indices past the end re-read the last item's entries.
-    const int *lst = a.clist + kListHead;
-    int b = __builtin_amdgcn_readfirstlane(lst[it / H]);
-    int pos = __builtin_amdgcn_readfirstlane(a.pos[b]);
-    int intv = __builtin_amdgcn_readfirstlane(a.intv[b]);
-    int nb = lst[min(it + stride, items - 1) / H];
-    int pend_old = 0, pend_b = -1, pend_seen = 0, pend_li = 0;
+    // list entries (slot, interval index of the new checkpoint); the next
+    // item's is read ahead, issued before the current item's loads so that
+    // waiting for it never waits for those (past the end: the last entry)
+    const int2 *lst = reinterpret_cast<const int2 *>(a.clist + kListHead + (size_t)e * 2 * a.nslots);
+    int2 cur = lst[it / per_slot];
+    int2 nxt = lst[min(it + stride, items - 1) / per_slot];
+    const int K = a.L;   // a listed slot holds L entries
     for (; it < items; it += stride) {
-        const int li = it / H;
-        const int h = it - li * H;
-        const int nb_u = __builtin_amdgcn_readfirstlane(nb);
-        const int npos = a.pos[nb_u], nintv = a.intv[nb_u];
-        const int nnb = lst[min(it + 2 * stride, items - 1) / H];
-        int K = pos;
-        if (K != a.L) {   // a listed slot holds L entries
-            if (lane == 0) atomicOr(a.err, kErrPos);
-            K = K < 1 ? 1 : (K > a.L ? a.L : K);
-        }
-        const uint32_t interval = (uint32_t)intv + 1u;
+        const int li = it / per_slot;
+        const int hq = it - li * per_slot;
+        const int h = hq / parts;
+        const int q0 = (hq - h * parts) * nq;   // the item's first quarter
+        const int b = __builtin_amdgcn_readfirstlane(cur.x);
+        const uint32_t interval = (uint32_t)__builtin_amdgcn_readfirstlane(cur.y);
+        cur = nxt;
+        nxt = lst[min(it + 2 * stride, items - 1) / per_slot];
         const TIn *xb = reinterpret_cast<const TIn *>(a.xbuf) + (size_t)b * a.Lcap * HP + (size_t)h * kP;
         const TIn *bb = reinterpret_cast<const TIn *>(a.bbuf) + (size_t)b * a.Lcap * GN + (size_t)(h / hpg) * kN;
         const TIn *db = reinterpret_cast<const TIn *>(a.dtbuf) + (size_t)b * a.Lcap * H + h;
@@ -212,13 +212,11 @@ split_commit_list_kernel(ReplayParams a) {
         };
         RawBlock<UB> raw0, raw1;
         float x0[NKB], x1[NKB];
-        load_quarter(0, raw0, x0);
+        load_quarter(q0, raw0, x0);
         B8<TIn> bo[NKB];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
             load_b8<TIn>(off_bytes(bb, (uint32_t)((jrow[kb] * (int)GN + 8 * pl) * sizeof(TIn))), bo[kb]);
-        // the previous item's arrival (its atomic was issued before these loads)
-        if (pend_b >= 0 && lane == 0) finish_arrival(a, pend_old, pend_b, pend_seen, pend_li, nlisted);
         // l_i = A dt_i in lane i; Lambda_K and w_j = dt_j exp(sum_{j<i<K} l_i)
         // with the sums grown in ascending i (the commit arithmetic of every
         // other commit path)
@@ -248,31 +246,19 @@ split_commit_list_kernel(ReplayParams a) {
         };
         // quarters in pairs, each one's loads in flight under the other's
         // arithmetic (static buffer names: a dynamic index would move the
-        // buffers to scratch memory)
+        // buffers to scratch memory); an item of one quarter has no pair
+        const int q1 = q0 + nq;
 #pragma nounroll
-        for (int q = 0; q < 4; q += 2) {
-            load_quarter(q + 1, raw1, x1);
+        for (int q = q0; q < q1; q += 2) {
+            if (q + 1 < q1) load_quarter(q + 1, raw1, x1);
             commit_quarter(q, raw0, x0);
             __builtin_amdgcn_sched_barrier(0);   // one quarter's arithmetic at a time
-            if (q + 2 < 4) load_quarter(q + 2, raw0, x0);
+            if (q + 1 >= q1) break;
+            if (q + 2 < q1) load_quarter(q + 2, raw0, x0);
             commit_quarter(q + 1, raw1, x1);
             __builtin_amdgcn_sched_barrier(0);
         }
-        // the arrival: an address the compiler cannot prove uniform keeps the
-        // atomic a single-lane one whose result is waited for only where the
-        // next item uses it
-        int zero = 0;
-        asm volatile("" : "+v"(zero));
-        if (lane == 0) pend_old = atomicAdd(&a.work[b + zero], 1);
-        pend_b = b;
-        pend_seen = pos;
-        pend_li = li;
-        b = nb_u;
-        pos = __builtin_amdgcn_readfirstlane(npos);
-        intv = __builtin_amdgcn_readfirstlane(nintv);
-        nb = nnb;
     }
-    if (lane == 0) finish_arrival(a, pend_old, pend_b, pend_seen, pend_li, nlisted);
 }
 
 #define RSSM_MODE_SWITCH(MODEVAR, CALL)                                  \
@@ -291,10 +277,39 @@ hipError_t split_step_t(const ReplayParams &p, int mode, dim3 g, dim3 b, hipStre
     return hipGetLastError();
 }
 
-template <typename TIn, int KMAX>
-hipError_t split_commit_list_t(const ReplayParams &p, int mode, dim3 g, dim3 b, hipStream_t st) {
-    RSSM_MODE_SWITCH(mode, hipLaunchKernelGGL((split_commit_list_kernel<TIn, KMAX, M_>), g, b, 0, st, p));
+// Waves of the commit pass: as many as the chip holds at once (they loop
+// over the items), and no more than the call's items.  A larger grid only
+// queues waves behind the resident ones, and on a short list those late
+// waves, each with an item, set the launch's length.  The resident count
+// comes from the occupancy query, once per device and kernel.
+constexpr int kMaxCommitDevices = 64;
+
+template <typename TIn, int KMAX, int MODE>
+hipError_t split_commit_list_launch(const ReplayParams &p, long items, hipStream_t st) {
+    static std::atomic<int> resident[kMaxCommitDevices];   // zero: not queried yet
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxCommitDevices) return hipErrorInvalidDevice;
+    int waves = resident[dev].load(std::memory_order_relaxed);
+    if (waves == 0) {
+        int per_cu = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_commit_list_kernel<TIn, KMAX, MODE>, 64, 0);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        waves = per_cu * cus > 0 ? per_cu * cus : 1;
+        resident[dev].store(waves, std::memory_order_relaxed);
+    }
+    const dim3 grid((unsigned)(items < waves ? items : waves));
+    hipLaunchKernelGGL((split_commit_list_kernel<TIn, KMAX, MODE>), grid, dim3(64), 0, st, p);
     return hipGetLastError();
+}
+
+template <typename TIn, int KMAX>
+hipError_t split_commit_list_t(const ReplayParams &p, int mode, long items, hipStream_t st) {
+    RSSM_MODE_SWITCH(mode, return (split_commit_list_launch<TIn, KMAX, M_>(p, items, st)));
+    return hipSuccess;
 }
 
 #undef RSSM_MODE_SWITCH
@@ -310,20 +325,13 @@ hipError_t launch_split_step(const ReplayParams &p, bool in_bf16, int mode, hipS
                    : split_step_t<float, 32>(p, mode, grid, block, stream);
 }
 
-// Waves of the commit pass: enough for every item (slot, head) of the call's
-// slots, at most sixteen per CU of the chip (they loop over the items).
-constexpr int kCommitListGrid = 4096;
-
-hipError_t launch_split_commit_list(const ReplayParams &p0, bool in_bf16, int mode, hipStream_t stream) {
-    if (p0.batch == 0) return hipSuccess;
-    ReplayParams p = p0;
-    p.wg_per_slot = p.H;   // one arrival per wave (one head) of a committed slot
-    const long items = (long)p.batch * p.wg_per_slot;
-    dim3 grid((unsigned)(items < kCommitListGrid ? items : kCommitListGrid)), block(64);
-    if (p.L <= 16) return in_bf16 ? split_commit_list_t<uint16_t, 16>(p, mode, grid, block, stream)
-                                   : split_commit_list_t<float, 16>(p, mode, grid, block, stream);
-    return in_bf16 ? split_commit_list_t<uint16_t, 32>(p, mode, grid, block, stream)
-                   : split_commit_list_t<float, 32>(p, mode, grid, block, stream);
+hipError_t launch_split_commit_list(const ReplayParams &p, bool in_bf16, int mode, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    const long items = (long)p.batch * p.H * 4;   // at most (slot, head, quarter) items
+    if (p.L <= 16) return in_bf16 ? split_commit_list_t<uint16_t, 16>(p, mode, items, stream)
+                                   : split_commit_list_t<float, 16>(p, mode, items, stream);
+    return in_bf16 ? split_commit_list_t<uint16_t, 32>(p, mode, items, stream)
+                   : split_commit_list_t<float, 32>(p, mode, items, stream);
 }
 
 }  // namespace rssm

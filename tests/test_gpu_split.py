@@ -152,6 +152,15 @@ def test_split_decode_teacher_forced(rs, fmt):
     _run_intervals(rs, fmt, w, batch=3, n_intervals=3, tail=5)
 
 
+@pytest.mark.parametrize("batch", [200, 300])
+def test_split_commit_long_lists(rs, batch):
+    """Every slot closes its interval on the same step: at 16 heads, 200 and
+    300 listed slots make the commit pass give each wave half a head and a
+    whole head (the short lists of the other tests give it single quarters)."""
+    w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
+    _run_intervals(rs, "split-bf16", w, batch=batch, n_intervals=1, tail=1)
+
+
 def test_split_decode_4b_layout(rs):
     """The 4B-class head layout (H=96, G=8), bf16 inputs, split-bf16."""
     w = synth.WORKLOADS["split"]
