@@ -241,20 +241,10 @@ struct StepIn {
     const void *xin, *Bin, *Cin, *dtin, *xb, *bb, *db;   // typed by the caller
 };
 
-// Reads pos (clamped into 0..kmax, flagged otherwise) and sets the slot's
-// input / buffer pointers.  kmax is L-1, or Lcap where deferred accepts can
-// leave k >= L entries: the step then replays and commits all k+1.
+// The slot's input / buffer pointers (everything of StepIn but the position).
 template <typename TIn>
-__device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s, int kmax, int k) {
+__device__ __forceinline__ StepIn step_pointers(const ReplayParams &a, const Slot &s) {
     StepIn in;
-    in.seen = k;
-    if (k < 0 || k > kmax) {
-        if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
-        k = k < 0 ? 0 : kmax;
-    }
-    in.k = k;
-    in.K = k + 1;
-    in.commit = (in.K >= a.L);   // > L only after a deferred accept
     in.HP = (size_t)a.H * kP;
     in.GN = (size_t)a.G * kN;
     in.xin = reinterpret_cast<const TIn *>(a.x) + (size_t)s.row * in.HP + (size_t)s.h * kP;
@@ -267,9 +257,65 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
     return in;
 }
 
+// Sets the position k as read: clamped into 0..kmax, flagged otherwise.
+// kmax is L-1, or Lcap where deferred accepts can leave k >= L entries: the
+// step then replays and commits all k+1.
+__device__ __forceinline__ void step_position(StepIn &in, const ReplayParams &a, int kmax, int k) {
+    in.seen = k;
+    if (k < 0 || k > kmax) {
+        if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
+        k = k < 0 ? 0 : kmax;
+    }
+    in.k = k;
+    in.K = k + 1;
+    in.commit = (in.K >= a.L);   // > L only after a deferred accept
+}
+
+// Pointers and position in one.
+template <typename TIn>
+__device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s, int kmax, int k) {
+    StepIn in = step_pointers<TIn>(a, s);
+    step_position(in, a, kmax, k);
+    return in;
+}
+
 template <typename TIn>
 __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot &s, int kmax) {
     return step_inputs<TIn>(a, s, kmax, a.pos[s.b]);
+}
+
+// After the Gram row and the x rows are in LDS (behind a barrier): with
+// l_i = A dt_i in lane i, Lambda_K = exp(sum_{i<K} l_i) in *lam, and each
+// lane's suffix sum_{lane < i < K} l_i grown in ascending i through lane
+// broadcasts (no LDS round trips); the buffer part of the output
+// sum_j w_j g_j x_j[prow] + D x_k[prow] in *ybuf.  Returns w_j in lane j
+// (zero for j >= K).
+template <typename TIn, int KMAX, typename SM>
+__device__ __forceinline__ float step_replay_terms(const Slot &s, int k, int K, float l, float d, float Dh, int prow,
+                                                   SM &sm, float *lam, float *ybuf) {
+    float tot = 0.f, suf = 0.f;
+    for (int i = 0; i < K; ++i) {
+        const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
+        tot += li;
+        if (i > s.lane) suf += li;
+    }
+    *lam = expf(tot);
+    const float wj = s.lane < K ? d * expf(suf) : 0.f;               // w_j in lane j, zero for j >= K
+    const float cyj = s.lane < K ? wj * sm.gram[s.lane < KMAX ? s.lane : 0] : 0.f;   // w_j g_j
+
+    const TIn *xrow = &sm.u.X[s.wave][0][prow];   // x_j[prow] at xrow[j * kP]
+    float yb = Dh * io<TIn>::load1(xrow + k * kP);
+    for (int j0 = 0; j0 < K; j0 += 4) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int j = j0 + u;
+            const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cyj), j));
+            const float term = cj * io<TIn>::load1(xrow + j * kP);
+            yb += (j < K) ? term : 0.f;   // select: entries beyond K never leak (even NaN)
+        }
+    }
+    *ybuf = yb;
+    return wj;
 }
 
 // Decay prep, Gram row, replay weights and the buffer part of the output for
@@ -334,34 +380,9 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
         if (i * xt_rows<TIn>() < K && j < K) store16(&sm.u.X[s.wave][j][col], xw[i]);
     }
     __syncthreads();
-
-    // l_i = A dt_i lives in lane i.  Lambda_K = exp(sum_{i<K} l_i) and each
-    // lane's suffix sum_{lane < i < K} l_i grow in ascending i through lane
-    // broadcasts (no LDS round trips).
-    const float l = Ah * d;
-    float tot = 0.f, suf = 0.f;
-    for (int i = 0; i < K; ++i) {
-        const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
-        tot += li;
-        if (i > s.lane) suf += li;
-    }
-    *lam = expf(tot);
-    const float wj = s.lane < K ? d * expf(suf) : 0.f;               // w_j in lane j, zero for j >= K
-    const float cyj = s.lane < K ? wj * sm.gram[s.lane < KMAX ? s.lane : 0] : 0.f;   // w_j g_j
-
-    const TIn *xrow = &sm.u.X[s.wave][0][prow];   // x_j[prow] at xrow[j * kP]
-    float yb = Dh * io<TIn>::load1(xrow + k * kP);
-    for (int j0 = 0; j0 < K; j0 += 4) {
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int j = j0 + u;
-            const float cj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, cyj), j));
-            const float term = cj * io<TIn>::load1(xrow + j * kP);
-            yb += (j < K) ? term : 0.f;   // select: entries beyond K never leak (even NaN)
-        }
-    }
-    *ybuf = yb;
+    const float wj = step_replay_terms<TIn, KMAX>(s, k, K, Ah * d, d, Dh, prow, sm, lam, ybuf);
     if (wj_out) *wj_out = wj;
+    const TIn *xrow = &sm.u.X[s.wave][0][prow];   // x_j[prow] at xrow[j * kP]
     if constexpr (SM::kCommit) {
         if (in.commit) {
             if constexpr (!SM::kCoefFromX) {

@@ -337,6 +337,37 @@ __device__ __forceinline__ void fp4_rows_dot(const Fp4Rows &o, const float (&c8)
     }
 }
 
+// The same for bf16 inputs: the codes widen exactly to bf16 (packed FP4 ->
+// bf16 conversion, two values per instruction) and meet the C values as
+// stored, two products per packed bf16 dot (products of an E2M1 value and a
+// bf16 value are exact in fp32).  craw[t] holds C_t's 8 bf16 of columns
+// 8cq..8cq+7.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+template <int T>
+__device__ __forceinline__ void fp4_rows_dot_bf16(const Fp4Rows &o, const uint4 (&craw)[T], int lane, float (&y0)[T]) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const uint32_t cw[4] = {craw[t].x, craw[t].y, craw[t].z, craw[t].w};
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            uint32_t w = o.code[i], sraw = o.scale[i];
+            if (T > 1) asm volatile("" : "+v"(w), "+v"(sraw));   // fresh decode per draft
+            float acc = 0.f;
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0),
+                                                  __builtin_bit_cast(bf16x2, cw[0]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1),
+                                                  __builtin_bit_cast(bf16x2, cw[1]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2),
+                                                  __builtin_bit_cast(bf16x2, cw[2]), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3),
+                                                  __builtin_bit_cast(bf16x2, cw[3]), acc, false);
+            v[i] = acc * e4m3_decode(sraw);
+        }
+        y0[t] = reduce_scatter16(v, lane);
+    }
+}
+
 // y0[t] = deq(U) . C_t for this lane's row 2c + hf, every draft t, from the
 // raw rows (4-column layout) -- decoded chunk by chunk.
 template <int UB, int T>

@@ -32,11 +32,19 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
 
     float y0[T];
     if constexpr (MT::fp4_out) {
-        float c8[T][8];
+        if constexpr (sizeof(TIn) == 2) {
+            uint4 craw[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t)
-            load_c8<TIn>(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN, s.lane & 15, c8[t]);
-        fp4_rows_dot<T>(o, c8, s.lane, y0);
+            for (int t = 0; t < T; ++t)
+                craw[t] = load16(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN + 8 * (s.lane & 15));
+            fp4_rows_dot_bf16<T>(o, craw, s.lane, y0);
+        } else {
+            float c8[T][8];
+#pragma unroll
+            for (int t = 0; t < T; ++t)
+                load_c8<TIn>(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN, s.lane & 15, c8[t]);
+            fp4_rows_dot<T>(o, c8, s.lane, y0);
+        }
     } else {
         float4 C4[T];
 #pragma unroll
