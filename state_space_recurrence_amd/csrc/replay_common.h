@@ -231,6 +231,7 @@ struct __align__(16) StepSmemNoCommit {
     union {
         TIn X[kMaxHpw][KMAX][kP];
     } u;
+    TIn C[kN];   // the group's C of the current token (for row-per-lane output dots)
 };
 
 struct StepIn {

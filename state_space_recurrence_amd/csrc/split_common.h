@@ -285,6 +285,26 @@ __device__ __forceinline__ void fp4_rows_load(const ReplayParams &a, const Slot 
     }
 }
 
+// A lane's whole row of the FP4 copy (lane = row): 128 codes in four 16-byte
+// pieces (piece i = block i, columns 32i..32i+31, element n in nibble n of
+// its dword) and the row's four block scales in one dword (byte i = block
+// i).  A wave reads the head's 4 KB of codes and 256 B of scales in five
+// contiguous wave-wide loads.
+struct Fp4Row {
+    uint4 code[4];
+    uint32_t scale;
+};
+
+__device__ __forceinline__ void fp4_row_load(const ReplayParams &a, const Slot &s, Fp4Row &o) {
+    const size_t hrow = ((size_t)s.b * a.H + s.h) * kP;
+    const __amdgpu_buffer_rsrc_t rc = uniform_rsrc(a.oq + hrow * (kN / 2), kP * (kN / 2));
+    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(a.os + hrow * (kN / 32), kP * (kN / 32));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        o.code[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, s.lane * (kN / 2) + 16 * i, 0, 0));
+    o.scale = __builtin_amdgcn_raw_buffer_load_b32(rs, s.lane * (kN / 32), 0, 0);
+}
+
 template <typename TIn>
 __device__ __forceinline__ void load_c8(const TIn *Cin, int cq, float (&c8)[8]) {
     const float4 c0 = io<TIn>::load4(Cin + 8 * cq), c1 = io<TIn>::load4(Cin + 8 * cq + 4);
@@ -366,6 +386,56 @@ __device__ __forceinline__ void fp4_rows_dot_bf16(const Fp4Rows &o, const uint4 
         }
         y0[t] = reduce_scatter16(v, lane);
     }
+}
+
+// deq(row) . C for a lane's whole row (Fp4Row), C read from LDS: 128 bf16 as
+// 64 packed pairs (pair p = columns 2p, 2p+1), the same for every lane.  Per
+// block: the codes widened exactly to bf16 meet the pairs in packed bf16 dots
+// (exact products), then the block's scale; blocks summed in order.
+__device__ __forceinline__ float fp4_row_dot(const Fp4Row &o, const uint16_t *sC) {
+    const uint32_t *cp = reinterpret_cast<const uint32_t *>(sC);
+    float y = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        const uint32_t w[4] = {o.code[blk].x, o.code[blk].y, o.code[blk].z, o.code[blk].w};
+        float acc = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const uint4 c = *reinterpret_cast<const uint4 *>(cp + 16 * blk + 4 * d);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 0),
+                                                  __builtin_bit_cast(bf16x2, c.x), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 1),
+                                                  __builtin_bit_cast(bf16x2, c.y), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 2),
+                                                  __builtin_bit_cast(bf16x2, c.z), acc, false);
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 3),
+                                                  __builtin_bit_cast(bf16x2, c.w), acc, false);
+        }
+        y += acc * e4m3_decode((o.scale >> (8 * blk)) & 0xFFu);
+    }
+    return y;
+}
+
+// The same with fp32 C in LDS (128 floats): codes widened to f32, one fused
+// multiply-add per element.
+__device__ __forceinline__ float fp4_row_dot(const Fp4Row &o, const float *sC) {
+    float y = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        const uint32_t w[4] = {o.code[blk].x, o.code[blk].y, o.code[blk].z, o.code[blk].w};
+        float acc = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            float v[8];
+            e2m1_decode8(w[d], v);
+            const float4 c0 = *reinterpret_cast<const float4 *>(sC + 32 * blk + 8 * d);
+            const float4 c1 = *reinterpret_cast<const float4 *>(sC + 32 * blk + 8 * d + 4);
+            acc += v[0] * c0.x + v[1] * c0.y + v[2] * c0.z + v[3] * c0.w;
+            acc += v[4] * c1.x + v[5] * c1.y + v[6] * c1.z + v[7] * c1.w;
+        }
+        y += acc * e4m3_decode((o.scale >> (8 * blk)) & 0xFFu);
+    }
+    return y;
 }
 
 // y0[t] = deq(U) . C_t for this lane's row 2c + hf, every draft t, from the

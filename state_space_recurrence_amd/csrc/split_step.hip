@@ -108,6 +108,10 @@ __device__ __forceinline__ void lean_prologue(const ReplayParams &a, const Slot 
     const float Ah = o.A, Dh = o.D;
     {   // Gram row g_j = B_j . C, 16 lanes x 8 elements per dot
         const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4, ngrp = blockDim.x >> 4;
+        if (grp == 0) {   // C into LDS for the output dots (the first 16 lanes hold all of it)
+            *reinterpret_cast<typename io<TIn>::raw4 *>(&sm.C[8 * t16]) = o.c0;
+            *reinterpret_cast<typename io<TIn>::raw4 *>(&sm.C[8 * t16 + 4]) = o.c1;
+        }
         const float4 c0 = io<TIn>::widen(o.c0), c1 = io<TIn>::widen(o.c1);
         {
             const typename io<TIn>::raw4 b0 = grp < k ? o.b0 : o.n0, b1 = grp < k ? o.b1 : o.n1;
@@ -152,7 +156,7 @@ split_step_kernel(ReplayParams a) {
     if (blockIdx.x == 0 && threadIdx.x == 0) a.clist[kListLast] = a.clist[kListFill];
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
-    const int prow = MT::fp4_out ? fp4_prow(s.lane) : s.prow;
+    const int prow = MT::fp4_out ? s.lane : s.prow;   // FP4 output copy: a whole row per lane
     const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
 
     // the position, the prologue's operands, then the output-source rows, all
@@ -163,10 +167,10 @@ split_step_kernel(ReplayParams a) {
     LeanOperands<TIn, KMAX> ops;
     lean_operands<TIn, KMAX>(a, s, in, ops);
     __builtin_amdgcn_sched_barrier(0);
-    Fp4Rows o;
+    Fp4Row o;
     typename Raw4<UB>::T raw[kNB][kPerChunk];   // update-source chunks (low modes)
     if constexpr (MT::fp4_out) {
-        fp4_rows_load(a, s, o);
+        fp4_row_load(a, s, o);
     } else {
 #pragma unroll
         for (int q = 0; q < kNB; ++q)
@@ -182,16 +186,8 @@ split_step_kernel(ReplayParams a) {
     lean_prologue<TIn, KMAX>(a, s, in, ops, prow, sm, &lam, &ybuf);
 
     if constexpr (MT::fp4_out) {
-        float y0[1];
-        if constexpr (sizeof(TIn) == 2) {
-            const uint4 craw[1] = {load16(static_cast<const TIn *>(in.Cin) + 8 * (s.lane & 15))};
-            fp4_rows_dot_bf16<1>(o, craw, s.lane, y0);
-        } else {
-            float c8[1][8];
-            load_c8<TIn>(static_cast<const TIn *>(in.Cin), s.lane & 15, c8[0]);
-            fp4_rows_dot<1>(o, c8, s.lane, y0);
-        }
-        a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + prow] = lam * y0[0] + ybuf;
+        const float y0 = fp4_row_dot(o, sm.C);
+        a.y[(size_t)s.row * in.HP + (size_t)s.h * kP + prow] = lam * y0 + ybuf;
     } else {
         const float4 C4 = io<TIn>::load4(static_cast<const TIn *>(in.Cin) + 4 * s.c);
         float r[kChunks];
