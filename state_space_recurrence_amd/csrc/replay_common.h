@@ -363,6 +363,12 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
         const TIn *pb0 = (j0 < k) ? bb + (size_t)j0 * in.GN : Bin;
         const typename io<TIn>::raw4 rb0 = io<TIn>::load_raw4(pb0 + 8 * t16), rb1 = io<TIn>::load_raw4(pb0 + 8 * t16 + 4);
         const float4 c0 = io<TIn>::widen(rc0), c1 = io<TIn>::widen(rc1);
+        if constexpr (!SM::kCommit) {   // C into LDS for row-per-lane output dots (16 lanes hold all of it)
+            if (grp == 0) {
+                *reinterpret_cast<typename io<TIn>::raw4 *>(&sm.C[8 * t16]) = rc0;
+                *reinterpret_cast<typename io<TIn>::raw4 *>(&sm.C[8 * t16 + 4]) = rc1;
+            }
+        }
         {   // computed by every group (keeps the loads ahead), stored where grp < K
             const float acc = row16_sum(dot4(io<TIn>::widen(rb0), c0) + dot4(io<TIn>::widen(rb1), c1));
             if (grp < K && t16 == 0) sm.gram[grp] = acc;

@@ -51,99 +51,10 @@ __device__ __forceinline__ void publish_step(const ReplayParams &a, int b, int n
     }
 }
 
-// The lean step's prologue operands, requested together with the slot's
-// position instead of after it: the x rows, steps and (first Gram pass) B
-// entries of every buffer entry the position could select, and the current
-// token's.  The position then picks among them (entries past it are never
-// used, not even multiplied), so the prologue waits for one round trip of
-// loads, not two.  The extra entries are recent buffer writes, which the
-// fabric cache mostly still holds.
-template <typename TIn, int KMAX>
-struct LeanOperands {
-    uint4 xw[xt_loads<TIn, KMAX>()];   // x rows i * xt_rows + r0 of the buffer (16-byte pieces)
-    uint4 xc;                          // the current token's piece of the same columns
-    TIn dtb, dtc;                      // step of buffer entry min(lane, KMAX - 1); the current step
-    typename io<TIn>::raw4 c0, c1;     // C: 8 elements of the lane's 16-lane group
-    typename io<TIn>::raw4 b0, b1;     // B of buffer entry (thread / 16), same elements
-    typename io<TIn>::raw4 n0, n1;     // the current token's B, same elements
-    float A, D;                        // the head's decay rate and skip weight
-};
-
-template <typename TIn, int KMAX>
-__device__ __forceinline__ void lean_operands(const ReplayParams &a, const Slot &s, const StepIn &in,
-                                              LeanOperands<TIn, KMAX> &o) {
-    const TIn *xb = static_cast<const TIn *>(in.xb), *xin = static_cast<const TIn *>(in.xin);
-    const TIn *bb = static_cast<const TIn *>(in.bb), *Bin = static_cast<const TIn *>(in.Bin);
-    const TIn *Cin = static_cast<const TIn *>(in.Cin), *db = static_cast<const TIn *>(in.db);
-    const int lpr = kP / xt_elems<TIn>();
-    const int r0 = s.lane / lpr, col = xt_elems<TIn>() * (s.lane % lpr);
-#pragma unroll
-    for (int i = 0; i < xt_loads<TIn, KMAX>(); ++i) {
-        int j = i * xt_rows<TIn>() + r0;
-        j = j < KMAX ? j : KMAX - 1;
-        o.xw[i] = load16(xb + (size_t)j * in.HP + col);
-    }
-    o.xc = load16(xin + col);
-    o.dtb = db[(size_t)(s.lane < KMAX ? s.lane : KMAX - 1) * a.H];
-    o.dtc = *static_cast<const TIn *>(in.dtin);
-    const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4;
-    const int jb = grp < KMAX ? grp : KMAX - 1;
-    o.c0 = io<TIn>::load_raw4(Cin + 8 * t16);
-    o.c1 = io<TIn>::load_raw4(Cin + 8 * t16 + 4);
-    o.b0 = io<TIn>::load_raw4(bb + (size_t)jb * in.GN + 8 * t16);
-    o.b1 = io<TIn>::load_raw4(bb + (size_t)jb * in.GN + 8 * t16 + 4);
-    o.n0 = io<TIn>::load_raw4(Bin + 8 * t16);
-    o.n1 = io<TIn>::load_raw4(Bin + 8 * t16 + 4);
-    o.A = a.A[s.h];
-    o.D = a.D[s.h];
-}
-
-// The prologue of step_prologue (no commit) from those operands, once the
-// position (in.k) is known.
-template <typename TIn, int KMAX>
-__device__ __forceinline__ void lean_prologue(const ReplayParams &a, const Slot &s, const StepIn &in,
-                                              const LeanOperands<TIn, KMAX> &o, int prow,
-                                              StepSmemNoCommit<TIn, KMAX> &sm, float *lam, float *ybuf) {
-    const int k = in.k, K = in.K;
-    const float Ah = o.A, Dh = o.D;
-    {   // Gram row g_j = B_j . C, 16 lanes x 8 elements per dot
-        const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4, ngrp = blockDim.x >> 4;
-        if (grp == 0) {   // C into LDS for the output dots (the first 16 lanes hold all of it)
-            *reinterpret_cast<typename io<TIn>::raw4 *>(&sm.C[8 * t16]) = o.c0;
-            *reinterpret_cast<typename io<TIn>::raw4 *>(&sm.C[8 * t16 + 4]) = o.c1;
-        }
-        const float4 c0 = io<TIn>::widen(o.c0), c1 = io<TIn>::widen(o.c1);
-        {
-            const typename io<TIn>::raw4 b0 = grp < k ? o.b0 : o.n0, b1 = grp < k ? o.b1 : o.n1;
-            const float acc = row16_sum(dot4(io<TIn>::widen(b0), c0) + dot4(io<TIn>::widen(b1), c1));
-            if (grp < K && t16 == 0) sm.gram[grp] = acc;
-        }
-        const TIn *bb = static_cast<const TIn *>(in.bb), *Bin = static_cast<const TIn *>(in.Bin);
-        for (int j = grp + ngrp; j < K; j += ngrp) {   // entries past the first pass (KMAX > 16)
-            const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin;
-            const float4 b0 = io<TIn>::load4(pb + 8 * t16), b1 = io<TIn>::load4(pb + 8 * t16 + 4);
-            const float acc = row16_sum(dot4(b0, c0) + dot4(b1, c1));
-            if (t16 == 0) sm.gram[j] = acc;
-        }
-    }
-    const float d = s.lane < k ? io<TIn>::load1(&o.dtb) : (s.lane == k ? io<TIn>::load1(&o.dtc) : 0.f);
-    const int lpr = kP / xt_elems<TIn>();
-    const int r0 = s.lane / lpr, col = xt_elems<TIn>() * (s.lane % lpr);
-#pragma unroll
-    for (int i = 0; i < xt_loads<TIn, KMAX>(); ++i) {
-        const int j = i * xt_rows<TIn>() + r0;
-        if (j < K) store16(&sm.u.X[s.wave][j][col], j < k ? o.xw[i] : o.xc);
-    }
-    __syncthreads();
-    step_replay_terms<TIn, KMAX>(s, k, K, Ah * d, d, Dh, prow, sm, lam, ybuf);
-    __syncthreads();
-}
-
 // Waves per SIMD: the step is latency-bound, so as many as the registers
-// allow without spilling (five: the prologue operands requested with the
-// position take the registers a sixth wave would need).
+// allow without spilling.
 template <typename TIn>
-constexpr int step_waves(int) { return sizeof(TIn) == 2 ? 5 : 4; }
+constexpr int step_waves(int kmax) { return sizeof(TIn) == 2 ? (kmax == 16 ? 6 : 5) : 4; }
 
 template <typename TIn, int KMAX, int MODE>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(step_waves<TIn>(KMAX))))
@@ -159,14 +70,9 @@ split_step_kernel(ReplayParams a) {
     const int prow = MT::fp4_out ? s.lane : s.prow;   // FP4 output copy: a whole row per lane
     const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
 
-    // the position, the prologue's operands, then the output-source rows, all
-    // requested before the position is waited for, in this order (waits
-    // count loads in issue order: the prologue then waits for its own)
-    int pos_in = a.pos[s.b];
-    StepIn in = step_pointers<TIn>(a, s);
-    LeanOperands<TIn, KMAX> ops;
-    lean_operands<TIn, KMAX>(a, s, in, ops);
-    __builtin_amdgcn_sched_barrier(0);
+    // the position first (the prologue's first need), then the output-source
+    // rows; the prologue runs under them
+    const int pos_in = a.pos[s.b];
     Fp4Row o;
     typename Raw4<UB>::T raw[kNB][kPerChunk];   // update-source chunks (low modes)
     if constexpr (MT::fp4_out) {
@@ -177,13 +83,11 @@ split_step_kernel(ReplayParams a) {
 #pragma unroll
             for (int m = 0; m < kPerChunk; ++m) raw[q][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q, m), s.c);
     }
-    // first use of the position only here (keeps its wait, and any scalar
-    // copy of it, behind the loads above)
-    asm volatile("" : "+v"(pos_in));
-    step_position(in, a, a.L - 1, pos_in);
+
+    StepIn in = step_inputs<TIn>(a, s, a.L - 1, pos_in);
     in.commit = false;   // the interval-closing commit is the commit kernel's
     float lam, ybuf;
-    lean_prologue<TIn, KMAX>(a, s, in, ops, prow, sm, &lam, &ybuf);
+    step_prologue<TIn, KMAX>(a, s, in, prow, sm, &lam, &ybuf);
 
     if constexpr (MT::fp4_out) {
         const float y0 = fp4_row_dot(o, sm.C);
