@@ -70,6 +70,10 @@ def _desc(rs, **kw):
     ({"deferred_commit": 1, "max_draft": 1}, -2),
     ({"deferred_commit": 1, "max_draft": 5, "ckpt_dtype": 1, "out_dtype": 3}, -2),
     ({"deferred_commit": 1, "max_draft": 5, "interval": 28}, -3),
+    # low-precision states: the flat element index must fit 32 bits
+    ({"batch": 32767, "heads": 16, "groups": 2, "ckpt_dtype": 1, "out_dtype": 3}, 0),
+    ({"batch": 32768, "heads": 16, "groups": 2, "ckpt_dtype": 1, "out_dtype": 3}, -1),
+    ({"batch": 32768, "heads": 16, "groups": 2}, 0),                # fp32 checkpoint: no rounding stream
 ])
 def test_descriptor_validation(rs, kw, code):
     L = rs.lib()

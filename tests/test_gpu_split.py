@@ -399,3 +399,56 @@ def test_split_decode_staggered_phases(rs, fmt):
     rs.check_device_errors(ls)
     assert n_commits == sum((steps - j) // L for j in joined)
     assert ls.intv.cpu().tolist() == [(steps - joined[b]) // L for b in range(batch)]
+
+
+@pytest.mark.parametrize("fmt", ["split-bf16", "split-e4m3"])
+def test_split_largest_pool_element_index(rs, fmt):
+    """The largest pool a low-precision state accepts (its flat element
+    index must fit 32 bits: at 16 heads, 32,767 slots), with rows mapped to
+    slots on both sides of element 2^31 and to the last slot, so the
+    rounding draws' element index must be carried unsigned (a signed 32-bit
+    index would turn negative past 2^31).  The loaded checkpoint and one
+    interval's commit are checked bit-exact against the oracle's
+    quantisation with each slot's own element offset, and every output of
+    the interval against the oracle's replay (one slot more is refused by
+    the descriptor check, tested on the host)."""
+    w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
+    L = w.interval
+    elems = w.heads * 64 * 128
+    nslots = 0xFFFFFFFF // elems
+    slots = [0, (1 << 31) // elems - 1, (1 << 31) // elems, nslots - 1]
+    assert slots[1] * elems < (1 << 31) <= slots[2] * elems
+    rows = len(slots)
+    A, D = synth.layer_params(w, 1)
+    S0 = _special_state((rows, w.heads, 64, 128), torch.Generator().manual_seed(21))
+    x, Bm, Cm, dt = synth.token_inputs(w, 1, L, batch=rows, stream=9)
+    ls = rs.LayerState(nslots, w.heads, w.groups, A, D, interval=L, in_dtype=x.dtype, state_format=fmt,
+                       seed=SEED, layer_id=LAYER, debug_prequant=True)
+    idx = torch.tensor(slots, dtype=torch.int32, device="cuda")
+    rs.load_checkpoint(ls, S0.cuda(), slots=idx)
+    sl = idx.long()
+
+    def check_bytes(values, interval, what):
+        got_u = ls.ckpt[sl].cpu().numpy()
+        got_u = got_u.view(np.uint16) if _ufmt(fmt) == "bf16" else got_u
+        for r, b in enumerate(slots):
+            v = values[r].numpy().astype(np.float32)
+            ref = oracle.sr_quantize(v.reshape(-1), _ufmt(fmt), SEED, LAYER, interval, elem0=b * elems)
+            assert np.array_equal(got_u[r].reshape(-1), ref), f"{fmt} {what}: update bytes of slot {b}"
+            codes, scales = oracle.fp4_quantize(v)
+            assert np.array_equal(ls.out_q[b].cpu().numpy(), codes), f"{fmt} {what}: FP4 codes of slot {b}"
+            assert np.array_equal(ls.out_scale[b].cpu().numpy(), scales), f"{fmt} {what}: FP4 scales of slot {b}"
+
+    check_bytes(S0, 0, "load")
+    out_src = oracle.fp4_dequantize(ls.out_q[sl].cpu().numpy(), ls.out_scale[sl].cpu().numpy())
+    upd_src = _decode_u(fmt, ls.ckpt[sl])
+    ys = [rs.step(ls, x[t].cuda(), Bm[t].cuda(), Cm[t].cuda(), dt[t].cuda(), slots=idx).cpu() for t in range(L)]
+    _, y_ref = oracle.recurrent(out_src, x, Bm, Cm, dt, A, D, w.groups)
+    for t in range(L):
+        assert_close(ys[t], y_ref[t], f"{fmt} y at step {t}")
+    S_new, _ = oracle.recurrent(upd_src, x, Bm, Cm, dt, A, D, w.groups)
+    dump = ls.debug_prequant[sl].cpu()
+    assert_close(dump, S_new, f"{fmt} commit values")
+    check_bytes(dump, 1, "commit")
+    assert ls.intv[sl].cpu().tolist() == [1] * rows and ls.pos[sl].cpu().tolist() == [0] * rows
+    rs.check_device_errors(ls)
