@@ -58,9 +58,6 @@ template <> struct ModeTraits<kLowE4M3> {
     static constexpr int ubits = 8;
 };
 
-// Rows 4i + rg of the output copy for lane l = 16 rg + cq end up as row 4cq + rg.
-__device__ __forceinline__ int fp4_prow(int lane) { return 4 * (lane & 15) + (lane >> 4); }
-
 // ----------------------------------------------------------- 4-col rows --
 // Raw source values of 4 consecutive elements (columns 4c..4c+3) of a row,
 // in the update-source format UB (16: bf16, 8: E4M3, 4: FP4 code16 | scale<<16).
@@ -262,29 +259,6 @@ __device__ __forceinline__ void commit_head(const ReplayParams &a, const Slot &s
 }
 
 // ------------------------------------------------------ output streams --
-// Rows of the FP4 output copy in the 8-columns-per-lane layout.
-struct Fp4Rows {
-    uint32_t code[16];   // 8 codes (one dword) of rows 4i + rg
-    uint32_t scale[16];  // E4M3 scale of the lane's 32-element block of those rows
-};
-
-// The head's codes (4 KB) and scales (256 B) as buffer resources: one
-// scalar base each, the lane's offset in one VGPR, and the row group in the
-// constant scalar offset (row 4i + rg: 256 i bytes of codes, 16 i of
-// scales), so the 32 loads need no address arithmetic.
-__device__ __forceinline__ void fp4_rows_load(const ReplayParams &a, const Slot &s, Fp4Rows &o) {
-    const int rg = s.lane >> 4, cq = s.lane & 15;
-    const size_t hrow = ((size_t)s.b * a.H + s.h) * kP;
-    const __amdgpu_buffer_rsrc_t rc = uniform_rsrc(a.oq + hrow * (kN / 2), kP * (kN / 2));
-    const __amdgpu_buffer_rsrc_t rs = uniform_rsrc(a.os + hrow * (kN / 32), kP * (kN / 32));
-    const int vc = rg * (kN / 2) + 4 * cq, vs = rg * (kN / 32) + (cq >> 2);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        o.code[i] = __builtin_amdgcn_raw_buffer_load_b32(rc, vc, 4 * i * (kN / 2), 0);
-        o.scale[i] = __builtin_amdgcn_raw_buffer_load_b8(rs, vs, 4 * i * (kN / 32), 0);
-    }
-}
-
 // A lane's whole row of the FP4 copy (lane = row): 128 codes in four 16-byte
 // pieces (piece i = block i, columns 32i..32i+31, element n in nibble n of
 // its dword) and the row's four block scales in one dword (byte i = block
@@ -305,13 +279,6 @@ __device__ __forceinline__ void fp4_row_load(const ReplayParams &a, const Slot &
     o.scale = __builtin_amdgcn_raw_buffer_load_b32(rs, s.lane * (kN / 32), 0, 0);
 }
 
-template <typename TIn>
-__device__ __forceinline__ void load_c8(const TIn *Cin, int cq, float (&c8)[8]) {
-    const float4 c0 = io<TIn>::load4(Cin + 8 * cq), c1 = io<TIn>::load4(Cin + 8 * cq + 4);
-    c8[0] = c0.x; c8[1] = c0.y; c8[2] = c0.z; c8[3] = c0.w;
-    c8[4] = c1.x; c8[5] = c1.y; c8[6] = c1.z; c8[7] = c1.w;
-}
-
 // The 8 E2M1 values of a dword of codes (element n in nibble n), decoded by
 // gfx950's packed FP4 -> f32 conversion with unit scale (exact; the block's
 // E4M3 scale, which is not a power of two, is applied by the caller).
@@ -324,69 +291,7 @@ __device__ __forceinline__ void e2m1_decode8(uint32_t w, float (&d)[8]) {
     d[0] = a.x; d[1] = a.y; d[2] = b.x; d[3] = b.y; d[4] = c.x; d[5] = c.y; d[6] = e.x; d[7] = e.y;
 }
 
-// Reduce-scatter of 16 values over the 16 lanes of a DPP row: lane with low
-// bits cq keeps the total of item cq.
-__device__ __forceinline__ float reduce_scatter16(float (&v)[16], int lane) {
-    rs_stage<kDppRowMirror, 8>(v, (lane & 8) != 0);
-    rs_stage<kDppRowHalfMirror, 4>(v, (lane & 4) != 0);
-    rs_stage<kDppQuadRev, 2>(v, (lane & 2) != 0);
-    rs_stage<kDppQuadSwap1, 1>(v, (lane & 1) != 0);
-    return v[0];
-}
-
-// y0[t] = deq(O) . C_t for this lane's row 4cq + rg, every draft t.  The
-// codes are re-decoded per draft (4 packed conversions per 8 values) rather
-// than held decoded across drafts (128 VGPRs).
-template <int T>
-__device__ __forceinline__ void fp4_rows_dot(const Fp4Rows &o, const float (&c8)[T][8], int lane, float (&y0)[T]) {
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint32_t w = o.code[i], sraw = o.scale[i];
-            if (T > 1) asm volatile("" : "+v"(w), "+v"(sraw));   // fresh decode per draft
-            float d[8];
-            e2m1_decode8(w, d);
-            float acc = 0.f;
-#pragma unroll
-            for (int n = 0; n < 8; ++n) acc += d[n] * c8[t][n];
-            v[i] = acc * e4m3_decode(sraw);
-        }
-        y0[t] = reduce_scatter16(v, lane);
-    }
-}
-
-// The same for bf16 inputs: the codes widen exactly to bf16 (packed FP4 ->
-// bf16 conversion, two values per instruction) and meet the C values as
-// stored, two products per packed bf16 dot (products of an E2M1 value and a
-// bf16 value are exact in fp32).  craw[t] holds C_t's 8 bf16 of columns
-// 8cq..8cq+7.
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-template <int T>
-__device__ __forceinline__ void fp4_rows_dot_bf16(const Fp4Rows &o, const uint4 (&craw)[T], int lane, float (&y0)[T]) {
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const uint32_t cw[4] = {craw[t].x, craw[t].y, craw[t].z, craw[t].w};
-        float v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            uint32_t w = o.code[i], sraw = o.scale[i];
-            if (T > 1) asm volatile("" : "+v"(w), "+v"(sraw));   // fresh decode per draft
-            float acc = 0.f;
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0),
-                                                  __builtin_bit_cast(bf16x2, cw[0]), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1),
-                                                  __builtin_bit_cast(bf16x2, cw[1]), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2),
-                                                  __builtin_bit_cast(bf16x2, cw[2]), acc, false);
-            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3),
-                                                  __builtin_bit_cast(bf16x2, cw[3]), acc, false);
-            v[i] = acc * e4m3_decode(sraw);
-        }
-        y0[t] = reduce_scatter16(v, lane);
-    }
-}
 
 // deq(row) . C for a lane's whole row (Fp4Row), C read from LDS: 128 bf16 as
 // 64 packed pairs (pair p = columns 2p, 2p+1), the same for every lane.  Per

@@ -12,38 +12,43 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
     using MT = ModeTraits<MODE>;
     constexpr int UB = MT::ubits;
     __shared__ VerifySmem<KMAX, T> sm;
+    __shared__ __align__(16) TIn sC[T][kN];   // the drafts' C, for row-per-lane output dots
 
     const Slot s = slot_of(a);
     if (s.b < 0) return;   // padding row
-    const int prow = MT::fp4_out ? fp4_prow(s.lane) : s.prow;
+    const int prow = MT::fp4_out ? s.lane : s.prow;   // FP4 output copy: a whole row per lane
     const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
 
-    Fp4Rows o;
+    Fp4Row o;
     typename Raw4<UB>::T raw[32];
     if constexpr (MT::fp4_out) {
-        fp4_rows_load(a, s, o);
+        fp4_row_load(a, s, o);
     } else {
 #pragma unroll
         for (int i = 0; i < 32; ++i) raw[i] = load_row4<UB>(a, hrow + 2 * i, s.c);
     }
     const VerifyIn in = verify_inputs<TIn, T>(a, s, a.L - 1);
+    if constexpr (MT::fp4_out) {   // staged ahead of the prologue, whose barriers publish it
+        constexpr int per = 16 / (int)sizeof(TIn);   // elements per 16-byte piece
+        for (int q = threadIdx.x; q < T * kN / per; q += blockDim.x) {
+            const int t = q / (kN / per), c = per * (q - t * (kN / per));
+            store16(&sC[t][c], load16(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN + c));
+        }
+    }
     float ybuf[T];
     verify_prologue<TIn, KMAX, T>(a, s, in, prow, sm, ybuf);
 
     float y0[T];
     if constexpr (MT::fp4_out) {
-        if constexpr (sizeof(TIn) == 2) {
-            uint4 craw[T];
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                craw[t] = load16(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN + 8 * (s.lane & 15));
-            fp4_rows_dot_bf16<T>(o, craw, s.lane, y0);
-        } else {
-            float c8[T][8];
+        for (int t = 0; t < T; ++t) {
+            Fp4Row ot = o;   // decoded afresh per draft (holding 128 widened values would cost 64 VGPRs)
+            if (T > 1) {
 #pragma unroll
-            for (int t = 0; t < T; ++t)
-                load_c8<TIn>(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN, s.lane & 15, c8[t]);
-            fp4_rows_dot<T>(o, c8, s.lane, y0);
+                for (int i = 0; i < 4; ++i)
+                    asm volatile("" : "+v"(ot.code[i].x), "+v"(ot.code[i].y), "+v"(ot.code[i].z), "+v"(ot.code[i].w));
+            }
+            y0[t] = fp4_row_dot(ot, sC[t]);
         }
     } else {
         float4 C4[T];
