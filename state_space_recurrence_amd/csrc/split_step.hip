@@ -3,16 +3,17 @@
 //
 // A step runs as two launches.  The step kernel computes every row's output
 // from the output source and appends the token to the buffer -- also the
-// token that closes the interval: a slot that reaches L entries is published
-// at once (pos = 0, intv + 1) and listed, with its new interval index, in
-// the commit list.  The commit kernel then rewrites the listed slots' state
-// (update checkpoint by stochastic rounding, FP4 copy) from the update
-// source and the L buffered entries, one wave per head (or per half or
-// quarter of a head when few slots commit), before any later launch reads
-// it.  Keeping the commit out of the step kernel keeps the step's registers and LDS small (no spills, more waves per SIMD on the
-// latency-bound steps), and spreads each interval's commit work over the
-// whole chip whether the slots commit together (lock-step phases) or a few
-// on every step (staggered phases).
+// token that closes the interval: a slot that reaches L entries gets its new
+// interval index (intv + 1) at once and is listed with it in the commit
+// list.  The commit kernel then moves the call's positions on (pos + 1, or 0
+// for a closed interval), and rewrites the listed slots' state (update
+// checkpoint by stochastic rounding, FP4 copy) from the update source and
+// the L buffered entries, one wave per head (or per half or quarter of a head
+// when few slots commit), before any later launch reads it.  Keeping the
+// commit out of the step kernel keeps the step's registers and LDS small (no
+// spills, more waves per SIMD on the latency-bound steps), and spreads each
+// interval's commit work over the whole chip whether the slots commit
+// together (lock-step phases) or a few on every step (staggered phases).
 #include <atomic>
 #include "split_common.h"
 
@@ -20,34 +21,45 @@ namespace rssm {
 
 namespace {
 
-// Last-arriving workgroup of slot b publishes its new position.  When the
-// step closed the interval (new_pos == L) it publishes the committed state
-// (pos = 0, intv + 1) and lists the slot with the new interval index in the
-// list the step fills (kListFill, fixed while the step runs).  Duplicate rows
-// are flagged as in publish_position.
-__device__ __forceinline__ void publish_step(const ReplayParams &a, int b, int new_pos, int seen) {
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        const int old = atomicAdd(&a.work[b], 1);
-        if (old >= a.wg_per_slot) atomicOr(a.err, kErrDup);
-        if (old == a.wg_per_slot - 1) {
-            if (a.pos[b] != seen) atomicOr(a.err, kErrDup);
-            a.work[b] = 0;
-            if (new_pos == a.L) {
-                const int e = a.clist[kListFill] & 1;
-                const int iv = a.intv[b] + 1;
-                a.pos[b] = 0;
-                a.intv[b] = iv;
-                const int i = atomicAdd(&a.clist[e], 1);
-                if (i < a.nslots) {
-                    *reinterpret_cast<int2 *>(a.clist + kListHead + (size_t)e * 2 * a.nslots + 2 * i) = make_int2(b, iv);
-                } else {
-                    atomicOr(a.err, kErrDup);   // more listings than slots: rows repeated a slot
-                }
-            } else {
-                a.pos[b] = new_pos;
-            }
+// The end of a row's step.  Positions stay as they are during the step
+// (every workgroup of the row reads its slot's) and move on in the commit
+// pass, which every step launches next, so no workgroup waits for the others
+// of its row here.  The row's first workgroup marks the slot (a slot on two
+// rows is marked twice, which the commit pass flags) and, when the step
+// closes the interval (K == L), publishes the new interval index and lists
+// the slot with it in the list the step fills (kListFill, fixed while the
+// step runs).  The commit pass reads the entries only after the whole step.
+__device__ __forceinline__ void step_arrive(const ReplayParams &a, const Slot &s, int K) {
+    if (s.tile != 0 || threadIdx.x != 0) return;
+    const int b = s.b;
+    atomicAdd(&a.work[b], 1);   // result unused: nothing waits for it
+    if (K == a.L) {
+        const int e = a.clist[kListFill] & 1;
+        const int iv = a.intv[b] + 1;
+        a.intv[b] = iv;
+        const int i = atomicAdd(&a.clist[e], 1);
+        if (i < a.nslots) {
+            *reinterpret_cast<int2 *>(a.clist + kListHead + (size_t)e * 2 * a.nslots + 2 * i) = make_int2(b, iv);
+        } else {
+            atomicOr(a.err, kErrDup);   // more listings than slots: rows repeated a slot
         }
+    }
+}
+
+// The positions of the call's rows after a step (run by the commit pass,
+// thread t taking rows t, t + threads, ...): k + 1, or 0 where the step closed
+// the interval, with k the position the step read (clamped as the step did);
+// the slot's mark is checked (one row per slot) and cleared.
+__device__ __forceinline__ void advance_positions(const ReplayParams &a) {
+    const int nthreads = gridDim.x * blockDim.x;
+    for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < a.batch; r += nthreads) {
+        const int b = a.slot_idx ? a.slot_idx[r] : r;
+        if (b < 0 || b >= a.nslots) continue;   // padding, or flagged by the step
+        if (a.work[b] != 1) atomicOr(a.err, kErrDup);
+        int k = a.pos[b];
+        k = k < 0 ? 0 : (k > a.L - 1 ? a.L - 1 : k);
+        a.pos[b] = k + 1 == a.L ? 0 : k + 1;
+        a.work[b] = 0;
     }
 }
 
@@ -115,7 +127,7 @@ split_step_kernel(ReplayParams a) {
     }
 
     step_append<TIn>(a, s, in);   // entry k, including the interval's last (k = L - 1)
-    publish_step(a, s.b, in.K, in.seen);
+    step_arrive(a, s, in.K);
 }
 
 // Commit pass over the listed slots: item = (listed slot, head, part), one
@@ -149,6 +161,7 @@ split_commit_list_kernel(ReplayParams a) {
     __shared__ __align__(16) uint8_t stage[16 * (kN * (UB >= 8 ? UB / 8 : 1) + 16)];
     // counts of both lists, the list the next step fills, the list the last
     // step filled, in one load
+    advance_positions(a);
     const int4 hd = *reinterpret_cast<const int4 *>(a.clist);
     const int e = __builtin_amdgcn_readfirstlane(hd.w) & 1;
     // (a count beyond the slots means rows repeated a slot, flagged by the

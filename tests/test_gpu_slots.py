@@ -216,3 +216,24 @@ def test_duplicate_slots_are_flagged(rs, heads, batch):
     for b in (0, 2):   # the other slots are untouched
         assert torch.equal(pool.ckpt[b], before["ckpt"][b]) and pool.pos[b].item() == 0
     rs.check_device_errors(pool)   # the flag was cleared by the read
+
+
+@pytest.mark.parametrize("fmt", ["split-bf16", "low-e4m3"])
+def test_duplicate_slots_are_flagged_low_precision(rs, fmt):
+    """The same race on a low-precision state: the step marks each row's
+    slot once, and the commit pass that follows it (which also moves the
+    positions on) finds a slot marked by 40 rows and raises the flag; the
+    other slots' bytes and positions are untouched."""
+    w = synth.WORKLOADS["4b"]
+    A, D = synth.layer_params(w, 0)
+    x, Bm, Cm, dt = synth.token_inputs(w, 0, 1, batch=40, stream=38)
+    pool = rs.LayerState(3, w.heads, w.groups, A, D, in_dtype=x.dtype, state_format=fmt)
+    before = {k: v.clone() for k, v in pool.tensors().items()}
+    rs.step(pool, x[0].cuda(), Bm[0].cuda(), Cm[0].cuda(), dt[0].cuda(), slots=_idx([1] * 40))
+    with pytest.raises(rs.ReplaySSMError, match="same slot"):
+        rs.check_device_errors(pool)
+    for b in (0, 2):
+        for k, v in pool.tensors().items():
+            if v is not None and v.dim() > 0 and v.shape[0] == 3:
+                assert torch.equal(v[b], before[k][b]), f"{k} of slot {b} changed"
+    rs.check_device_errors(pool)
