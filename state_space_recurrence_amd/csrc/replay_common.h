@@ -408,8 +408,10 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
             else
                 stage_B<TIn, KMAX>(sm.u.B, bb, Bin, in.GN, k, K);
         }
+        __syncthreads();
     }
-    __syncthreads();
+    // (a step that never commits writes no LDS after the barrier above: its
+    // waves go on without waiting for each other)
 }
 
 // Append the current token at buffer entry k (x and dt per head; B once per
