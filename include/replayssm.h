@@ -43,8 +43,9 @@
  *    recorded in a sticky flag read by
  *    replayssm_check_device_errors().  Two rows of one call mapped to the
  *    same slot race (results undefined); the position-publishing kernels
- *    flag it in the same word when they see it (more arrivals on the slot
- *    than one row brings, or its position changed during the call).
+ *    flag it in the same word when they see it (more arrivals or marks on
+ *    the slot than one row brings, or its position changed during the
+ *    call).
  *
  * Shapes (B = batch, H = n_heads, P = head_dim, N = d_state, G = n_groups,
  * L = interval, Tmax = max_draft, Lcap = L + Tmax - 1):
@@ -148,7 +149,7 @@ typedef struct rssm_state {
     int32_t *pos;         /* [B] valid buffer entries since the checkpoint: 0..L-1 at rest,
                              up to Lcap after replayssm_accept_deferred */
     int32_t *intv;        /* [B] checkpoints written so far (the rounding stream's interval index) */
-    int32_t *work;        /* [B+1] library scratch: per-slot arrival counters + sticky error word; zero-initialise once */
+    int32_t *work;        /* [B+1] library scratch: per-slot arrival counters / marks + sticky error word; zero-initialise once */
     const float *A;       /* [H] decay rate, A < 0 */
     const float *D;       /* [H] skip weight */
     float *debug_prequant;/* optional [B,H,P,N] fp32: commit values before rounding (split path tests); NULL */
