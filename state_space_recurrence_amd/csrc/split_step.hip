@@ -183,7 +183,7 @@ split_commit_list_kernel(ReplayParams a) {
     const int lane = threadIdx.x & 63, pl = lane & 15, g = lane >> 4;
     const size_t HP = (size_t)H * kP, GN = (size_t)a.G * kN;
     const int hpg = H / a.G;
-    int it = blockIdx.x;
+    int it = xcd_remap(blockIdx.x, stride);   // consecutive items (a group's heads) on one XCD's L2
     if (it >= items) return;
     // list entries (slot, interval index of the new checkpoint); the next
     // item's is read ahead, issued before the current item's loads so that
