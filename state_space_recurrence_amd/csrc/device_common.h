@@ -130,6 +130,11 @@ constexpr int kDppRowMirror = 0x140;      // lane i <- lane 15-i within a 16-lan
 constexpr int kDppRowHalfMirror = 0x141;  // lane i <- lane 7-i within 8 lanes
 constexpr int kDppQuadRev = 0x1B;         // quad_perm [3,2,1,0]
 constexpr int kDppQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]
+constexpr int kDppRowShl1 = 0x101;        // lane i <- lane i+1 within a row (0 past its end)
+constexpr int kDppRowShl2 = 0x102;
+constexpr int kDppRowShl4 = 0x104;
+constexpr int kDppRowShl8 = 0x108;
+constexpr int kDppWaveShl1 = 0x130;       // lane i <- lane i+1 across the wave (0 for lane 63)
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -206,6 +211,24 @@ __device__ __forceinline__ float row16_sum(float v) {
     v += dpp<kDppRowHalfMirror>(v);
     v += dpp<kDppQuadRev>(v);
     v += dpp<kDppQuadSwap1>(v);
+    return v;
+}
+
+// Suffix sums over lanes 0..NL-1 (NL = 16 or 32): lane i gets the sum of v
+// over lanes i..NL-1 (Hillis-Steele within each row; for 32 lanes the second
+// row's total is then added to the first row).  Lanes at or past NL must hold
+// zeros.
+template <int NL>
+__device__ __forceinline__ float suffix_sum(float v, int lane) {
+    static_assert(NL == 16 || NL == 32, "one or two DPP rows");
+    v += dpp<kDppRowShl1>(v);
+    v += dpp<kDppRowShl2>(v);
+    v += dpp<kDppRowShl4>(v);
+    v += dpp<kDppRowShl8>(v);
+    if constexpr (NL == 32) {
+        const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+        if (lane < 16) v += r1;
+    }
     return v;
 }
 

@@ -228,6 +228,7 @@ template <typename TIn, int KMAX>
 struct __align__(16) StepSmemNoCommit {
     static constexpr bool kCommit = false;
     float gram[KMAX];
+    float cy[kMaxHpw][KMAX];   // per head: w_j g_j, read back as broadcasts
     union {
         TIn X[kMaxHpw][KMAX][kP];
     } u;
@@ -294,6 +295,31 @@ __device__ __forceinline__ StepIn step_inputs(const ReplayParams &a, const Slot 
 template <typename TIn, int KMAX, typename SM>
 __device__ __forceinline__ float step_replay_terms(const Slot &s, int k, int K, float l, float d, float Dh, int prow,
                                                    SM &sm, float *lam, float *ybuf) {
+    if constexpr (!SM::kCommit) {
+        // A step that never commits uses its weights for the output alone, so
+        // the sums need not follow the commit's ascending order: a DPP suffix
+        // scan gives every lane sum_{i >= lane} l_i at once (l_i = 0 for
+        // i >= K), its right neighbour's value is the exclusive suffix, lane
+        // 0's the total.  w_j g_j goes to LDS and returns as broadcasts; the
+        // x rows in LDS up to K rounded up to 4 hold finite values (entries
+        // past K repeat entry K-1) and meet zero weights there, so the sum
+        // needs no selects.
+        const float R = suffix_sum<KMAX>(l, s.lane);
+        const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, R), 0));
+        const float suf = dpp<kDppWaveShl1>(R);
+        *lam = expf(tot);
+        const float wj = s.lane < K ? d * expf(suf) : 0.f;
+        if (s.lane < KMAX) sm.cy[s.wave][s.lane] = s.lane < K ? wj * sm.gram[s.lane] : 0.f;
+        const TIn *xrow = &sm.u.X[s.wave][0][prow];
+        const float *cy = sm.cy[s.wave];
+        float yb = Dh * io<TIn>::load1(xrow + k * kP);
+        for (int j0 = 0; j0 < K; j0 += 4) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) yb = fmaf(cy[j0 + u], io<TIn>::load1(xrow + (j0 + u) * kP), yb);
+        }
+        *ybuf = yb;
+        return wj;
+    }
     float tot = 0.f, suf = 0.f;
     for (int i = 0; i < K; ++i) {
         const float li = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
@@ -384,7 +410,9 @@ __device__ __forceinline__ void step_prologue(const ReplayParams &a, const Slot 
 #pragma unroll
     for (int i = 0; i < xt_loads<TIn, KMAX>(); ++i) {
         const int j = i * xt_rows<TIn>() + r0;
-        if (i * xt_rows<TIn>() < K && j < K) store16(&sm.u.X[s.wave][j][col], xw[i]);
+        // steps that never commit also keep the repeated rows past K (the
+        // output sum reads up to K rounded up to 4)
+        if (i * xt_rows<TIn>() < K && (!SM::kCommit || j < K)) store16(&sm.u.X[s.wave][j][col], xw[i]);
     }
     __syncthreads();
     const float wj = step_replay_terms<TIn, KMAX>(s, k, K, Ah * d, d, Dh, prow, sm, lam, ybuf);

@@ -46,13 +46,16 @@ __device__ __forceinline__ void step_arrive(const ReplayParams &a, const Slot &s
     }
 }
 
-// The positions of the call's rows after a step (run by the commit pass,
-// thread t taking rows t, t + threads, ...): k + 1, or 0 where the step closed
-// the interval, with k the position the step read (clamped as the step did);
-// the slot's mark is checked (one row per slot) and cleared.
-__device__ __forceinline__ void advance_positions(const ReplayParams &a) {
+// The positions of the call's rows after a step (run by the commit pass):
+// k + 1, or 0 where the step closed the interval, with k the position the
+// step read (clamped as the step did); the slot's mark is checked (one row per
+// slot) and cleared.  The workgroup of rank w takes rows 64w + lane, then
+// those a grid further on; the pass gives rank 0 to the workgroup with the
+// last item, so on a short list these rows go to waves with no item, and
+// the item waves' load chains do not wait for them.
+__device__ __forceinline__ void advance_positions(const ReplayParams &a, int rank) {
     const int nthreads = gridDim.x * blockDim.x;
-    for (int r = blockIdx.x * blockDim.x + threadIdx.x; r < a.batch; r += nthreads) {
+    for (int r = rank * blockDim.x + threadIdx.x; r < a.batch; r += nthreads) {
         const int b = a.slot_idx ? a.slot_idx[r] : r;
         if (b < 0 || b >= a.nslots) continue;   // padding, or flagged by the step
         if (a.work[b] != 1) atomicOr(a.err, kErrDup);
@@ -159,10 +162,12 @@ split_commit_list_kernel(ReplayParams a) {
     constexpr int NKB = KMAX / 4;
     // the wave's staging tile for the update checkpoint's rows (bf16 or E4M3)
     __shared__ __align__(16) uint8_t stage[16 * (kN * (UB >= 8 ? UB / 8 : 1) + 16)];
+    const int stride = gridDim.x;
+    int it = xcd_remap(blockIdx.x, stride);   // consecutive items (a group's heads) on one XCD's L2
     // counts of both lists, the list the next step fills, the list the last
-    // step filled, in one load
-    advance_positions(a);
+    // step filled, in one load, in flight while the positions move on
     const int4 hd = *reinterpret_cast<const int4 *>(a.clist);
+    advance_positions(a, stride - 1 - it);
     const int e = __builtin_amdgcn_readfirstlane(hd.w) & 1;
     // (a count beyond the slots means rows repeated a slot, flagged by the
     // step; only the entries written are read)
@@ -173,7 +178,6 @@ split_commit_list_kernel(ReplayParams a) {
         a.clist[kListFill] = 1 - e;
     }
     const int H = a.H;
-    const int stride = gridDim.x;
     // parts per head: as many as keep every item on a wave of its own, one
     // when the heads alone fill the grid (the grid is the resident waves)
     const int parts = nlisted * H * 4 <= stride ? 4 : nlisted * H * 2 <= stride ? 2 : 1;
@@ -183,7 +187,6 @@ split_commit_list_kernel(ReplayParams a) {
     const int lane = threadIdx.x & 63, pl = lane & 15, g = lane >> 4;
     const size_t HP = (size_t)H * kP, GN = (size_t)a.G * kN;
     const int hpg = H / a.G;
-    int it = xcd_remap(blockIdx.x, stride);   // consecutive items (a group's heads) on one XCD's L2
     if (it >= items) return;
     // list entries (slot, interval index of the new checkpoint); the next
     // item's is read ahead, issued before the current item's loads so that
