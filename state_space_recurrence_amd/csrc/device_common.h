@@ -83,6 +83,19 @@ __device__ __forceinline__ void stream_store4(float *p, float4 v) {
     __builtin_nontemporal_store(u, reinterpret_cast<f4v *>(p));
 }
 
+// The same for 16 bytes of packed codes.
+typedef unsigned int u4v __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 stream_load16(const uint4 *p) {
+    const u4v v = __builtin_nontemporal_load(reinterpret_cast<const u4v *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void stream_store16(uint4 *p, uint4 v) {
+    const u4v u = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(u, reinterpret_cast<u4v *>(p));
+}
+
 // Buffer-resource form of the same accesses (raw buffer, stride 0): word 3
 // of the descriptor selects 32-bit data; cache-policy operand 2 is the
 // non-temporal hint.

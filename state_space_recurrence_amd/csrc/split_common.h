@@ -68,10 +68,15 @@ template <> struct Raw4<4> { using T = uint32_t; };
 
 template <int UB>
 __device__ __forceinline__ typename Raw4<UB>::T load_row4(const ReplayParams &a, size_t row, int c) {
+    // (the single checkpoint is streamed whole on every step: non-temporal,
+    // like the fp32 checkpoint stream)
     if constexpr (UB == 16) {
-        return *reinterpret_cast<const uint2 *>(reinterpret_cast<const uint16_t *>(a.u) + row * kN + 4 * c);
+        typedef unsigned int u2v __attribute__((ext_vector_type(2)));
+        const u2v t = __builtin_nontemporal_load(
+            reinterpret_cast<const u2v *>(reinterpret_cast<const uint16_t *>(a.u) + row * kN + 4 * c));
+        return make_uint2(t.x, t.y);
     } else if constexpr (UB == 8) {
-        return *reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(a.u) + row * kN + 4 * c);
+        return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(reinterpret_cast<const uint8_t *>(a.u) + row * kN + 4 * c));
     } else {
         const uint32_t code16 = *reinterpret_cast<const uint16_t *>(a.oq + row * (kN / 2) + 2 * c);
         const uint32_t sc = a.os[row * (kN / 32) + (c >> 3)];
@@ -419,8 +424,11 @@ __device__ __forceinline__ void load_block(const ReplayParams &a, const BlockAt 
         constexpr int eb = UB / 8;   // bytes per element
         const uint4 *p = off_bytes(reinterpret_cast<const uint4 *>(reinterpret_cast<const uint8_t *>(a.u) + at.row0 * (kN * eb)),
                                    (uint32_t)((at.r * kN + 32 * at.g) * eb));
+        // (non-temporal: the update source is streamed once per interval and
+        // would otherwise displace the output copies and buffer entries that
+        // the next steps read from the fabric cache)
 #pragma unroll
-        for (int k = 0; k < 2 * eb; ++k) r.q[k] = p[k];
+        for (int k = 0; k < 2 * eb; ++k) r.q[k] = stream_load16(p + k);
     } else {
         r.q[0] = *off_bytes(reinterpret_cast<const uint4 *>(a.oq + at.row0 * (kN / 2)), (uint32_t)(at.r * (kN / 2) + 16 * at.g));
         r.sc = *off_bytes(a.os + at.row0 * (kN / 32), (uint32_t)(at.r * (kN / 32) + at.g));
@@ -662,7 +670,7 @@ __device__ __forceinline__ void quantize_store_block(const ReplayParams &a, cons
         for (int m = 0; m < 16 * rowb / 1024; ++m) {
             const uint32_t i = 1024 * m + 16 * lane;   // byte within the 16 rows
             const uint4 d = *reinterpret_cast<const uint4 *>(stage + (i / rowb) * pitch + i % rowb);
-            *off_bytes(reinterpret_cast<uint4 *>(ub), i) = d;
+            stream_store16(off_bytes(reinterpret_cast<uint4 *>(ub), i), d);
         }
         __builtin_amdgcn_wave_barrier();
     }
@@ -691,8 +699,12 @@ __device__ __forceinline__ void quantize_store_block(const ReplayParams &a, cons
 #pragma unroll
             for (int k = 0; k < 4; ++k) c[k] = fp4_exact8(e + 8 * k, t, sc == 0u);
         }
-        *off_bytes(reinterpret_cast<uint4 *>(a.oq + at.row0 * (kN / 2)), lrow / 2) = make_uint4(c[0], c[1], c[2], c[3]);
-        *off_bytes(a.os + at.row0 * (kN / 32), lrow / 32) = (uint8_t)sc;
+        // (the commit's stores are non-temporal: written back to memory as
+        // they go, not left dirty in the fabric cache for the next launches
+        // to evict)
+        stream_store16(off_bytes(reinterpret_cast<uint4 *>(a.oq + at.row0 * (kN / 2)), lrow / 2),
+                       make_uint4(c[0], c[1], c[2], c[3]));
+        __builtin_nontemporal_store((uint8_t)sc, off_bytes(a.os + at.row0 * (kN / 32), lrow / 32));
     }
 }
 
