@@ -161,7 +161,7 @@ split_commit_list_kernel(ReplayParams a) {
     constexpr int UB = ModeTraits<MODE>::ubits;
     constexpr int NKB = KMAX / 4;
     // the wave's staging tile for the update checkpoint's rows (bf16 or E4M3)
-    __shared__ __align__(16) uint8_t stage[16 * (kN * (UB >= 8 ? UB / 8 : 1) + 16)];
+    __shared__ __align__(16) uint8_t stage[16 * stage_pitch<UB>()];
     const int stride = gridDim.x;
     int it = xcd_remap(blockIdx.x, stride);   // consecutive items (a group's heads) on one XCD's L2
     // counts of both lists, the list the next step fills, the list the last
@@ -249,11 +249,12 @@ split_commit_list_kernel(ReplayParams a) {
         for (int kb = 0; kb < NKB; ++kb) w[kb] = __shfl(wj, 4 * kb + g);
         // one quarter: coefficients w_j x_j[r] of the lane's row for entries
         // j = 4kb + g, the update, the rounding and the stores
-        auto commit_quarter = [&](int q, const RawBlock<UB> &raw, const float (&xq)[NKB]) {
+        auto commit_quarter = [&](int q, RawBlock<UB> &raw, const float (&xq)[NKB]) {
             float cf[NKB];
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) cf[kb] = 4 * kb + g < K ? w[kb] * xq[kb] : 0.f;
             float e[32];
+            block_to_lanes<UB>(BlockAt{hrow0 + 16 * q, pl, g}, raw, stage);
             decode_block<UB>(raw, e);
             mfma_update<TIn, KMAX>(e, lam, cf, bo, g, K);
             quantize_store_block<MODE>(a, BlockAt{hrow0 + 16 * q, pl, g}, e, interval, stage);
