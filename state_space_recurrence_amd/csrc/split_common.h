@@ -637,12 +637,19 @@ __device__ __forceinline__ void quantize_store_block(const ReplayParams &a, cons
         for (int k = 0; k < 8; ++k)
             stream_store4(db + 4 * k, make_float4(e[4 * k], e[4 * k + 1], e[4 * k + 2], e[4 * k + 3]));
     }
-    // twice the largest magnitude bit pattern (sign shifted out; a form no
-    // later quantiser step shares, so none of the 32 values is kept for it)
-    uint32_t mmax2 = 0;
+    // the largest magnitude bit pattern from two three-way reductions of the
+    // raw bits: the unsigned maximum is the largest negative value's pattern
+    // (sign set) when there is one, the signed maximum the largest
+    // non-negative value's (negative when there is none)
+    uint32_t umax = 0;
+    int32_t imax = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) mmax2 = max(mmax2, __float_as_uint(e[i]) << 1);
-    const bool plain = mmax2 <= (0x7F7F0000u << 1);
+    for (int i = 0; i < 32; i += 2) {
+        umax = max(umax, max(__float_as_uint(e[i]), __float_as_uint(e[i + 1])));   // v_max3_u32
+        imax = max(imax, max(__float_as_int(e[i]), __float_as_int(e[i + 1])));      // v_max3_i32
+    }
+    const uint32_t mmag = max(umax & 0x7FFFFFFFu, (uint32_t)imax);   // imax starts at 0: never negative
+    const bool plain = mmag <= 0x7F7F0000u;
     if constexpr (MT::has_u) {
         // The rounded block goes through the wave's LDS tile (16 rows of the
         // update checkpoint) and leaves it in 1 KB contiguous stores: the
@@ -713,7 +720,7 @@ __device__ __forceinline__ void quantize_store_block(const ReplayParams &a, cons
         uint32_t sc;
         bool exact = !plain;
         if (plain) {
-            sc = fp4_scale_code(__uint_as_float(mmax2 >> 1));
+            sc = fp4_scale_code(__uint_as_float(mmag));
             const float r = sc == 0u ? 0.f : __builtin_amdgcn_rcpf(e4m3_decode(sc));
             const float rlo = r * (1.0f - 0x1p-20f), rhi = r * (1.0f + 0x1p-20f);
             uint32_t diff = 0;

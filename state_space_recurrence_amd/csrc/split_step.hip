@@ -231,17 +231,16 @@ split_commit_list_kernel(ReplayParams a) {
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
             load_b8<TIn>(off_bytes(bb, (uint32_t)((jrow[kb] * (int)GN + 8 * pl) * sizeof(TIn))), bo[kb]);
-        // l_i = A dt_i in lane i; Lambda_K and w_j = dt_j exp(sum_{j<i<K} l_i)
-        // with the sums grown in ascending i (the commit arithmetic of every
-        // other commit path)
+        // l_i = A dt_i in lane i (zero from K on); Lambda_K and
+        // w_j = dt_j exp(sum_{j<i<K} l_i) from one DPP suffix scan: lane i
+        // holds sum_{m>=i} l_m, its right neighbour's value is lane i's
+        // exclusive suffix and lane 0's the total.  (The stored bytes are the
+        // rounding of this pass's own fp32 values, so the summation order
+        // only has to keep those values within the parity bound.)
         const float dl = lane < K ? dt_l : 0.f;
-        const float l = Ah * dl;
-        float tot = 0.f, suf = 0.f;
-        for (int i = 0; i < K; ++i) {
-            const float li_ = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, l), i));
-            tot += li_;
-            if (i > lane) suf += li_;
-        }
+        const float R = suffix_sum<KMAX>(Ah * dl, lane);
+        const float tot = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, R), 0));
+        const float suf = dpp<kDppWaveShl1>(R);
         const float wj = lane < K ? dl * expf(suf) : 0.f;
         const float lam = expf(tot);
         float w[NKB];
