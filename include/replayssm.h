@@ -336,10 +336,15 @@ int replayssm_check_device_errors(const rssm_state *st, int32_t n_slots, hipStre
  *              of |v| / scale (precision split, article section 4);
  *   counts[1]: patterns with |v| <= 0x7F7F0000 where bf16 stochastic rounding
  *              by integer addition differs from the selecting form (a draw
- *              hashed from the pattern).
- * counts: device array of 2 unsigned 64-bit counters, zeroed by the caller;
+ *              hashed from the pattern);
+ *   counts[2]: (pattern, draw) pairs, NaNs included, where the E4M3
+ *              stochastic rounding the kernels use (carry form in the normal
+ *              range, exact floor split below it) differs from the grid-split
+ *              form (two draws per pattern: the hashed one and its
+ *              complement).
+ * counts: device array of 3 unsigned 64-bit counters, zeroed by the caller;
  * the kernel adds to them.  Asynchronous on stream; RSSM_E_ARG for a NULL
- * counts or begin > end or end > 2^32.  Both counts are 0 on a conforming
+ * counts or begin > end or end > 2^32.  All counts are 0 on a conforming
  * device.
  */
 int replayssm_check_conversions(uint64_t begin, uint64_t end, unsigned long long *counts, hipStream_t stream);

@@ -356,8 +356,8 @@ def hbm_probe(mode: int, src: torch.Tensor, dst: torch.Tensor, grid: int, stream
 def check_conversions(begin: int = 0, end: int = 1 << 32, stream=None) -> tuple:
     """Run the device conversion self-check over fp32 bit patterns
     [begin, end); returns (FP4 conversion mismatches, bf16 rounding
-    mismatches) -- both 0 on a conforming device."""
-    counts = torch.zeros(2, dtype=torch.int64, device="cuda")
+    mismatches, E4M3 rounding mismatches) -- all 0 on a conforming device."""
+    counts = torch.zeros(3, dtype=torch.int64, device="cuda")
     _check(lib().replayssm_check_conversions(begin, end, _ptr(counts), _stream(stream)))
     return tuple(int(c) for c in counts.cpu())
 

@@ -81,26 +81,27 @@ __global__ void __launch_bounds__(256) probe_head_read_kernel(const float *src, 
 __global__ void __launch_bounds__(256) conversion_check_kernel(uint64_t begin, uint64_t end,
                                                                unsigned long long *counts) {
     const Fp4Thresholds t = fp4_thresholds(1.0f);
-    unsigned long long bad_fp4 = 0, bad_sr = 0;
+    unsigned long long bad_fp4 = 0, bad_sr = 0, bad_e4m3 = 0;
     const uint64_t step = (uint64_t)gridDim.x * blockDim.x;
     for (uint64_t i = begin + (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < end; i += step) {
         const uint32_t bits = (uint32_t)i;
         const uint32_t mag = bits & 0x7FFFFFFFu;
-        if (mag > 0x7F800000u) continue;
         const float v = __uint_as_float(bits);
+        uint32_t w = bits * 0x9E3779B1u;   // a draw hashed from the pattern
+        w ^= w >> 15;
+        w *= 0x85EBCA77u;
+        w ^= w >> 13;
+        const uint32_t r16 = w & 0xFFFFu;
+        // E4M3 stochastic rounding, NaNs included, with the draw and its complement
+        bad_e4m3 += (e4m3_sr(v, r16) != e4m3_sr_grid(v, r16)) + (e4m3_sr(v, r16 ^ 0xFFFFu) != e4m3_sr_grid(v, r16 ^ 0xFFFFu));
+        if (mag > 0x7F800000u) continue;
         const uint32_t hw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v, 0.0f, 1.0f, 0) & 0xFu;
         bad_fp4 += hw != fp4_encode(v, t, false);
-        if (mag <= 0x7F7F0000u) {
-            uint32_t w = bits * 0x9E3779B1u;
-            w ^= w >> 15;
-            w *= 0x85EBCA77u;
-            w ^= w >> 13;
-            const uint32_t r16 = w & 0xFFFFu;
-            bad_sr += ((bits + (r16 ^ 0xFFFFu)) >> 16) != bf16_sr(v, r16);
-        }
+        if (mag <= 0x7F7F0000u) bad_sr += ((bits + (r16 ^ 0xFFFFu)) >> 16) != bf16_sr(v, r16);
     }
     if (bad_fp4) atomicAdd(&counts[0], bad_fp4);
     if (bad_sr) atomicAdd(&counts[1], bad_sr);
+    if (bad_e4m3) atomicAdd(&counts[2], bad_e4m3);
 }
 
 }  // namespace

@@ -129,7 +129,7 @@ __device__ __forceinline__ uint32_t e4m3_encode_grid(uint32_t k, int qe) {
 
 constexpr uint32_t kE4M3MaxBits = 0x43E00000u;   // 448.0f
 
-__device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t r16) {
+__device__ __forceinline__ uint32_t e4m3_sr_grid(float v, uint32_t r16) {
     const uint32_t bits = __float_as_uint(v);
     const uint32_t mag = bits & 0x7FFFFFFFu;
     const uint32_t sign = (bits >> 24) & 0x80u;
@@ -142,6 +142,28 @@ __device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t r16) {
     code = code < 0x7Eu ? code : 0x7Eu;
     code = mag >= kE4M3MaxBits ? 0x7Eu : code;                  // saturate at 448 (inf too)
     return mag > 0x7F800000u ? 0x7Fu : (sign | code);          // NaN -> canonical NaN
+}
+
+// The same rounding in fewer operations (the form the kernels use; the
+// conversion self-check compares the two over every fp32 pattern).  In the
+// normal range [2^-6, 448) the grid drops the low 20 bits of the fp32
+// pattern, and rem > 16 r16 is exactly the carry out of those bits when
+// 0xFFFFF - 16 r16 is added, the carry moving into the 3-bit mantissa and
+// the exponent where it must; the code is then the pattern's top bits less
+// the exponent bias difference.  Below 2^-6 the grid is k 2^-9:
+// y = |v| 2^9 = k + f exactly (scaling by a power of two, floor and the
+// difference are exact), and the rounding goes up iff r16 < f 2^16.
+__device__ __forceinline__ uint32_t e4m3_sr(float v, uint32_t r16) {
+    const uint32_t bits = __float_as_uint(v);
+    const uint32_t mag = bits & 0x7FFFFFFFu;
+    const uint32_t sign = (bits >> 24) & 0x80u;
+    const uint32_t cn = ((mag + (0xFFFFFu - (r16 << 4))) >> 20) - (120u << 3);
+    const float y = __uint_as_float(mag) * 512.0f;
+    const float k = floorf(y);
+    const uint32_t cs = (uint32_t)k + (((float)r16 < (y - k) * 65536.0f) ? 1u : 0u);
+    uint32_t code = mag >= 0x3C800000u ? cn : cs;    // 2^-6: the smallest normal
+    code = mag >= kE4M3MaxBits ? 0x7Eu : code;        // saturate at 448 (inf too)
+    return mag > 0x7F800000u ? 0x7Fu : (sign | code);  // NaN -> canonical NaN
 }
 
 // Round-to-nearest-even of a non-negative finite fp32 magnitude to E4M3,
