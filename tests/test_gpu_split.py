@@ -152,6 +152,16 @@ def test_split_decode_teacher_forced(rs, fmt):
     _run_intervals(rs, fmt, w, batch=3, n_intervals=3, tail=5)
 
 
+@pytest.mark.parametrize("fmt", ["split-bf16", "split-e4m3", "shared-fp4"])
+@pytest.mark.parametrize("L", [24, 32])
+def test_split_decode_long_intervals(rs, fmt, L):
+    """Intervals longer than 16 run the 32-entry step and commit instances
+    (their decay sums span two DPP rows); outputs and commit values against
+    the oracle, stored bytes bit-exact, over two intervals and a tail."""
+    w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2, interval=L)
+    _run_intervals(rs, fmt, w, batch=3, n_intervals=2, tail=5)
+
+
 @pytest.mark.parametrize("batch", [200, 300])
 def test_split_commit_long_lists(rs, batch):
     """Every slot closes its interval on the same step: at 16 heads, 200 and
