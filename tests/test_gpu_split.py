@@ -162,13 +162,15 @@ def test_split_decode_long_intervals(rs, fmt, L):
     _run_intervals(rs, fmt, w, batch=3, n_intervals=2, tail=5)
 
 
-@pytest.mark.parametrize("batch", [200, 300])
-def test_split_commit_long_lists(rs, batch):
-    """Every slot closes its interval on the same step: at 16 heads, 200 and
-    300 listed slots make the commit pass give each wave half a head and a
-    whole head (the short lists of the other tests give it single quarters)."""
+@pytest.mark.parametrize("fmt,batch", [("split-bf16", 90)] + [(f, 300) for f in SPLIT_FORMATS])
+def test_split_commit_long_lists(rs, fmt, batch):
+    """Every slot closes its interval on the same step: at 16 heads on
+    MI355X (3,072 or 4,096 resident commit waves), 90 listed slots make the
+    commit pass give each wave half a head and 300 whole heads, several per
+    wave (the short lists of the other tests give it single quarters); every
+    format's update source goes through the coalesced loads."""
     w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
-    _run_intervals(rs, "split-bf16", w, batch=batch, n_intervals=1, tail=1)
+    _run_intervals(rs, fmt, w, batch=batch, n_intervals=1, tail=1)
 
 
 def test_split_decode_4b_layout(rs):
