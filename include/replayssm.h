@@ -158,10 +158,12 @@ typedef struct rssm_state {
                                 must be distinct (a duplicate is flagged when detected, see above).
                                 Rows mapped outside 0..S-1 are skipped and flagged */
     int32_t *commit_list; /* [RSSM_COMMIT_LIST_WORDS(S)] int32, zero-initialise once and leave to the
-                             library afterwards: the slots whose interval a low-precision step
-                             closes, committed by the step's second launch (needed by
-                             replayssm_step with BF16 / FP8 / shared-FP4 states; unused, may be
-                             NULL, otherwise).  Calls on one state must not overlap */
+                             library afterwards: the slots whose interval a low-precision step,
+                             accept or flush closes, committed by the call's second launch
+                             (needed by replayssm_step, replayssm_accept and replayssm_commit
+                             with BF16 / FP8 / shared-FP4 states, RSSM_E_ARG when NULL there;
+                             unused, may be NULL, otherwise).  Calls on one state must not
+                             overlap */
 } rssm_state;
 
 /*

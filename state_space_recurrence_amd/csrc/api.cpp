@@ -262,7 +262,10 @@ int replayssm_accept(const rssm_desc *desc, const rssm_state *st, const int32_t 
     p.T = T;
     const bool bf = desc->in_dtype == RSSM_BF16;
     const int mode = split_mode(desc);
-    if (mode >= 0) return hip_status(rssm::launch_split_commit(p, bf, mode, true, stream), "split accept launch");
+    if (mode >= 0) {
+        if (!st->commit_list) return fail(RSSM_E_ARG, "accept: a low-precision state needs state->commit_list");
+        return hip_status(rssm::launch_split_accept(p, bf, mode, true, stream), "split accept launch");
+    }
     return hip_status(rssm::launch_replay_commit(p, bf, true, stream), "accept launch");
 }
 
@@ -289,7 +292,10 @@ int replayssm_commit(const rssm_desc *desc, const rssm_state *st, hipStream_t st
     rssm::ReplayParams p = replay_params(desc, st);
     const bool bf = desc->in_dtype == RSSM_BF16;
     const int mode = split_mode(desc);
-    if (mode >= 0) return hip_status(rssm::launch_split_commit(p, bf, mode, false, stream), "split commit launch");
+    if (mode >= 0) {
+        if (!st->commit_list) return fail(RSSM_E_ARG, "commit: a low-precision state needs state->commit_list");
+        return hip_status(rssm::launch_split_accept(p, bf, mode, false, stream), "split commit launch");
+    }
     return hip_status(rssm::launch_replay_commit(p, bf, false, stream), "commit launch");
 }
 

@@ -73,7 +73,6 @@ hipError_t launch_defer_accept(const ReplayParams &p, hipStream_t s);
 hipError_t launch_prefill(const ReplayParams &p, bool in_bf16, bool outputs, int mode, hipStream_t s);
 hipError_t launch_split_step(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
 hipError_t launch_split_verify(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
-hipError_t launch_split_commit(const ReplayParams &p, bool in_bf16, int mode, bool accept, hipStream_t s);
 hipError_t launch_split_load(const ReplayParams &p, int mode, hipStream_t s);
 hipError_t launch_recurrent(const RecurrentParams &p, bool in_bf16, bool pool, hipStream_t s);
 hipError_t launch_conversion_check(uint64_t begin, uint64_t end, unsigned long long *counts, hipStream_t stream);
@@ -85,13 +84,20 @@ hipError_t launch_recurrent_accept(int32_t *sel, const int32_t *n_keep, int batc
 // words): two lists used in turn, so that the commit pass never clears the
 // count it reads.  [0], [1] entries in list 0 / 1; [kListFill] the list the
 // next step fills; [kListLast] the list the last step filled; list e's
-// entries (slot, new interval index) from kListHead + 2 e slots.  Zero at
-// creation; afterwards the words between calls are the library's.
+// entries (slot | entries << kListCountShift, new interval index) from
+// kListHead + 2 e slots (a slot index fits 24 bits: the rounding draws'
+// element index of a pool fits 32).  Zero at creation; afterwards the words
+// between calls are the library's.  Accepts and flushes use the same lists.
 constexpr int kListFill = 2;
 constexpr int kListLast = 3;
 constexpr int kListHead = 32;
+constexpr int kListCountShift = 24;
+constexpr int kListSlotMask = (1 << kListCountShift) - 1;
 constexpr long list_words(long slots) { return kListHead + 4 * slots; }
 hipError_t launch_split_commit_list(const ReplayParams &p, bool in_bf16, int mode, hipStream_t s);
+// Accept (n_keep) or flush for the low-precision formats: positions and the
+// commit list in one small launch, then the commit pass over the list.
+hipError_t launch_split_accept(const ReplayParams &p, bool in_bf16, int mode, bool accept, hipStream_t s);
 
 // Library scratch for callers that cannot allocate: per-slot arrival counters
 // of up to kNoAllocMaxSlots slots and the commit lists of as many slots, one

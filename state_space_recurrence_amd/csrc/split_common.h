@@ -176,93 +176,6 @@ __device__ __forceinline__ void quantize_store_rows(const ReplayParams &a, size_
     quantize_store_row<MODE>(a, row1, c, lane, v1, r1);
 }
 
-// New state rows of chunk q (rows 2(q + 4m) + hf) from the decoded source
-// rows: S_new = lam * U + sum_j cs[r][j] B_j (B_j staged in LDS as fp32),
-// then rounded and stored.
-template <int KMAX, int MODE>
-__device__ __forceinline__ void commit_chunk_q(const ReplayParams &a, const Slot &s, float4 (&st)[kPerChunk],
-                                               int q, float lam, const float *cs, const float (*sB)[kN],
-                                               uint32_t interval) {
-#pragma unroll
-    for (int m = 0; m < kPerChunk; ++m) {
-        st[m].x *= lam; st[m].y *= lam; st[m].z *= lam; st[m].w *= lam;
-    }
-    // An opaque column offset per chunk: the B_j reads are redone for every
-    // chunk instead of being hoisted and held (64 VGPRs) across chunks.
-    int col = 4 * s.c;
-    asm volatile("" : "+v"(col));
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        const float4 b = *reinterpret_cast<const float4 *>(&sB[j][col]);
-        const float *cp = cs + cs_index<KMAX>(s.hf, q, j, 0);
-        const float4 c0 = *reinterpret_cast<const float4 *>(cp);
-        const float4 c1 = *reinterpret_cast<const float4 *>(cp + 4);
-        const float cf[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-#pragma unroll
-        for (int m = 0; m < kPerChunk; ++m) {
-            st[m].x += cf[m] * b.x;
-            st[m].y += cf[m] * b.y;
-            st[m].z += cf[m] * b.z;
-            st[m].w += cf[m] * b.w;
-        }
-        if ((j & 3) == 3) __builtin_amdgcn_sched_barrier(0);   // bound hoisted LDS reads
-    }
-    // all rows of the chunk are complete before any is rounded (keeps the
-    // rounding streams from being interleaved with, and stretching, the FMAs)
-#pragma unroll
-    for (int m = 0; m < kPerChunk; ++m) asm volatile("" : "+v"(st[m].x), "+v"(st[m].y), "+v"(st[m].z), "+v"(st[m].w));
-    if constexpr (ModeTraits<MODE>::has_u) {
-#pragma unroll
-        for (int m = 0; m < kPerChunk; m += 2) {
-            const size_t row0 = ((size_t)s.b * a.H + s.h) * kP + 2 * chunk_index(q, m) + s.hf;
-            const size_t row1 = ((size_t)s.b * a.H + s.h) * kP + 2 * chunk_index(q, m + 1) + s.hf;
-            quantize_store_rows<MODE>(a, row0, row1, s.c, s.lane, st[m], st[m + 1], interval);
-            __builtin_amdgcn_sched_barrier(0);   // one row pair's rounding streams at a time
-        }
-    } else {   // no stochastic rounding (shared FP4): one row at a time
-        const uint32_t none[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int m = 0; m < kPerChunk; ++m) {
-            const size_t row = ((size_t)s.b * a.H + s.h) * kP + 2 * chunk_index(q, m) + s.hf;
-            quantize_store_row<MODE>(a, row, s.c, s.lane, st[m], none);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-}
-
-// Rewrites the whole head from its source (U, or O for the shared mode),
-// streaming the source rows chunk by chunk with kNB chunks in flight.
-template <int KMAX, int MODE>
-__device__ __forceinline__ void commit_head(const ReplayParams &a, const Slot &s, float lam, const float *cs,
-                                            const float (*sB)[kN], uint32_t interval) {
-    constexpr int UB = ModeTraits<MODE>::ubits;
-    const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
-    typename Raw4<UB>::T raw[kNB][kPerChunk];
-#pragma unroll
-    for (int q = 0; q < kNB; ++q)
-#pragma unroll
-        for (int m = 0; m < kPerChunk; ++m) raw[q][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q, m), s.c);
-    // The commit body is too large for the chunk loop to be unrolled whole;
-    // the inner loop over the kNB buffers is, so every buffer index stays
-    // static (a dynamic index would move the buffers to scratch memory).
-#pragma nounroll
-    for (int q0 = 0; q0 < kChunks; q0 += kNB) {
-#pragma unroll
-        for (int qq = 0; qq < kNB; ++qq) {
-            const int q = q0 + qq;
-            float4 st[kPerChunk];
-#pragma unroll
-            for (int m = 0; m < kPerChunk; ++m) st[m] = decode_row4<UB>(raw[qq][m]);
-            if (q + kNB < kChunks) {
-#pragma unroll
-                for (int m = 0; m < kPerChunk; ++m)
-                    raw[qq][m] = load_row4<UB>(a, hrow + 2 * chunk_index(q + kNB, m), s.c);
-            }
-            commit_chunk_q<KMAX, MODE>(a, s, st, q, lam, cs, sB, interval);
-        }
-    }
-}
-
 // ------------------------------------------------------ output streams --
 // A lane's whole row of the FP4 copy (lane = row): 128 codes in four 16-byte
 // pieces (piece i = block i, columns 32i..32i+31, element n in nibble n of

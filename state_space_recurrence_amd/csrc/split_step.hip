@@ -21,6 +21,12 @@ namespace rssm {
 
 namespace {
 
+// A commit-list entry: the slot with the number of entries it commits, and
+// the interval index of the checkpoint the commit writes.
+__device__ __forceinline__ int2 list_entry(int b, int K, int iv) {
+    return make_int2(b | (K << kListCountShift), iv);
+}
+
 // The end of a row's step.  Positions stay as they are during the step
 // (every workgroup of the row reads its slot's) and move on in the commit
 // pass, which every step launches next, so no workgroup waits for the others
@@ -39,11 +45,62 @@ __device__ __forceinline__ void step_arrive(const ReplayParams &a, const Slot &s
         a.intv[b] = iv;
         const int i = atomicAdd(&a.clist[e], 1);
         if (i < a.nslots) {
-            *reinterpret_cast<int2 *>(a.clist + kListHead + (size_t)e * 2 * a.nslots + 2 * i) = make_int2(b, iv);
+            *reinterpret_cast<int2 *>(a.clist + kListHead + (size_t)e * 2 * a.nslots + 2 * i) = list_entry(b, K, iv);
         } else {
             atomicOr(a.err, kErrDup);   // more listings than slots: rows repeated a slot
         }
     }
+}
+
+// Accept / flush (article section 3) for the low-precision formats, one
+// thread per call row.  The row's slot holds K = pos + n_keep valid entries
+// after an accept (K = pos for a flush), with the same range checks and
+// flags as the fp32 accept; a slot that commits (K >= L; any K > 0 for a
+// flush) gets its new interval index, is listed with it and K, and its
+// position becomes 0, any other slot's becomes K.  The slot is marked like a
+// step's; the commit pass that follows rewrites the listed slots from their
+// K entries and checks and clears the marks.
+template <bool ACCEPT>
+__global__ void __launch_bounds__(256) split_accept_list_kernel(ReplayParams a) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.clist[kListLast] = a.clist[kListFill];
+    const int r = blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= a.batch) return;
+    const int b = a.slot_idx ? a.slot_idx[r] : r;
+    if (b >= a.nslots || b < -1) {
+        atomicOr(a.err, kErrSlot);
+        return;
+    }
+    if (b < 0) return;   // padding row
+    atomicAdd(&a.work[b], 1);
+    // an accept follows a verify (k <= L - 1); a flush folds up to Lcap entries
+    const int kmax = ACCEPT ? a.L - 1 : a.Lcap;
+    int k = a.pos[b];
+    if (k < 0 || k > kmax) {
+        atomicOr(a.err, kErrPos);
+        k = k < 0 ? 0 : kmax;
+    }
+    int nk = 0;
+    if (ACCEPT) {
+        nk = a.n_keep[r];
+        if (nk < 0 || nk > a.T) {
+            atomicOr(a.err, kErrKeep);
+            nk = nk < 0 ? 0 : a.T;
+        }
+    }
+    const int K = k + nk;
+    const bool commit = ACCEPT ? K >= a.L : K > 0;
+    if (commit) {
+        const int e = a.clist[kListFill] & 1;
+        const int iv = a.intv[b] + 1;
+        a.intv[b] = iv;
+        const int i = atomicAdd(&a.clist[e], 1);
+        if (i < a.nslots) {
+            *reinterpret_cast<int2 *>(a.clist + kListHead + (size_t)e * 2 * a.nslots + 2 * i) = list_entry(b, K, iv);
+        } else {
+            atomicOr(a.err, kErrDup);
+        }
+    }
+    a.pos[b] = commit ? 0 : K;
 }
 
 // The positions of the call's rows after a step (run by the commit pass):
@@ -53,15 +110,18 @@ __device__ __forceinline__ void step_arrive(const ReplayParams &a, const Slot &s
 // those a grid further on; the pass gives rank 0 to the workgroup with the
 // last item, so on a short list these rows go to waves with no item, and
 // the item waves' load chains do not wait for them.
+template <bool MOVE>
 __device__ __forceinline__ void advance_positions(const ReplayParams &a, int rank) {
     const int nthreads = gridDim.x * blockDim.x;
     for (int r = rank * blockDim.x + threadIdx.x; r < a.batch; r += nthreads) {
         const int b = a.slot_idx ? a.slot_idx[r] : r;
         if (b < 0 || b >= a.nslots) continue;   // padding, or flagged by the step
         if (a.work[b] != 1) atomicOr(a.err, kErrDup);
-        int k = a.pos[b];
-        k = k < 0 ? 0 : (k > a.L - 1 ? a.L - 1 : k);
-        a.pos[b] = k + 1 == a.L ? 0 : k + 1;
+        if (MOVE) {
+            int k = a.pos[b];
+            k = k < 0 ? 0 : (k > a.L - 1 ? a.L - 1 : k);
+            a.pos[b] = k + 1 == a.L ? 0 : k + 1;
+        }
         a.work[b] = 0;
     }
 }
@@ -155,7 +215,7 @@ split_step_kernel(ReplayParams a) {
 template <typename TIn>
 constexpr int commit_waves(int kmax) { return sizeof(TIn) == 2 && kmax == 16 ? 3 : 2; }
 
-template <typename TIn, int KMAX, int MODE>
+template <typename TIn, int KMAX, int MODE, bool MOVE>
 __global__ void __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(commit_waves<TIn>(KMAX))))
 split_commit_list_kernel(ReplayParams a) {
     constexpr int UB = ModeTraits<MODE>::ubits;
@@ -167,7 +227,7 @@ split_commit_list_kernel(ReplayParams a) {
     // counts of both lists, the list the next step fills, the list the last
     // step filled, in one load, in flight while the positions move on
     const int4 hd = *reinterpret_cast<const int4 *>(a.clist);
-    advance_positions(a, stride - 1 - it);
+    advance_positions<MOVE>(a, stride - 1 - it);
     const int e = __builtin_amdgcn_readfirstlane(hd.w) & 1;
     // (a count beyond the slots means rows repeated a slot, flagged by the
     // step; only the entries written are read)
@@ -188,19 +248,20 @@ split_commit_list_kernel(ReplayParams a) {
     const size_t HP = (size_t)H * kP, GN = (size_t)a.G * kN;
     const int hpg = H / a.G;
     if (it >= items) return;
-    // list entries (slot, interval index of the new checkpoint); the next
-    // item's is read ahead, issued before the current item's loads so that
-    // waiting for it never waits for those (past the end: the last entry)
+    // list entries (slot and entry count, interval index of the new
+    // checkpoint); the next item's is read ahead, issued before the current
+    // item's loads so that waiting for it never waits for those (past the
+    // end: the last entry)
     const int2 *lst = reinterpret_cast<const int2 *>(a.clist + kListHead + (size_t)e * 2 * a.nslots);
     int2 cur = lst[it / per_slot];
     int2 nxt = lst[min(it + stride, items - 1) / per_slot];
-    const int K = a.L;   // a listed slot holds L entries
     for (; it < items; it += stride) {
         const int li = it / per_slot;
         const int hq = it - li * per_slot;
         const int h = hq / parts;
         const int q0 = (hq - h * parts) * nq;   // the item's first quarter
-        const int b = __builtin_amdgcn_readfirstlane(cur.x);
+        const int b = __builtin_amdgcn_readfirstlane(cur.x) & kListSlotMask;
+        const int K = (int)((uint32_t)__builtin_amdgcn_readfirstlane(cur.x) >> kListCountShift);   // 1..KMAX
         const uint32_t interval = (uint32_t)__builtin_amdgcn_readfirstlane(cur.y);
         cur = nxt;
         nxt = lst[min(it + 2 * stride, items - 1) / per_slot];
@@ -298,7 +359,7 @@ hipError_t split_step_t(const ReplayParams &p, int mode, dim3 g, dim3 b, hipStre
 // comes from the occupancy query, once per device and kernel.
 constexpr int kMaxCommitDevices = 64;
 
-template <typename TIn, int KMAX, int MODE>
+template <typename TIn, int KMAX, int MODE, bool MOVE>
 hipError_t split_commit_list_launch(const ReplayParams &p, long items, hipStream_t st) {
     static std::atomic<int> resident[kMaxCommitDevices];   // zero: not queried yet
     int dev = 0;
@@ -308,7 +369,7 @@ hipError_t split_commit_list_launch(const ReplayParams &p, long items, hipStream
     int waves = resident[dev].load(std::memory_order_relaxed);
     if (waves == 0) {
         int per_cu = 0, cus = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_commit_list_kernel<TIn, KMAX, MODE>, 64, 0);
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, split_commit_list_kernel<TIn, KMAX, MODE, MOVE>, 64, 0);
         if (e != hipSuccess) return e;
         e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
@@ -316,14 +377,25 @@ hipError_t split_commit_list_launch(const ReplayParams &p, long items, hipStream
         resident[dev].store(waves, std::memory_order_relaxed);
     }
     const dim3 grid((unsigned)(items < waves ? items : waves));
-    hipLaunchKernelGGL((split_commit_list_kernel<TIn, KMAX, MODE>), grid, dim3(64), 0, st, p);
+    hipLaunchKernelGGL((split_commit_list_kernel<TIn, KMAX, MODE, MOVE>), grid, dim3(64), 0, st, p);
     return hipGetLastError();
 }
 
-template <typename TIn, int KMAX>
+template <typename TIn, int KMAX, bool MOVE>
 hipError_t split_commit_list_t(const ReplayParams &p, int mode, long items, hipStream_t st) {
-    RSSM_MODE_SWITCH(mode, return (split_commit_list_launch<TIn, KMAX, M_>(p, items, st)));
+    RSSM_MODE_SWITCH(mode, return (split_commit_list_launch<TIn, KMAX, M_, MOVE>(p, items, st)));
     return hipSuccess;
+}
+
+// The commit pass over a list; the instance holds up to KMAX entries per
+// slot (16 or 32), sized by the most a listed slot can hold.
+template <bool MOVE>
+hipError_t commit_list_pass(const ReplayParams &p, bool in_bf16, int mode, int kneed, hipStream_t stream) {
+    const long items = (long)p.batch * p.H * 4;   // at most (slot, head, quarter) items
+    if (kneed <= 16) return in_bf16 ? split_commit_list_t<uint16_t, 16, MOVE>(p, mode, items, stream)
+                                    : split_commit_list_t<float, 16, MOVE>(p, mode, items, stream);
+    return in_bf16 ? split_commit_list_t<uint16_t, 32, MOVE>(p, mode, items, stream)
+                   : split_commit_list_t<float, 32, MOVE>(p, mode, items, stream);
 }
 
 #undef RSSM_MODE_SWITCH
@@ -341,11 +413,17 @@ hipError_t launch_split_step(const ReplayParams &p, bool in_bf16, int mode, hipS
 
 hipError_t launch_split_commit_list(const ReplayParams &p, bool in_bf16, int mode, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
-    const long items = (long)p.batch * p.H * 4;   // at most (slot, head, quarter) items
-    if (p.L <= 16) return in_bf16 ? split_commit_list_t<uint16_t, 16>(p, mode, items, stream)
-                                   : split_commit_list_t<float, 16>(p, mode, items, stream);
-    return in_bf16 ? split_commit_list_t<uint16_t, 32>(p, mode, items, stream)
-                   : split_commit_list_t<float, 32>(p, mode, items, stream);
+    return commit_list_pass<true>(p, in_bf16, mode, p.L, stream);   // a step lists slots holding L entries
+}
+
+hipError_t launch_split_accept(const ReplayParams &p, bool in_bf16, int mode, bool accept, hipStream_t stream) {
+    if (p.batch == 0) return hipSuccess;
+    const dim3 grid((unsigned)((p.batch + 255) / 256)), block(256);
+    if (accept) hipLaunchKernelGGL((split_accept_list_kernel<true>), grid, block, 0, stream, p);
+    else hipLaunchKernelGGL((split_accept_list_kernel<false>), grid, block, 0, stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return commit_list_pass<false>(p, in_bf16, mode, p.Lcap, stream);   // a listed slot holds up to Lcap
 }
 
 }  // namespace rssm

@@ -26,7 +26,7 @@ RSSM_STUB(hipError_t launch_defer_accept(const ReplayParams &, hipStream_t))
 RSSM_STUB(hipError_t launch_prefill(const ReplayParams &, bool, bool, int, hipStream_t))
 RSSM_STUB(hipError_t launch_split_step(const ReplayParams &, bool, int, hipStream_t))
 RSSM_STUB(hipError_t launch_split_verify(const ReplayParams &, bool, int, hipStream_t))
-RSSM_STUB(hipError_t launch_split_commit(const ReplayParams &, bool, int, bool, hipStream_t))
+RSSM_STUB(hipError_t launch_split_accept(const ReplayParams &, bool, int, bool, hipStream_t))
 RSSM_STUB(hipError_t launch_split_load(const ReplayParams &, int, hipStream_t))
 RSSM_STUB(hipError_t launch_recurrent(const RecurrentParams &, bool, bool, hipStream_t))
 RSSM_STUB(hipError_t launch_probe(int, const float *, float *, size_t, int, hipStream_t))
@@ -134,6 +134,17 @@ int main() {
     expect("accept null keep", replayssm_accept(&d, &st, nullptr, 2, s), RSSM_E_ARG);
     expect("accept T", replayssm_accept(&d, &st, (const int32_t *)p, 7, s), 1);
     expect("deferred undeclared", replayssm_accept_deferred(&d, &st, (const int32_t *)p, 2, s), 1);
+    // a low-precision state without its commit lists is refused before any launch
+    rssm_desc lp = good_desc();
+    lp.ckpt_dtype = RSSM_BF16;
+    lp.out_dtype = RSSM_FP4_E2M1;
+    rssm_state lst = st;
+    lst.out_q = p;
+    lst.out_scale = p;
+    lst.commit_list = nullptr;
+    expect("lowp step lists", replayssm_step(&lp, &lst, p, p, p, p, y, s), RSSM_E_ARG);
+    expect("lowp accept lists", replayssm_accept(&lp, &lst, (const int32_t *)p, 2, s), RSSM_E_ARG);
+    expect("lowp commit lists", replayssm_commit(&lp, &lst, s), RSSM_E_ARG);
     expect("prefill Tp", replayssm_prefill(&d, &st, -1, 0, p, p, p, p, y, s), 1);
     expect("prefill null", replayssm_prefill(&d, &st, 5, 0, nullptr, p, p, p, y, s), RSSM_E_ARG);
     expect("load null", replayssm_load_checkpoint(&d, &st, nullptr, s), RSSM_E_ARG);
