@@ -650,7 +650,28 @@ def run_spec(rs, L, torch, synth, dev, stream, sh, log, rounds=64, warm=8):
     log(f"[bench] spec: replay {out['replay_kept_tokens_per_s']:.0f} kept tok/s (deferred commit "
         f"{out['deferred_kept_tokens_per_s']:.0f}), recurrent {out['recurrent_kept_tokens_per_s']:.0f} "
         f"({out['replay_speedup_vs_recurrent']:.2f}x / {out['deferred_speedup_vs_recurrent']:.2f}x)")
-    del pools, layers
+    del pools
+    torch.cuda.empty_cache()
+    # the same rounds on low-precision states (verify reads the output copy,
+    # accepts list the committing slots for the commit pass)
+    out["split"] = {}
+    for fmt in ("split-bf16", "split-e4m3", "shared-fp4"):
+        for l, lay in enumerate(layers):
+            lay["ls"] = None
+            torch.cuda.empty_cache()
+            ls = rs.LayerState(w.batch, w.heads, w.groups, lay["A"], lay["D"], interval=w.interval, max_draft=T,
+                               in_dtype=lay["in"][0].dtype, device=dev, state_format=fmt, seed=w.seed,
+                               layer_id=l)
+            rs.load_checkpoint(ls, lay["S0"])
+            lay["ls"], lay["desc"], lay["st"] = ls, ls.desc(), ls.cstate()
+        replay_rounds(0, warm)
+        ssec = t(replay_rounds, warm, rounds)
+        for lay in layers:
+            rs.check_device_errors(lay["ls"])
+        out["split"][fmt] = {"ms_per_round": ssec / rounds * 1e3, "kept_tokens_per_s": kept / ssec,
+                             "speedup_vs_fp32_replay": sec / ssec}
+        log(f"[bench] spec {fmt}: {kept / ssec:.0f} kept tok/s ({sec / ssec:.2f}x the fp32 state)")
+    del layers
     torch.cuda.empty_cache()
     return out
 
