@@ -239,6 +239,44 @@ __device__ __forceinline__ float fp4_row_dot(const Fp4Row &o, const uint16_t *sC
     return y;
 }
 
+// The same for T drafts at once (C of draft t at sC[t]): each pair of codes is
+// widened once and meets the T drafts' pairs, so the conversions do not grow
+// with T and no widened row is held.  Per draft the same products and sums in
+// the same order as fp4_row_dot.
+template <int T>
+__device__ __forceinline__ void fp4_row_dots(const Fp4Row &o, const uint16_t (*sC)[kN], float (&y)[T]) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) y[t] = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 4; ++blk) {
+        const uint32_t w[4] = {o.code[blk].x, o.code[blk].y, o.code[blk].z, o.code[blk].w};
+        float acc[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[t] = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            uint4 c[T];
+#pragma unroll
+            for (int t = 0; t < T; ++t) c[t] = *reinterpret_cast<const uint4 *>(reinterpret_cast<const uint32_t *>(sC[t]) + 16 * blk + 4 * d);
+            const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 0);
+            const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 1);
+            const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 2);
+            const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[d], 1.0f, 3);
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                acc[t] = __builtin_amdgcn_fdot2_f32_bf16(v0, __builtin_bit_cast(bf16x2, c[t].x), acc[t], false);
+                acc[t] = __builtin_amdgcn_fdot2_f32_bf16(v1, __builtin_bit_cast(bf16x2, c[t].y), acc[t], false);
+                acc[t] = __builtin_amdgcn_fdot2_f32_bf16(v2, __builtin_bit_cast(bf16x2, c[t].z), acc[t], false);
+                acc[t] = __builtin_amdgcn_fdot2_f32_bf16(v3, __builtin_bit_cast(bf16x2, c[t].w), acc[t], false);
+            }
+            __builtin_amdgcn_sched_barrier(0);   // one dword of codes (T drafts' C pieces) live at a time
+        }
+        const float sc = e4m3_decode((o.scale >> (8 * blk)) & 0xFFu);
+#pragma unroll
+        for (int t = 0; t < T; ++t) y[t] += acc[t] * sc;
+    }
+}
+
 // The same with fp32 C in LDS (128 floats): codes widened to f32, one fused
 // multiply-add per element.
 __device__ __forceinline__ float fp4_row_dot(const Fp4Row &o, const float *sC) {

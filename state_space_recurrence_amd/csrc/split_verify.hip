@@ -39,7 +39,9 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
     verify_prologue<TIn, KMAX, T>(a, s, in, prow, sm, ybuf);
 
     float y0[T];
-    if constexpr (MT::fp4_out) {
+    if constexpr (MT::fp4_out && sizeof(TIn) == 2) {
+        fp4_row_dots<T>(o, sC, y0);
+    } else if constexpr (MT::fp4_out) {
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             Fp4Row ot = o;   // decoded afresh per draft (holding 128 widened values would cost 64 VGPRs)
