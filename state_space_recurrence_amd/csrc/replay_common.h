@@ -474,14 +474,6 @@ __device__ __forceinline__ void step_append(const ReplayParams &a, const Slot &s
 // ------------------------------------------------------------------------
 // Speculative-verify prologue.
 // ------------------------------------------------------------------------
-template <int KMAX, int T>
-struct VerifySmem {
-    float l[kMaxHpw][KMAX];
-    float dt[kMaxHpw][KMAX];
-    float gram[T][KMAX];
-    float cy[kMaxHpw][T][KMAX];
-    float lam[kMaxHpw][T];
-};
 
 struct VerifyIn {
     int k, KL;
@@ -491,9 +483,8 @@ struct VerifyIn {
 };
 
 template <typename TIn, int T>
-__device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const Slot &s, int kmax) {
+__device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const Slot &s, int kmax, int k) {
     VerifyIn in;
-    int k = a.pos[s.b];
     in.seen = k;
     if (k < 0 || k > kmax) {
         if (threadIdx.x == 0) atomicOr(a.err, kErrPos);
@@ -514,84 +505,9 @@ __device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const S
     return in;
 }
 
-// Weights, decays and the buffer part of every draft output for row prow:
-// ybuf[t] = sum_{j < k+t+1} w_tj (B_j . C_t) x_j[prow] + D x_t[prow];
-// Lambda_t is left in sm.lam[wave][t].
-template <typename TIn, int KMAX, int T>
-__device__ __forceinline__ void verify_prologue(const ReplayParams &a, const Slot &s, const VerifyIn &in,
-                                                int prow, VerifySmem<KMAX, T> &sm, float (&ybuf)[T]) {
-    const int k = in.k, KL = in.KL;
-    const TIn *xin = static_cast<const TIn *>(in.xin);
-    const TIn *Bin = static_cast<const TIn *>(in.Bin);
-    const TIn *Cin = static_cast<const TIn *>(in.Cin);
-    const TIn *dtin = static_cast<const TIn *>(in.dtin);
-    const TIn *xb = static_cast<const TIn *>(in.xb);
-    const TIn *bb = static_cast<const TIn *>(in.bb);
-    const TIn *db = static_cast<const TIn *>(in.db);
-
-    float xv[KMAX];
-#pragma unroll
-    for (int j = 0; j < KMAX; ++j) {
-        int t = j - k;
-        t = t < 0 ? 0 : (t > T - 1 ? T - 1 : t);
-        const TIn *px = (j < k) ? xb + (size_t)j * in.HP + prow : xin + (size_t)t * in.HP + prow;
-        xv[j] = io<TIn>::load1(px);
-    }
-#pragma unroll
-    for (int t = 0; t < T; ++t) ybuf[t] = io<TIn>::load1(xin + (size_t)t * in.HP + prow);
-    const float Ah = a.A[s.h], Dh = a.D[s.h];
-
-    if (s.lane < KL) {
-        const TIn *pd = (s.lane < k) ? db + (size_t)s.lane * a.H : dtin + (size_t)(s.lane - k) * a.H;
-        const float d = io<TIn>::load1(pd);
-        sm.dt[s.wave][s.lane] = d;
-        sm.l[s.wave][s.lane] = Ah * d;
-    }
-    {   // Gram g[t][j] = B_j . C_t for every draft t and entry j < KL
-        const int t16 = threadIdx.x & 15, grp = threadIdx.x >> 4, ngrp = blockDim.x >> 4;
-        for (int d = grp; d < T * KL; d += ngrp) {
-            const int t = d / KL, j = d - t * KL;
-            const TIn *pb = (j < k) ? bb + (size_t)j * in.GN : Bin + (size_t)(j - k) * in.GN;
-            const TIn *pc = Cin + (size_t)t * in.GN;
-            const float4 b0 = io<TIn>::load4(pb + 8 * t16), b1 = io<TIn>::load4(pb + 8 * t16 + 4);
-            const float4 c0 = io<TIn>::load4(pc + 8 * t16), c1 = io<TIn>::load4(pc + 8 * t16 + 4);
-            const float acc = row16_sum(dot4(b0, c0) + dot4(b1, c1));
-            if (t16 == 0) sm.gram[t][j] = acc;
-        }
-    }
-    __syncthreads();
-
-    if (s.lane < KMAX) {
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int Kt = k + t + 1;
-            float cy = 0.f;
-            if (s.lane < Kt) {
-                float suf = 0.f;
-                for (int i = s.lane + 1; i < Kt; ++i) suf += sm.l[s.wave][i];
-                cy = sm.dt[s.wave][s.lane] * expf(suf) * sm.gram[t][s.lane];
-            }
-            sm.cy[s.wave][t][s.lane] = cy;
-        }
-    }
-    if (s.lane < T) {
-        float tot = 0.f;
-        for (int i = 0; i < k + s.lane + 1; ++i) tot += sm.l[s.wave][i];
-        sm.lam[s.wave][s.lane] = expf(tot);
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int Kt = k + t + 1;
-        float acc = Dh * ybuf[t];
-#pragma unroll
-        for (int j = 0; j < KMAX; ++j) {
-            const float term = sm.cy[s.wave][t][j] * xv[j];
-            acc += (j < Kt) ? term : 0.f;   // later drafts never reach output t
-        }
-        ybuf[t] = acc;
-    }
+template <typename TIn, int T>
+__device__ __forceinline__ VerifyIn verify_inputs(const ReplayParams &a, const Slot &s, int kmax) {
+    return verify_inputs<TIn, T>(a, s, kmax, a.pos[s.b]);
 }
 
 // ---- Split form of the verify prologue for the verify kernel.  Loads
@@ -603,8 +519,9 @@ __device__ __forceinline__ void verify_prologue(const ReplayParams &a, const Slo
 // (lane broadcasts), then the buffer part of the outputs from the staged x
 // rows and replay coefficients.  The raw pieces occupy few registers while
 // the first chunks are in flight, which keeps the kernel at four waves per
-// SIMD.  Per-output arithmetic and summation order are those of
-// verify_prologue.
+// SIMD.  Per draft t (entries j < k + t + 1): w_tj = dt_j exp(sum of l_i over
+// j < i <= k + t) and Lambda_t = exp(sum of l_i over i <= k + t), sums grown
+// in ascending i; ybuf[t] = D x_t[prow] + sum_j w_tj (B_j . C_t) x_j[prow].
 template <int KMAX, int T>
 constexpr int stage_pieces() { return (KMAX + T) * (kN / 4); }
 template <int KMAX, int T>

@@ -11,7 +11,7 @@ template <typename TIn, int KMAX, int T, int MODE>
 __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
     using MT = ModeTraits<MODE>;
     constexpr int UB = MT::ubits;
-    __shared__ VerifySmem<KMAX, T> sm;
+    __shared__ VerifySmemF<TIn, KMAX, KMAX, T> sm;
     __shared__ __align__(16) TIn sC[T][kN];   // the drafts' C, for row-per-lane output dots
 
     const Slot s = slot_of(a);
@@ -19,6 +19,9 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
     const int prow = MT::fp4_out ? s.lane : s.prow;   // FP4 output copy: a whole row per lane
     const size_t hrow = ((size_t)s.b * a.H + s.h) * kP + s.hf;
 
+    // the position first (the prologue's first need), then the output-source
+    // rows, then the prologue's loads, whose data the prologue waits for
+    const int pos_in = a.pos[s.b];
     Fp4Row o;
     typename Raw4<UB>::T raw[32];
     if constexpr (MT::fp4_out) {
@@ -27,7 +30,9 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
 #pragma unroll
         for (int i = 0; i < 32; ++i) raw[i] = load_row4<UB>(a, hrow + 2 * i, s.c);
     }
-    const VerifyIn in = verify_inputs<TIn, T>(a, s, a.L - 1);
+    const VerifyIn in = verify_inputs<TIn, T>(a, s, a.L - 1, pos_in);
+    VerifyPre<TIn, KMAX, KMAX, T> pre;
+    verify_preload<TIn, KMAX, KMAX, T>(a, s, in, pre);
     if constexpr (MT::fp4_out) {   // staged ahead of the prologue, whose barriers publish it
         constexpr int per = 16 / (int)sizeof(TIn);   // elements per 16-byte piece
         for (int q = threadIdx.x; q < T * kN / per; q += blockDim.x) {
@@ -35,8 +40,8 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
             store16(&sC[t][c], load16(static_cast<const TIn *>(in.Cin) + (size_t)t * in.GN + c));
         }
     }
-    float ybuf[T];
-    verify_prologue<TIn, KMAX, T>(a, s, in, prow, sm, ybuf);
+    float ybuf[T], lam[T];
+    verify_finish<TIn, KMAX, KMAX, T>(a, s, in, pre, sm, prow, ybuf, lam);
 
     float y0[T];
     if constexpr (MT::fp4_out && sizeof(TIn) == 2) {
@@ -61,7 +66,7 @@ __global__ void __launch_bounds__(256) split_verify_kernel(ReplayParams a) {
     }
 #pragma unroll
     for (int t = 0; t < T; ++t)
-        a.y[((size_t)s.row * T + t) * in.HP + (size_t)s.h * kP + prow] = sm.lam[s.wave][t] * y0[t] + ybuf[t];
+        a.y[((size_t)s.row * T + t) * in.HP + (size_t)s.h * kP + prow] = lam[t] * y0[t] + ybuf[t];
     verify_append<TIn, T>(a, s, in);
 }
 
