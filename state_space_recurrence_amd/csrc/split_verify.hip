@@ -108,8 +108,13 @@ hipError_t split_verify_t(const ReplayParams &p, int mode, dim3 g, dim3 b, hipSt
 hipError_t launch_split_verify(const ReplayParams &p, bool in_bf16, int mode, hipStream_t stream) {
     if (p.batch == 0) return hipSuccess;
     dim3 grid(p.batch * p.wg_per_slot), block(64 * p.hpw);
+    // entries per instance: 16, 24 (the 20-entry buffer of L = 16 with 4
+    // drafts: 30.8 KB of LDS against 39.8 KB at 32, five workgroups per CU
+    // instead of four) or 32
     if (p.Lcap <= 16) return in_bf16 ? split_verify_t<uint16_t, 16>(p, mode, grid, block, stream)
                                      : split_verify_t<float, 16>(p, mode, grid, block, stream);
+    if (p.Lcap <= 24) return in_bf16 ? split_verify_t<uint16_t, 24>(p, mode, grid, block, stream)
+                                     : split_verify_t<float, 24>(p, mode, grid, block, stream);
     return in_bf16 ? split_verify_t<uint16_t, 32>(p, mode, grid, block, stream)
                    : split_verify_t<float, 32>(p, mode, grid, block, stream);
 }

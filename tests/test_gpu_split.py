@@ -199,12 +199,15 @@ def test_update_checkpoint_ignores_output_copy(rs):
     assert torch.equal(cks[0], cks[1])
 
 
-@pytest.mark.parametrize("fmt", ["split-bf16", "split-e4m3", "shared-fp4"])
-def test_split_speculative_rounds(rs, fmt):
+@pytest.mark.parametrize("fmt,L", [("split-bf16", 16), ("split-e4m3", 16), ("shared-fp4", 16),
+                                   ("split-bf16", 24), ("shared-fp4", 8)])
+def test_split_speculative_rounds(rs, fmt, L):
     """Verify reads the output source; accept commits from the update source
-    once the position count reaches L (teacher-forced at every commit)."""
-    w = dataclasses.replace(synth.WORKLOADS["spec"], heads=16, groups=2, in_dtype="bf16")
-    batch, R = 4, 14
+    once the position count reaches L (teacher-forced at every commit).
+    With 5 positions the buffer holds 20 entries at L = 16 (the 24-entry
+    verify instance), 28 at L = 24 (the 32-entry one) and 12 at L = 8."""
+    w = dataclasses.replace(synth.WORKLOADS["spec"], heads=16, groups=2, in_dtype="bf16", interval=L)
+    batch, R = 4, 14 * max(1, L // 16)
     T = w.drafts + 1
     A, D = synth.layer_params(w, 0)
     S0 = synth.init_state(w, 0, batch=batch)
