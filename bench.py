@@ -1145,7 +1145,7 @@ def summarize_kernels(fetch_csv: str, write_csv: str, out_md: str, extra_csv: st
         """Algorithmic bytes of one launch (None where the model does not
         cover it)."""
         if key.startswith("split_step_kernel") or key.startswith("split_commit_list_kernel"):
-            mode = int(key.split("<")[1].split(">")[0].split(",")[-1])
+            mode = int(key.split("<")[1].split(">")[0].split(",")[2])   # <input type, entries, mode, ...>
             fmt = modes[mode]
             # bytes per element: output source read, update source read, state written
             out_r, upd_r, cw = {"split-bf16": (fp4, 2, 2 + fp4), "split-e4m3": (fp4, 1, 1 + fp4),
