@@ -470,3 +470,78 @@ def test_split_largest_pool_element_index(rs, fmt):
     check_bytes(dump, 1, "commit")
     assert ls.intv[sl].cpu().tolist() == [1] * rows and ls.pos[sl].cpu().tolist() == [0] * rows
     rs.check_device_errors(ls)
+
+
+@pytest.mark.parametrize("fmt", ["split-bf16", "split-e4m3", "shared-fp4"])
+def test_split_flush_commits_open_slots(rs, fmt):
+    """A flush commits every slot holding entries, each from its own count
+    (slots at different positions, one at 0): values against the oracle's
+    recurrence from the update source, stored bytes bit-exact, positions 0
+    and interval counts moved on only where a commit happened."""
+    w = dataclasses.replace(synth.WORKLOADS["split"], heads=16, groups=2)
+    batch, steps = 4, 11
+    A, D = synth.layer_params(w, 0)
+    S0 = synth.init_state(w, 0, batch=batch)
+    x, Bm, Cm, dt = synth.token_inputs(w, 0, steps, batch=batch)
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=w.interval, in_dtype=x.dtype, state_format=fmt,
+                       seed=SEED, layer_id=LAYER, debug_prequant=True)
+    rs.load_checkpoint(ls, S0.cuda())
+    counts = [11, 5, 0, 1]   # entries per slot before the flush
+    for t in range(steps):
+        rows = [b for b in range(batch) if counts[b] > t]
+        idx = torch.tensor(rows, dtype=torch.int32, device="cuda")
+        rs.step(ls, x[t, rows].cuda(), Bm[t, rows].cuda(), Cm[t, rows].cuda(), dt[t, rows].cuda(), slots=idx)
+    assert ls.pos.cpu().tolist() == counts
+    _, upd_src = _sources(fmt, ls)
+    ls.debug_prequant.zero_()
+    rs.commit(ls)
+    rs.check_device_errors(ls)
+    assert ls.pos.cpu().tolist() == [0] * batch
+    assert ls.intv.cpu().tolist() == [1 if c else 0 for c in counts]
+    dump = ls.debug_prequant.cpu()
+    for b, c in enumerate(counts):
+        if c == 0:
+            continue
+        S_new, _ = oracle.recurrent(upd_src[b:b + 1], x[:c, b:b + 1], Bm[:c, b:b + 1], Cm[:c, b:b + 1],
+                                    dt[:c, b:b + 1], A, D, w.groups)
+        assert_close(dump[b:b + 1], S_new, f"{fmt} flush values of slot {b}")
+    # bytes: committed slots from the dumped values (stream index 1), the
+    # untouched slot kept its load-time bytes (stream index 0)
+    v = dump.numpy().astype(np.float32)
+    if _ufmt(fmt):
+        got = ls.ckpt.cpu().numpy()
+        got = got.view(np.uint16) if _ufmt(fmt) == "bf16" else got
+        for b, c in enumerate(counts):
+            if c:
+                ref = oracle.sr_quantize(v[b].reshape(-1), _ufmt(fmt), SEED, LAYER, 1, elem0=b * v[b].size)
+                assert np.array_equal(got[b].reshape(-1), ref), f"{fmt} update bytes of slot {b}"
+    codes, scales = oracle.fp4_quantize(v)
+    for b, c in enumerate(counts):
+        if c:
+            assert np.array_equal(ls.out_q[b].cpu().numpy(), codes[b]), f"{fmt} FP4 codes of slot {b}"
+            assert np.array_equal(ls.out_scale[b].cpu().numpy(), scales[b]), f"{fmt} FP4 scales of slot {b}"
+
+
+@pytest.mark.parametrize("fmt", ["split-bf16", "shared-fp4"])
+def test_split_accept_flags(rs, fmt):
+    """Low-precision accepts flag n_keep outside 0..T (clamped) and two rows
+    on one slot, like the fp32 accept."""
+    w = dataclasses.replace(synth.WORKLOADS["spec"], heads=16, groups=2, in_dtype="bf16")
+    batch = 2
+    T = w.drafts + 1
+    A, D = synth.layer_params(w, 0)
+    x, Bm, Cm, dt = synth.token_inputs(w, 0, 1, batch=batch, tokens=T)
+    bt = lambda t: t[0].transpose(0, 1).contiguous().cuda()
+    ls = rs.LayerState(batch, w.heads, w.groups, A, D, interval=w.interval, max_draft=T, in_dtype=x.dtype,
+                       state_format=fmt, seed=SEED, layer_id=LAYER)
+    rs.load_checkpoint(ls, synth.init_state(w, 0, batch=batch).cuda())
+    rs.verify(ls, bt(x), bt(Bm), bt(Cm), bt(dt))
+    rs.accept(ls, torch.tensor([9, -1], dtype=torch.int32, device="cuda"), T)
+    with pytest.raises(rs.ReplaySSMError, match="device"):
+        rs.check_device_errors(ls)
+    assert ls.pos.cpu().tolist() == [T, 0]
+    rs.verify(ls, bt(x), bt(Bm), bt(Cm), bt(dt), slots=torch.tensor([0, 1], dtype=torch.int32, device="cuda"))
+    rs.accept(ls, torch.tensor([1, 1], dtype=torch.int32, device="cuda"), T,
+              slots=torch.tensor([1, 1], dtype=torch.int32, device="cuda"))
+    with pytest.raises(rs.ReplaySSMError, match="same slot"):
+        rs.check_device_errors(ls)
