@@ -14,6 +14,10 @@
 // spills, more waves per SIMD on the latency-bound steps), and spreads each
 // interval's commit work over the whole chip whether the slots commit
 // together (lock-step phases) or a few on every step (staggered phases).
+// Accepts and flushes of the low-precision formats (article section 3) list
+// their committing slots the same way, with each slot's entry count, set the
+// positions themselves, and run the same commit pass, which then leaves the
+// positions alone.
 #include <atomic>
 #include "split_common.h"
 
